@@ -1,0 +1,277 @@
+"""Float64 oracle of the sparse pre-filling path (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, the package smoke check and the benchmark's CPU-baseline leg use
+this module.  See the package docstring for the sources [P1], [P1-PIT], [P2]
+and the readings R1..R8 taken where the pages are silent.
+
+Notation: n keys/rows, d = 128, BM = 64 query rows per query block,
+NB = n / BM, c = 1/sqrt(d).  q_last is the last L rows of one Q head, k and v
+are the rows of its KV head.  Index of one head = a list over query blocks of
+(ranges, cols): ranges an int64 array [r, 2] of half-open [lo, hi) key spans,
+sorted, disjoint and non-touching; cols an ascending int64 array of single
+key columns that lie in no range.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+BM = 64  # query rows per block, and the pooling block of Block-Sparse heads ([P2] "Key points")
+
+# Pattern codes of the per-head parameters (the offline search's output, [P2] "Summary").
+A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, DENSE = 0, 1, 2, 3
+
+BlockIndex = Tuple[np.ndarray, np.ndarray]
+
+
+# --------------------------------------------------------------------------
+# Vertical-Slash estimation ([P2] "Key points": the last query vectors are
+# scored against all keys).  Readings R2, R3.
+# --------------------------------------------------------------------------
+def vs_probabilities(q_last: np.ndarray, k: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """Causal softmax of the last L rows against all n keys.
+
+    Row r stands for sequence position i = n - L + r; key j is allowed iff
+    j <= i.  Returns P with shape [L, n] (zeros where j > i).
+    """
+    L, d = q_last.shape
+    n = k.shape[0]
+    c = 1.0 / math.sqrt(d) if scale is None else scale
+    z = (q_last @ k.T) * c                       # [L, n] logits
+    rows = np.arange(n - L, n)[:, None]
+    allowed = np.arange(n)[None, :] <= rows
+    z = np.where(allowed, z, -np.inf)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)                            # exp(-inf) = 0 on masked keys
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def vs_scores(q_last: np.ndarray, k: np.ndarray, scale: Optional[float] = None):
+    """Vertical scores v[j] and slash scores s[o], o = i - j (R3).
+
+    v[j] = sum over the L rows of P[i, j];
+    s[o] = sum over the L rows with i - o >= 0 of P[i, i - o].
+    """
+    p = vs_probabilities(q_last, k, scale)
+    L, n = p.shape
+    v = p.sum(axis=0)
+    s = np.zeros(n)
+    for r in range(L):
+        i = n - L + r
+        # p[r, i::-1] lists P[i, i], P[i, i-1], ..., P[i, 0], i.e. offsets o = 0..i
+        s[: i + 1] += p[r, i::-1]
+    return v, s
+
+
+# --------------------------------------------------------------------------
+# Top-k (R4, R5): the k largest, equal values resolved toward the lower index,
+# all candidates when k exceeds their number, returned ascending.
+# --------------------------------------------------------------------------
+def topk(scores: np.ndarray, k: int) -> np.ndarray:
+    scores = np.asarray(scores, dtype=np.float64)
+    idx = np.arange(scores.shape[0])
+    order = np.lexsort((idx, -scores))           # by score descending, then index ascending
+    return np.sort(order[: min(k, scores.shape[0])]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Block-Sparse estimation ([P2] "Key points": queries and keys mean-pooled in
+# 64-token blocks).  Reading R6: rank the raw dot products of the means.
+# --------------------------------------------------------------------------
+def bs_pool(x: np.ndarray) -> np.ndarray:
+    n, d = x.shape
+    return x.reshape(n // BM, BM, d).mean(axis=1)
+
+
+def bs_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """S[b, c] = mean(q over block b) . mean(k over block c) for c <= b; -inf above."""
+    qh, kh = bs_pool(q), bs_pool(k)
+    s = qh @ kh.T
+    nb = s.shape[0]
+    return np.where(np.tril(np.ones((nb, nb), dtype=bool)), s, -np.inf)
+
+
+def bs_select(scores: np.ndarray, top_k: int) -> List[np.ndarray]:
+    """B_b = top-min(k, b+1) of S[b, 0..b], ascending (R5)."""
+    return [topk(scores[b, : b + 1], top_k) for b in range(scores.shape[0])]
+
+
+# --------------------------------------------------------------------------
+# Index conversion (R7): per query block, merged key ranges plus columns.
+# --------------------------------------------------------------------------
+def _merge(lo: np.ndarray, hi: np.ndarray) -> np.ndarray:
+    """Merge half-open spans that overlap or touch; returns sorted [r, 2]."""
+    if lo.size == 0:
+        return np.zeros((0, 2), dtype=np.int64)
+    order = np.argsort(lo, kind="stable")
+    lo, hi = lo[order], hi[order]
+    out = [[int(lo[0]), int(hi[0])]]
+    for a, b in zip(lo[1:].tolist(), hi[1:].tolist()):
+        if a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return np.asarray(out, dtype=np.int64)
+
+
+def vs_block_index(vert: np.ndarray, slash: np.ndarray, b: int) -> BlockIndex:
+    """Ranges and columns of query block b (rows [b*BM, b*BM + BM))."""
+    row0, last = b * BM, b * BM + BM - 1
+    o = np.asarray(slash, dtype=np.int64)
+    o = o[o <= last]                              # diagonals that reach some row of the block
+    ranges = _merge(np.maximum(0, row0 - o), row0 + BM - o)
+    j = np.asarray(vert, dtype=np.int64)
+    j = j[j <= last]
+    if ranges.shape[0]:
+        pos = np.searchsorted(ranges[:, 0], j, side="right") - 1
+        covered = (pos >= 0) & (j < ranges[np.maximum(pos, 0), 1])
+        j = j[~covered]
+    return ranges, np.sort(j)
+
+
+def vs_index(vert: np.ndarray, slash: np.ndarray, n: int) -> List[BlockIndex]:
+    return [vs_block_index(vert, slash, b) for b in range(n // BM)]
+
+
+def bs_block_index(blocks: np.ndarray) -> BlockIndex:
+    c = np.asarray([x for x in blocks if x >= 0], dtype=np.int64)
+    return _merge(c * BM, c * BM + BM), np.zeros(0, dtype=np.int64)
+
+
+def bs_index(selected: Sequence[np.ndarray]) -> List[BlockIndex]:
+    return [bs_block_index(s) for s in selected]
+
+
+def ashape_block_index(sink: int, window: int, b: int) -> BlockIndex:
+    """Union over the block's rows of {j < sink} and {i - window < j <= i} (R1)."""
+    row0, end = b * BM, b * BM + BM
+    lo = [max(0, row0 - window + 1)]
+    hi = [end]
+    if sink > 0:
+        lo.append(0)
+        hi.append(min(sink, end))
+    return _merge(np.asarray(lo, dtype=np.int64), np.asarray(hi, dtype=np.int64)), np.zeros(0, dtype=np.int64)
+
+
+def ashape_index(sink: int, window: int, n: int) -> List[BlockIndex]:
+    return [ashape_block_index(sink, window, b) for b in range(n // BM)]
+
+
+def dense_block_index(b: int) -> BlockIndex:
+    return np.asarray([[0, b * BM + BM]], dtype=np.int64), np.zeros(0, dtype=np.int64)
+
+
+def dense_index(n: int) -> List[BlockIndex]:
+    return [dense_block_index(b) for b in range(n // BM)]
+
+
+def index_to_csr(index: Sequence[BlockIndex]):
+    """(rng_ptr[NB+1], rng[R, 2], col_ptr[NB+1], col[C]) as int32 arrays."""
+    nr = [r.shape[0] for r, _ in index]
+    nc = [c.shape[0] for _, c in index]
+    rng_ptr = np.concatenate([[0], np.cumsum(nr)]).astype(np.int32)
+    col_ptr = np.concatenate([[0], np.cumsum(nc)]).astype(np.int32)
+    rng = (np.concatenate([r for r, _ in index]) if sum(nr) else np.zeros((0, 2))).astype(np.int32).reshape(-1, 2)
+    col = (np.concatenate([c for _, c in index]) if sum(nc) else np.zeros(0)).astype(np.int32)
+    return rng_ptr, rng, col_ptr, col
+
+
+def csr_to_index(rng_ptr, rng, col_ptr, col) -> List[BlockIndex]:
+    nb = len(rng_ptr) - 1
+    return [(np.asarray(rng[rng_ptr[b]:rng_ptr[b + 1]], dtype=np.int64).reshape(-1, 2),
+             np.asarray(col[col_ptr[b]:col_ptr[b + 1]], dtype=np.int64)) for b in range(nb)]
+
+
+# --------------------------------------------------------------------------
+# Mask and attention ([P1]: attention only over the estimated indices; [P2]
+# "Summary", third stage).  Readings R1 (A-shape window), R7, R8.
+# --------------------------------------------------------------------------
+def block_mask(bidx: BlockIndex, b: int, n: int, ashape: Optional[Tuple[int, int]] = None) -> np.ndarray:
+    """Boolean [BM, n]: row i = b*BM + r may attend key j."""
+    ranges, cols = bidx
+    keep = np.zeros(n, dtype=bool)
+    for lo, hi in ranges.tolist():
+        keep[lo:hi] = True
+    keep[np.asarray(cols, dtype=np.int64)] = True
+    i = np.arange(b * BM, b * BM + BM)[:, None]
+    j = np.arange(n)[None, :]
+    m = keep[None, :] & (j <= i)
+    if ashape is not None:
+        sink, window = ashape
+        m &= (j < sink) | (i - j < window)
+    return m
+
+
+def attention_block(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, bidx: BlockIndex, b: int,
+                    scale: Optional[float] = None, ashape: Optional[Tuple[int, int]] = None):
+    """Masked softmax attention for the 64 rows of block b; returns (out [BM, d], lse [BM])."""
+    n, d = k.shape
+    c = 1.0 / math.sqrt(d) if scale is None else scale
+    ranges, cols = bidx
+    keys = np.unique(np.concatenate([np.concatenate([np.arange(lo, hi) for lo, hi in ranges.tolist()])
+                                     if ranges.shape[0] else np.zeros(0, dtype=np.int64),
+                                     np.asarray(cols, dtype=np.int64)]).astype(np.int64))
+    out = np.zeros((BM, d))
+    lse = np.full(BM, -np.inf)
+    if keys.size == 0:
+        return out, lse
+    z = (q_rows @ k[keys].T) * c                  # [BM, |keys|]
+    i = np.arange(b * BM, b * BM + BM)[:, None]
+    j = keys[None, :]
+    allowed = j <= i
+    if ashape is not None:
+        sink, window = ashape
+        allowed &= (j < sink) | (i - j < window)
+    z = np.where(allowed, z, -np.inf)
+    has = allowed.any(axis=1)
+    m = np.where(has, z.max(axis=1), 0.0)
+    e = np.exp(z - m[:, None])
+    l = e.sum(axis=1)
+    out[has] = (e[has] @ v[keys]) / l[has, None]
+    lse[has] = m[has] + np.log(l[has])
+    return out, lse
+
+
+def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, index: Sequence[BlockIndex],
+                   scale: Optional[float] = None, ashape: Optional[Tuple[int, int]] = None,
+                   blocks: Optional[Sequence[int]] = None):
+    """Attention of one Q head over its index; ``blocks`` restricts to some query blocks.
+
+    Returns (out [n, d], lse [n]); rows of skipped blocks stay NaN.
+    """
+    n, d = q.shape
+    out = np.full((n, d), np.nan)
+    lse = np.full(n, np.nan)
+    for b in (range(n // BM) if blocks is None else blocks):
+        o, l = attention_block(q[b * BM:(b + 1) * BM], k, v, index[b], b, scale, ashape)
+        out[b * BM:(b + 1) * BM] = o
+        lse[b * BM:(b + 1) * BM] = l
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# One head, end to end: estimation then index ([P1]: pattern fixed offline,
+# indices built per prompt).
+# --------------------------------------------------------------------------
+def estimate_head(params, q: np.ndarray, k: np.ndarray, scale: Optional[float] = None):
+    """Selections of one Q head: ('vs', vert, slash), ('bs', list of B_b) or (pattern,)."""
+    n = q.shape[0]
+    if params.pattern == VERTICAL_SLASH:
+        L = min(params.last_q, n)
+        v_sc, s_sc = vs_scores(q[n - L:], k, scale)
+        return "vs", topk(v_sc, params.n_vertical), topk(s_sc, params.n_slash)
+    if params.pattern == BLOCK_SPARSE:
+        return "bs", bs_select(bs_scores(q, k), params.top_k_blocks)
+    return ("static",)
+
+
+def head_index(params, sel, n: int) -> List[BlockIndex]:
+    if params.pattern == VERTICAL_SLASH:
+        return vs_index(sel[1], sel[2], n)
+    if params.pattern == BLOCK_SPARSE:
+        return bs_index(sel[1])
+    if params.pattern == A_SHAPE:
+        return ashape_index(params.sink, params.window, n)
+    return dense_index(n)

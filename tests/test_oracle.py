@@ -1,0 +1,328 @@
+"""Pins of the float64 oracle against things other than itself.
+
+Each test ties one oracle function to a closed form, a library routine with a
+different code path (numpy's trace, torch's softmax / logsumexp /
+scaled-dot-product attention), brute force on tiny inputs, or a fixture worked
+by hand under tests/golden/.  A plausible slip in the oracle (a dropped term,
+an off-by-one in a span, a flipped diagonal sign, a transposed operand, a
+wrong tie-break) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.core import BM
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- softmax / VS scores
+def test_vs_rows_sum_to_one_and_causal_zeros():
+    r = rng(0)
+    n, L, d = 320, 64, 128
+    q = r.standard_normal((L, d))
+    k = r.standard_normal((n, d))
+    p = oracle.vs_probabilities(q, k)
+    assert np.all(np.abs(p.sum(axis=1) - 1.0) <= 1e-12)
+    for rr in range(L):
+        i = n - L + rr
+        assert np.all(p[rr, i + 1:] == 0.0)
+        assert np.all(p[rr, : i + 1] > 0.0)
+
+
+def test_vs_scores_zero_query_closed_form():
+    # q = 0: every allowed logit is 0, so P[i, j] = 1/(i+1) for j <= i.
+    n, L, d = 256, 64, 128
+    q = np.zeros((L, d))
+    k = rng(1).standard_normal((n, d))
+    v, s = oracle.vs_scores(q, k)
+    rows = range(n - L, n)
+    v_ref = np.array([sum(1.0 / (i + 1) for i in rows if i >= j) for j in range(n)])
+    s_ref = np.array([sum(1.0 / (i + 1) for i in rows if i - o >= 0) for o in range(n)])
+    np.testing.assert_allclose(v, v_ref, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(s, s_ref, rtol=1e-13, atol=0)
+
+
+def test_vs_scores_against_library_routines():
+    # torch.softmax over masked logits, column sums of the embedded [n, n]
+    # matrix and numpy's trace along each sub-diagonal (offset -o).
+    r = rng(2)
+    n, L, d = 200 + 56, 64, 128
+    q = r.standard_normal((L, d))
+    k = r.standard_normal((n, d))
+    v, s = oracle.vs_scores(q, k)
+    z = torch.from_numpy(q @ k.T / math.sqrt(d))
+    i = torch.arange(n - L, n)[:, None]
+    z = z.masked_fill(torch.arange(n)[None, :] > i, float("-inf"))
+    p = torch.softmax(z, dim=1).numpy()
+    full = np.zeros((n, n))
+    full[n - L:] = p
+    np.testing.assert_allclose(v, full.sum(axis=0), rtol=1e-12, atol=1e-15)
+    s_ref = np.array([np.trace(full, offset=-o) for o in range(n)])
+    np.testing.assert_allclose(s, s_ref, rtol=1e-12, atol=1e-15)
+
+
+def test_vs_one_hot_key_is_top_vertical():
+    r = rng(3)
+    n, L, d = 512, 64, 128
+    q = r.standard_normal((L, d)) * 0.1
+    k = r.standard_normal((n, d)) * 0.1
+    jstar = 77
+    k[jstar] = 40.0 * q.mean(axis=0) / np.linalg.norm(q.mean(axis=0))
+    v, s = oracle.vs_scores(q, k)
+    assert oracle.topk(v, 1).tolist() == [jstar]
+
+
+def test_vs_pure_diagonal_is_top_slash():
+    # Keys equal to their own query (large) make offset 0 dominate.
+    r = rng(4)
+    n, L, d = 512, 64, 128
+    qfull = r.standard_normal((n, d))
+    k = r.standard_normal((n, d)) * 0.05
+    k += 3.0 * qfull
+    v, s = oracle.vs_scores(qfull[n - L:], k)
+    assert oracle.topk(s, 1).tolist() == [0]
+
+
+# ---------------------------------------------------------------- top-k
+def _topk_brute(x, k):
+    x = list(map(float, x))
+    chosen = []
+    alive = set(range(len(x)))
+    for _ in range(min(k, len(x))):
+        best = None
+        for i in sorted(alive):
+            if best is None or x[i] > x[best]:
+                best = i
+        chosen.append(best)
+        alive.remove(best)
+    return sorted(chosen)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_brute_force_with_ties(seed):
+    r = rng(10 + seed)
+    n = int(r.integers(1, 300))
+    x = r.integers(-5, 6, size=n).astype(np.float64)   # many exact ties
+    for k in (0, 1, 7, n // 2, n, n + 3):
+        assert oracle.topk(x, k).tolist() == _topk_brute(x, k)
+
+
+def test_topk_signed_zero_and_ascending_output():
+    x = np.array([0.0, -0.0, 1.0, -0.0, 0.0, 2.0])
+    # -0 and +0 compare equal, so the lower indices win among the zeros.
+    assert oracle.topk(x, 3).tolist() == [0, 2, 5]
+    assert oracle.topk(x, 4).tolist() == [0, 1, 2, 5]
+
+
+# ---------------------------------------------------------------- Block-Sparse
+def _integer_blocks(coeffs, d=128, delta=0.25):
+    """Block b's rows are coeffs[b]*e1 plus +-delta*e2 in pairs; the mean is exactly coeffs[b]*e1."""
+    rows = []
+    for a in coeffs:
+        blk = np.zeros((BM, d))
+        blk[:, 0] = a
+        blk[0::2, 1] = delta
+        blk[1::2, 1] = -delta
+        rows.append(blk)
+    return np.concatenate(rows)
+
+
+def test_bs_integer_construction_hand_worked():
+    # Pooled means are exactly a_b e1, so S[b, c] = a_b * a_c.
+    qa = [1, 2, -1, 2, 0, 3]
+    ka = [1, 2, -1, 2, 0, 3]
+    q, k = _integer_blocks(qa), _integer_blocks(ka)
+    sc = oracle.bs_scores(q, k)
+    np.testing.assert_array_equal(oracle.bs_pool(q)[:, 0], qa)
+    np.testing.assert_array_equal(oracle.bs_pool(q)[:, 1], 0.0)
+    # Row b = 5: S = 3*[1, 2, -1, 2, 0, 3] = [3, 6, -3, 6, 0, 9].
+    np.testing.assert_array_equal(sc[5], [3, 6, -3, 6, 0, 9])
+    assert np.all(np.isneginf(sc[0, 1:]))
+    sel = oracle.bs_select(sc, 2)
+    # b=0: only c=0.  b=1: S=[2,4] -> both.  b=2: S=[-1,-2,1] -> {0,2}.
+    # b=3: S=[2,4,-2,4] -> 4 at c=1 and c=3 -> {1,3}.  b=4: S all 0 -> lowest {0,1}.
+    # b=5: 9 at c=5, then the tie 6 at c=1 and c=3 goes to c=1 -> {1,5}.
+    assert [s.tolist() for s in sel] == [[0], [0, 1], [0, 2], [1, 3], [0, 1], [1, 5]]
+    sel3 = oracle.bs_select(sc, 3)
+    assert sel3[5].tolist() == [1, 3, 5]
+
+
+def test_bs_pool_is_block_mean():
+    r = rng(20)
+    x = r.standard_normal((4 * BM, 128))
+    ref = np.stack([x[b * BM:(b + 1) * BM].sum(axis=0) / BM for b in range(4)])
+    np.testing.assert_allclose(oracle.bs_pool(x), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_bs_index_merges_consecutive_blocks():
+    ranges, cols = oracle.bs_block_index(np.array([0, 1, 3, 5, 6, 7, -1, -1]))
+    assert ranges.tolist() == [[0, 128], [192, 256], [320, 512]]
+    assert cols.size == 0
+
+
+# ---------------------------------------------------------------- index conversion
+def test_vs_index_golden_hand_worked():
+    g = json.load(open(os.path.join(GOLDEN, "vs_index_n512.json")))
+    idx = oracle.vs_index(np.array(g["vertical"]), np.array(g["slash"]), g["n"])
+    for blk in g["blocks"]:
+        r, c = idx[blk["b"]]
+        assert r.tolist() == blk["ranges"], blk
+        assert c.tolist() == blk["cols"], blk
+
+
+def test_ashape_index_golden_hand_worked():
+    g = json.load(open(os.path.join(GOLDEN, "ashape_index_n512.json")))
+    idx = oracle.ashape_index(g["sink"], g["window"], g["n"])
+    for blk in g["blocks"]:
+        assert idx[blk["b"]][0].tolist() == blk["ranges"], blk
+    rm = g["row_masks"][0]
+    b = rm["row"] // BM
+    m = oracle.block_mask(idx[b], b, g["n"], ashape=(g["sink"], g["window"]))[rm["row"] % BM]
+    kept = np.nonzero(m)[0]
+    assert kept.tolist() == list(range(rm["sink_kept"])) + list(range(rm["kept_lo"], rm["kept_hi"] + 1))
+
+
+def _vs_mask_by_definition(vert, slash, n):
+    """(i, j) kept iff j <= i and (j is a vertical, or some slash o reaching block(i)
+    has 64b - o <= j < 64b + 64 - o); built element by element."""
+    vert, slash = set(int(x) for x in vert), [int(x) for x in slash]
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        b = i // BM
+        row0 = b * BM
+        for j in range(i + 1):
+            keep = j in vert
+            if not keep:
+                for o in slash:
+                    if o <= row0 + BM - 1 and row0 - o <= j < row0 + BM - o:
+                        keep = True
+                        break
+            m[i, j] = keep
+    return m
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_vs_index_matches_elementwise_definition(seed):
+    r = rng(30 + seed)
+    n = 256
+    vert = np.sort(r.choice(n, size=int(r.integers(1, 12)), replace=False))
+    slash = np.sort(r.choice(n, size=int(r.integers(1, 10)), replace=False))
+    idx = oracle.vs_index(vert, slash, n)
+    ref = _vs_mask_by_definition(vert, slash, n)
+    got = np.concatenate([oracle.block_mask(idx[b], b, n) for b in range(n // BM)])
+    np.testing.assert_array_equal(got, ref)
+    # Canonical form: sorted, disjoint and non-touching ranges inside [0, 64b+64);
+    # columns ascending, causal for the block, and outside every range.
+    for b, (rg, cols) in enumerate(idx):
+        end = b * BM + BM
+        assert np.all(rg[:, 0] < rg[:, 1])
+        assert np.all(rg[1:, 0] > rg[:-1, 1])
+        assert np.all((rg >= 0) & (rg <= end))
+        assert np.all(np.diff(cols) > 0)
+        assert np.all(cols < end)
+        for j in cols:
+            assert not np.any((rg[:, 0] <= j) & (j < rg[:, 1]))
+
+
+def test_csr_round_trip():
+    r = rng(40)
+    n = 512
+    idx = oracle.vs_index(np.sort(r.choice(n, 9, replace=False)), np.sort(r.choice(n, 7, replace=False)), n)
+    back = oracle.csr_to_index(*oracle.index_to_csr(idx))
+    for (a, b), (c, d) in zip(idx, back):
+        np.testing.assert_array_equal(a, c)
+        np.testing.assert_array_equal(b, d)
+
+
+# ---------------------------------------------------------------- attention
+def _qkv(seed, n, d=128, scale=1.0):
+    r = rng(seed)
+    return (r.standard_normal((n, d)) * scale, r.standard_normal((n, d)) * scale,
+            r.standard_normal((n, d)))
+
+
+def test_dense_equals_torch_causal_sdpa():
+    n = 256
+    q, k, v = _qkv(50, n)
+    out, lse = oracle.attention_head(q, k, v, oracle.dense_index(n))
+    tq, tk, tv = (torch.from_numpy(x)[None, None] for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0, 0].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    z = torch.from_numpy(q @ k.T / math.sqrt(128)).masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_zero_query_gives_masked_mean_of_values():
+    # q = 0: all allowed logits tie, so out_i is the plain mean of v over row i's keys.
+    n = 512
+    _, k, v = _qkv(51, n)
+    q = np.zeros_like(k)
+    r = rng(52)
+    vert = np.sort(r.choice(n, 6, replace=False))
+    slash = np.sort(r.choice(n, 5, replace=False))
+    idx = oracle.vs_index(vert, slash, n)
+    out, lse = oracle.attention_head(q, k, v, idx)
+    mask = _vs_mask_by_definition(vert, slash, n)
+    for i in range(n):
+        js = np.nonzero(mask[i])[0]
+        if js.size == 0:
+            assert np.all(out[i] == 0) and np.isneginf(lse[i])
+        else:
+            np.testing.assert_allclose(out[i], v[js].mean(axis=0), rtol=1e-11, atol=1e-13)
+            assert abs(lse[i] - math.log(js.size)) < 1e-12
+
+
+def test_single_key_per_row_returns_own_value():
+    n = 256
+    q, k, v = _qkv(53, n)
+    out, _ = oracle.attention_head(q, k, v, oracle.ashape_index(0, 1, n), ashape=(0, 1))
+    np.testing.assert_array_equal(out, v)
+
+
+@pytest.mark.parametrize("case", ["ashape_wide", "bs_all", "vs_all_offsets"])
+def test_full_coverage_reduces_to_dense(case):
+    n = 320
+    q, k, v = _qkv(54, n)
+    ref, ref_lse = oracle.attention_head(q, k, v, oracle.dense_index(n))
+    if case == "ashape_wide":
+        out, lse = oracle.attention_head(q, k, v, oracle.ashape_index(0, n, n), ashape=(0, n))
+    elif case == "bs_all":
+        out, lse = oracle.attention_head(q, k, v, oracle.bs_index(oracle.bs_select(oracle.bs_scores(q, k), n // BM)))
+    else:
+        out, lse = oracle.attention_head(q, k, v, oracle.vs_index(np.arange(0), np.arange(n), n))
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_brute_force_masked_softmax():
+    # Full [n, n] masked softmax from the element-wise mask definition.
+    n = 256
+    q, k, v = _qkv(55, n)
+    r = rng(56)
+    vert = np.sort(r.choice(n, 10, replace=False))
+    slash = np.sort(r.choice(n, 4, replace=False))
+    out, _ = oracle.attention_head(q, k, v, oracle.vs_index(vert, slash, n))
+    mask = _vs_mask_by_definition(vert, slash, n)
+    z = torch.from_numpy(q @ k.T / math.sqrt(128)).masked_fill(~torch.from_numpy(mask), float("-inf"))
+    p = torch.softmax(z, dim=1).nan_to_num(0.0).numpy()
+    np.testing.assert_allclose(out, p @ v, rtol=1e-11, atol=1e-13)
+
+
+def test_attention_invariant_to_range_and_column_order():
+    n = 384
+    q, k, v = _qkv(57, n)
+    idx = oracle.vs_index(np.array([3, 90, 200, 333]), np.array([0, 40, 150]), n)
+    shuffled = [(rg[::-1].copy(), c[::-1].copy()) for rg, c in idx]
+    a, _ = oracle.attention_head(q, k, v, idx)
+    b, _ = oracle.attention_head(q, k, v, shuffled)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
