@@ -1,0 +1,609 @@
+// Host side of the C ABI declared in msattn.h: argument validation, the
+// layout of workspaces and of the index arena, and the launch sequence of
+// each call.  Nothing here allocates device memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "internal.h"
+
+namespace msa {
+namespace {
+
+thread_local std::string g_err;
+
+ms_status fail(ms_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ms_status device_fail(hipError_t e, const char* what) {
+  return fail(MS_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int64_t n = 0, nb = 0;
+  int hq = 0, hkv = 0, grp = 0;
+  float scale_log2 = 0.f;
+  int out_f32 = 0;
+  std::vector<ms_head_params> p;
+  int n_vs = 0, n_bs = 0;
+  std::vector<int> vs_slot, bs_slot;
+  std::vector<int16_t> vs_heads, bs_heads;       // Q heads by slot
+  std::vector<int16_t> bs_kv_heads;              // distinct KV heads read by BS heads
+  std::vector<int16_t> bs_kv_slot;               // per BS slot: index into bs_kv_heads
+  std::vector<int64_t> vert_off, slash_off, blk_off;
+  int64_t n_vert = 0, n_slash = 0, n_blocks = 0;
+  int ntiles = 0;
+  // estimation workspace (byte offsets)
+  size_t e_part = 0, e_stats = 0, e_diag = 0, e_v = 0, e_s = 0, e_qpool = 0, e_kpool = 0, e_scores = 0;
+  size_t est_bytes = 0;
+  // index arena
+  std::vector<int64_t> cap_r, cap_c;
+  std::vector<HeadDesc> desc;
+  size_t index_bytes = 0;
+  // attention workspace
+  size_t attn_bytes = 0;
+  // one-shot workspace
+  size_t o_vert = 0, o_slash = 0, o_blocks = 0, o_est = 0, o_index = 0, o_attn = 0, o_total = 0;
+};
+
+ms_status validate(const ms_problem* prob, const ms_head_params* params, bool need_params) {
+  if (!prob) return fail(MS_ERR_INVALID_ARG, "prob is null");
+  if (need_params && !params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  if (prob->head_dim != kD) return fail(MS_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", prob->head_dim);
+  if (prob->n < kBM || prob->n % kBM != 0)
+    return fail(MS_ERR_UNSUPPORTED, "n = %lld: must be a positive multiple of 64", (long long)prob->n);
+  if (prob->n > (int64_t{1} << 24)) return fail(MS_ERR_UNSUPPORTED, "n = %lld exceeds 2^24", (long long)prob->n);
+  if (prob->n_q_heads < 1 || prob->n_q_heads > kMaxHeads)
+    return fail(MS_ERR_INVALID_ARG, "n_q_heads = %d: must be 1..%d", prob->n_q_heads, kMaxHeads);
+  if (prob->n_kv_heads < 1 || prob->n_q_heads % prob->n_kv_heads != 0)
+    return fail(MS_ERR_INVALID_ARG, "n_kv_heads = %d must divide n_q_heads = %d", prob->n_kv_heads, prob->n_q_heads);
+  if (prob->out_dtype != MS_OUT_BF16 && prob->out_dtype != MS_OUT_F32)
+    return fail(MS_ERR_INVALID_ARG, "out_dtype = %d", prob->out_dtype);
+  if (prob->reserved != 0) return fail(MS_ERR_INVALID_ARG, "reserved must be 0");
+  if (!std::isfinite(prob->scale) || prob->scale < 0.f) return fail(MS_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (!need_params) return MS_OK;
+  const int64_t n = prob->n, nb = n / kBM;
+  for (int h = 0; h < prob->n_q_heads; ++h) {
+    const ms_head_params& q = params[h];
+    switch (q.pattern) {
+      case MS_VERTICAL_SLASH:
+        if (q.last_q != kLastQ) return fail(MS_ERR_UNSUPPORTED, "head %d: last_q = %d, only 64 is supported", h, q.last_q);
+        if (q.n_vertical < 0 || q.n_vertical > n) return fail(MS_ERR_INVALID_ARG, "head %d: n_vertical = %d out of 0..n", h, q.n_vertical);
+        if (q.n_slash < 0 || q.n_slash > n) return fail(MS_ERR_INVALID_ARG, "head %d: n_slash = %d out of 0..n", h, q.n_slash);
+        break;
+      case MS_BLOCK_SPARSE:
+        if (q.block != kBM) return fail(MS_ERR_UNSUPPORTED, "head %d: block = %d, only 64 is supported", h, q.block);
+        if (q.top_k_blocks < 1 || q.top_k_blocks > nb)
+          return fail(MS_ERR_INVALID_ARG, "head %d: top_k_blocks = %d out of 1..n/64", h, q.top_k_blocks);
+        break;
+      case MS_A_SHAPE:
+        if (q.sink < 0 || q.sink > n) return fail(MS_ERR_INVALID_ARG, "head %d: sink = %d out of 0..n", h, q.sink);
+        if (q.window < 1 || q.window > n) return fail(MS_ERR_INVALID_ARG, "head %d: window = %d out of 1..n", h, q.window);
+        break;
+      case MS_DENSE:
+        break;
+      default:
+        return fail(MS_ERR_INVALID_ARG, "head %d: pattern = %d", h, q.pattern);
+    }
+  }
+  return MS_OK;
+}
+
+// Per-head capacities of the CSR, the sums over query blocks of the bounds
+// the index kernels clamp to.
+std::pair<int64_t, int64_t> head_caps(const ms_head_params& q, int64_t nb) {
+  int64_t r = 0, c = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t last = b * kBM + kBM - 1;
+    switch (q.pattern) {
+      case MS_VERTICAL_SLASH:
+        r += std::min<int64_t>(q.n_slash, last / 65 + 1);
+        c += std::min<int64_t>(q.n_vertical, last + 1);
+        break;
+      case MS_BLOCK_SPARSE:
+        r += std::min<int64_t>(std::min<int64_t>(q.top_k_blocks, b + 1), b / 2 + 1);
+        break;
+      case MS_A_SHAPE:
+        r += 2;
+        break;
+      default:
+        r += 1;
+    }
+  }
+  return {r, c};
+}
+
+ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& P) {
+  const bool have_params = params != nullptr;
+  ms_status st = validate(prob, params, have_params);
+  if (st != MS_OK) return st;
+  P.n = prob->n;
+  P.nb = P.n / kBM;
+  P.hq = prob->n_q_heads;
+  P.hkv = prob->n_kv_heads;
+  P.grp = P.hq / P.hkv;
+  const float scale = prob->scale == 0.f ? 1.f / std::sqrt((float)kD) : prob->scale;
+  P.scale_log2 = scale * 1.4426950408889634f;
+  P.out_f32 = prob->out_dtype == MS_OUT_F32;
+  P.attn_bytes = align_up((size_t)P.hkv * (size_t)P.n * kD * 2);
+  if (!have_params) return MS_OK;
+  P.p.assign(params, params + P.hq);
+  P.vs_slot.assign(P.hq, -1);
+  P.bs_slot.assign(P.hq, -1);
+  P.vert_off.assign(P.hq, 0);
+  P.slash_off.assign(P.hq, 0);
+  P.blk_off.assign(P.hq, 0);
+  std::vector<int> kv_slot_of(P.hkv, -1);
+  for (int h = 0; h < P.hq; ++h) {
+    const ms_head_params& q = P.p[h];
+    if (q.pattern == MS_VERTICAL_SLASH) {
+      P.vs_slot[h] = P.n_vs++;
+      P.vs_heads.push_back((int16_t)h);
+      P.vert_off[h] = P.n_vert;
+      P.slash_off[h] = P.n_slash;
+      P.n_vert += q.n_vertical;
+      P.n_slash += q.n_slash;
+    } else if (q.pattern == MS_BLOCK_SPARSE) {
+      P.bs_slot[h] = P.n_bs++;
+      P.bs_heads.push_back((int16_t)h);
+      P.blk_off[h] = P.n_blocks;
+      P.n_blocks += P.nb * q.top_k_blocks;
+      const int kv = h / P.grp;
+      if (kv_slot_of[kv] < 0) {
+        kv_slot_of[kv] = (int)P.bs_kv_heads.size();
+        P.bs_kv_heads.push_back((int16_t)kv);
+      }
+      P.bs_kv_slot.push_back((int16_t)kv_slot_of[kv]);
+    }
+  }
+  // Estimation workspace.
+  P.ntiles = (int)((P.n + kVsTile - 1) / kVsTile);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const size_t f = sizeof(float);
+  P.e_part = take((size_t)P.n_vs * P.ntiles * kLastQ * 2 * f);
+  P.e_stats = take((size_t)P.n_vs * kLastQ * 2 * f);
+  P.e_diag = take((size_t)P.n_vs * P.ntiles * 320 * f);
+  P.e_v = take((size_t)P.n_vs * P.n * f);
+  P.e_s = take((size_t)P.n_vs * P.n * f);
+  P.e_qpool = take((size_t)P.n_bs * P.nb * kD * f);
+  P.e_kpool = take((size_t)P.bs_kv_heads.size() * P.nb * kD * f);
+  P.e_scores = take((size_t)P.n_bs * P.nb * P.nb * f);
+  P.est_bytes = std::max<size_t>(off, kAlign);
+  // Index arena: descriptor table, then each head's CSR.
+  off = align_up((size_t)kTableBytes);
+  P.cap_r.assign(P.hq, 0);
+  P.cap_c.assign(P.hq, 0);
+  P.desc.assign(P.hq, HeadDesc{});
+  std::map<std::tuple<int, int, int>, std::pair<int64_t, int64_t>> memo;
+  for (int h = 0; h < P.hq; ++h) {
+    const ms_head_params& q = P.p[h];
+    const int a = q.pattern == MS_VERTICAL_SLASH ? q.n_vertical : q.pattern == MS_BLOCK_SPARSE ? q.top_k_blocks : 0;
+    const int b = q.pattern == MS_VERTICAL_SLASH ? q.n_slash : 0;
+    const auto key = std::make_tuple(q.pattern, a, b);
+    auto it = memo.find(key);
+    if (it == memo.end()) it = memo.emplace(key, head_caps(q, P.nb)).first;
+    P.cap_r[h] = it->second.first;
+    P.cap_c[h] = it->second.second;
+    if (P.cap_r[h] >= (int64_t{1} << 31) || P.cap_c[h] >= (int64_t{1} << 31))
+      return fail(MS_ERR_UNSUPPORTED, "head %d: index capacity exceeds int32", h);
+    HeadDesc& d = P.desc[h];
+    d.pattern = q.pattern;
+    d.vs_slot = P.vs_slot[h];
+    d.bs_slot = P.bs_slot[h];
+    if (q.pattern == MS_VERTICAL_SLASH) {
+      d.p0 = q.n_vertical;
+      d.p1 = q.n_slash;
+    } else if (q.pattern == MS_BLOCK_SPARSE) {
+      d.p0 = q.top_k_blocks;
+    } else if (q.pattern == MS_A_SHAPE) {
+      d.p0 = q.sink;
+      d.p1 = q.window;
+    }
+    d.vert_off = P.vert_off[h];
+    d.slash_off = P.slash_off[h];
+    d.blk_off = P.blk_off[h];
+    d.rng_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    d.rng_off = (int64_t)take((size_t)P.cap_r[h] * 8);
+    d.col_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    d.col_off = (int64_t)take((size_t)P.cap_c[h] * 4);
+    d.run_off = (int64_t)take(q.pattern == MS_VERTICAL_SLASH ? (size_t)(q.n_slash + 1) * 4 : 4);
+  }
+  P.index_bytes = off;
+  // One-shot workspace.
+  off = 0;
+  P.o_vert = take((size_t)P.n_vert * 4);
+  P.o_slash = take((size_t)P.n_slash * 4);
+  P.o_blocks = take((size_t)P.n_blocks * 4);
+  P.o_est = take(P.est_bytes);
+  P.o_index = take(P.index_bytes);
+  P.o_attn = take(P.attn_bytes);
+  P.o_total = off;
+  return MS_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+ms_status check_tensor(const void* p, const char* name) {
+  if (!p) return fail(MS_ERR_INVALID_ARG, "%s is null", name);
+  if (!aligned(p, 16)) return fail(MS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MS_OK;
+}
+
+ms_status check_ws(const void* ws, size_t have, size_t need, const char* name) {
+  if (need == 0) return MS_OK;
+  if (!ws) return fail(MS_ERR_INVALID_ARG, "%s is null", name);
+  if (!aligned(ws, kAlign)) return fail(MS_ERR_INVALID_ARG, "%s is not 256-byte aligned", name);
+  if (have < need) return fail(MS_ERR_CAPACITY, "%s holds %zu bytes, %zu needed", name, have, need);
+  return MS_OK;
+}
+
+#define MS_TRY(x)                          \
+  do {                                     \
+    const ms_status st_ = (x);             \
+    if (st_ != MS_OK) return st_;          \
+  } while (0)
+#define HIP_TRY(x, what)                   \
+  do {                                     \
+    const hipError_t e_ = (x);             \
+    if (e_ != hipSuccess) return device_fail(e_, what); \
+  } while (0)
+
+// ---------------------------------------------------------------- stages
+ms_status run_estimate_vs(const Plan& P, const uint16_t* q, const uint16_t* k, int32_t* vert, int32_t* slash,
+                          float* dbg_v, float* dbg_s, char* ws, hipStream_t s) {
+  if (P.n_vs == 0) return MS_OK;
+  VsGroups g{};
+  for (int kv = 0; kv < P.hkv; ++kv) {
+    const int begin = g.q_begin[g.n_groups];
+    int cnt = 0;
+    for (int h = kv * P.grp; h < (kv + 1) * P.grp; ++h)
+      if (P.vs_slot[h] >= 0) {
+        g.q_head[begin + cnt] = (int16_t)h;
+        g.q_slot[begin + cnt] = (int16_t)P.vs_slot[h];
+        ++cnt;
+      }
+    if (cnt) {
+      g.kv_head[g.n_groups] = (int16_t)kv;
+      g.q_begin[g.n_groups + 1] = (int16_t)(begin + cnt);
+      ++g.n_groups;
+    }
+  }
+  float* v_sc = reinterpret_cast<float*>(ws + P.e_v);
+  float* s_sc = reinterpret_cast<float*>(ws + P.e_s);
+  HIP_TRY(launch_vs_estimate(q, k, P.n, P.hq, P.scale_log2, g, P.n_vs, reinterpret_cast<float*>(ws + P.e_part),
+                             reinterpret_cast<float*>(ws + P.e_stats), reinterpret_cast<float*>(ws + P.e_diag), v_sc,
+                             s_sc, s),
+          "vertical-slash estimation launch");
+  TopkJobs jv{}, js{};
+  for (int i = 0; i < P.n_vs; ++i) {
+    const int h = P.vs_heads[i];
+    jv.src_off[jv.count] = (int64_t)i * P.n;
+    jv.dst_off[jv.count] = P.vert_off[h];
+    jv.k[jv.count++] = P.p[h].n_vertical;
+    js.src_off[js.count] = (int64_t)i * P.n;
+    js.dst_off[js.count] = P.slash_off[h];
+    js.k[js.count++] = P.p[h].n_slash;
+  }
+  if (P.n_vert > 0) HIP_TRY(launch_topk_rows(v_sc, P.n, jv, vert, s), "vertical top-k launch");
+  if (P.n_slash > 0) HIP_TRY(launch_topk_rows(s_sc, P.n, js, slash, s), "slash top-k launch");
+  for (int i = 0; i < P.n_vs; ++i) {
+    const int h = P.vs_heads[i];
+    if (dbg_v)
+      HIP_TRY(hipMemcpyAsync(dbg_v + (int64_t)h * P.n, v_sc + (int64_t)i * P.n, P.n * 4, hipMemcpyDeviceToDevice, s),
+              "copy of vertical scores");
+    if (dbg_s)
+      HIP_TRY(hipMemcpyAsync(dbg_s + (int64_t)h * P.n, s_sc + (int64_t)i * P.n, P.n * 4, hipMemcpyDeviceToDevice, s),
+              "copy of slash scores");
+  }
+  return MS_OK;
+}
+
+ms_status run_estimate_block(const Plan& P, const uint16_t* q, const uint16_t* k, int32_t* blocks, float* dbg_scores,
+                             char* ws, hipStream_t s) {
+  if (P.n_bs == 0) return MS_OK;
+  float* qpool = reinterpret_cast<float*>(ws + P.e_qpool);
+  float* kpool = reinterpret_cast<float*>(ws + P.e_kpool);
+  float* scores = reinterpret_cast<float*>(ws + P.e_scores);
+  HIP_TRY(launch_bs_pool(q, P.n, P.bs_heads.data(), P.n_bs, qpool, s), "query pooling launch");
+  HIP_TRY(launch_bs_pool(k, P.n, P.bs_kv_heads.data(), (int)P.bs_kv_heads.size(), kpool, s), "key pooling launch");
+  HIP_TRY(launch_bs_scores(qpool, kpool, (int)P.nb, P.bs_kv_slot.data(), P.n_bs, scores, s), "block score launch");
+  std::vector<int32_t> kk(P.n_bs);
+  std::vector<int64_t> off(P.n_bs);
+  for (int i = 0; i < P.n_bs; ++i) {
+    kk[i] = P.p[P.bs_heads[i]].top_k_blocks;
+    off[i] = P.blk_off[P.bs_heads[i]];
+  }
+  HIP_TRY(launch_bs_select(scores, (int)P.nb, P.n_bs, kk.data(), off.data(), blocks, s), "block selection launch");
+  if (dbg_scores)
+    for (int i = 0; i < P.n_bs; ++i)
+      HIP_TRY(hipMemcpyAsync(dbg_scores + (int64_t)P.bs_heads[i] * P.nb * P.nb, scores + (int64_t)i * P.nb * P.nb,
+                             (size_t)P.nb * P.nb * 4, hipMemcpyDeviceToDevice, s),
+              "copy of block scores");
+  return MS_OK;
+}
+
+ms_status run_build_index(const Plan& P, const int32_t* vert, const int32_t* slash, const int32_t* blocks,
+                          char* index, hipStream_t s) {
+  HIP_TRY(launch_write_table(reinterpret_cast<HeadDesc*>(index), P.desc.data(), 0, P.hq, s), "index table launch");
+  HIP_TRY(launch_index_build(reinterpret_cast<const HeadDesc*>(index), index, P.hq, (int)P.nb, vert, slash, blocks, s),
+          "index build launch");
+  return MS_OK;
+}
+
+ms_status run_attention(const Plan& P, const void* q, const void* k, const void* v, const char* index, void* out,
+                        float* lse, char* attn_ws, hipStream_t s) {
+  _Float16* v16 = reinterpret_cast<_Float16*>(attn_ws);
+  HIP_TRY(launch_v_to_f16(static_cast<const uint16_t*>(v), v16, (int64_t)P.hkv * P.n * kD, s), "V conversion launch");
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v16 = v16;
+  a.out = out;
+  a.lse = lse;
+  a.table = reinterpret_cast<const HeadDesc*>(index);
+  a.arena = index;
+  a.n = P.n;
+  a.hq = P.hq;
+  a.hkv = P.hkv;
+  a.grp = P.grp;
+  a.nb = (int)P.nb;
+  a.scale_log2 = P.scale_log2;
+  a.out_f32 = P.out_f32;
+  HIP_TRY(launch_sparse_attn(a, s), "attention launch");
+  return MS_OK;
+}
+
+ms_status check_selection_ptrs(const Plan& P, const void* vert, const void* slash, const void* blocks, bool vs,
+                               bool bs) {
+  if (vs && P.n_vert > 0 && !vert) return fail(MS_ERR_INVALID_ARG, "vert is null but a Vertical-Slash head keeps verticals");
+  if (vs && P.n_slash > 0 && !slash) return fail(MS_ERR_INVALID_ARG, "slash is null but a Vertical-Slash head keeps slashes");
+  if (bs && P.n_blocks > 0 && !blocks) return fail(MS_ERR_INVALID_ARG, "blocks is null but a Block-Sparse head is present");
+  for (const void* p : {vert, slash, blocks})
+    if (p && !aligned(p, 4)) return fail(MS_ERR_INVALID_ARG, "selection arrays must be 4-byte aligned");
+  return MS_OK;
+}
+
+}  // namespace
+}  // namespace msa
+
+using namespace msa;
+
+extern "C" {
+
+const char* ms_status_string(ms_status s) {
+  switch (s) {
+    case MS_OK: return "ok";
+    case MS_ERR_INVALID_ARG: return "invalid argument";
+    case MS_ERR_UNSUPPORTED: return "unsupported";
+    case MS_ERR_CAPACITY: return "insufficient capacity";
+    case MS_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* ms_last_error(void) { return g_err.c_str(); }
+
+int32_t ms_version(void) { return 10000; }
+
+ms_status ms_validate(const ms_problem* prob, const ms_head_params* params) {
+  g_err.clear();
+  Plan P;
+  return make_plan(prob, params, P);
+}
+
+ms_status ms_selection_sizes(const ms_problem* prob, const ms_head_params* params, int64_t* n_vert, int64_t* n_slash,
+                             int64_t* n_blocks) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  if (n_vert) *n_vert = P.n_vert;
+  if (n_slash) *n_slash = P.n_slash;
+  if (n_blocks) *n_blocks = P.n_blocks;
+  return MS_OK;
+}
+
+ms_status ms_estimate_workspace_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes) {
+  g_err.clear();
+  if (!params || !bytes) return fail(MS_ERR_INVALID_ARG, "params and bytes must be non-null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  *bytes = P.est_bytes;
+  return MS_OK;
+}
+
+ms_status ms_index_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes) {
+  g_err.clear();
+  if (!params || !bytes) return fail(MS_ERR_INVALID_ARG, "params and bytes must be non-null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  *bytes = P.index_bytes;
+  return MS_OK;
+}
+
+ms_status ms_index_layout(const ms_problem* prob, const ms_head_params* params, int64_t* offsets, int64_t* caps) {
+  g_err.clear();
+  if (!params || !offsets || !caps) return fail(MS_ERR_INVALID_ARG, "params, offsets and caps must be non-null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  for (int h = 0; h < P.hq; ++h) {
+    offsets[4 * h + 0] = P.desc[h].rng_ptr_off;
+    offsets[4 * h + 1] = P.desc[h].rng_off;
+    offsets[4 * h + 2] = P.desc[h].col_ptr_off;
+    offsets[4 * h + 3] = P.desc[h].col_off;
+    caps[2 * h + 0] = P.cap_r[h];
+    caps[2 * h + 1] = P.cap_c[h];
+  }
+  return MS_OK;
+}
+
+ms_status ms_attn_workspace_bytes(const ms_problem* prob, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MS_ERR_INVALID_ARG, "bytes is null");
+  Plan P;
+  MS_TRY(make_plan(prob, nullptr, P));
+  *bytes = P.attn_bytes;
+  return MS_OK;
+}
+
+ms_status ms_workspace_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes) {
+  g_err.clear();
+  if (!params || !bytes) return fail(MS_ERR_INVALID_ARG, "params and bytes must be non-null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  *bytes = P.o_total;
+  return MS_OK;
+}
+
+ms_status ms_estimate_vs(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                         int32_t* vert, int32_t* slash, float* dbg_v, float* dbg_s, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  if (P.n_vs == 0) return MS_OK;
+  MS_TRY(check_tensor(q, "q"));
+  MS_TRY(check_tensor(k, "k"));
+  MS_TRY(check_selection_ptrs(P, vert, slash, nullptr, true, false));
+  if ((dbg_v && !aligned(dbg_v, 4)) || (dbg_s && !aligned(dbg_s, 4)))
+    return fail(MS_ERR_INVALID_ARG, "debug score arrays must be 4-byte aligned");
+  MS_TRY(check_ws(ws, ws_bytes, P.est_bytes, "ws"));
+  return run_estimate_vs(P, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vert, slash, dbg_v,
+                         dbg_s, static_cast<char*>(ws), stream);
+}
+
+ms_status ms_estimate_block(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                            int32_t* blocks, float* dbg_scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  if (P.n_bs == 0) return MS_OK;
+  MS_TRY(check_tensor(q, "q"));
+  MS_TRY(check_tensor(k, "k"));
+  MS_TRY(check_selection_ptrs(P, nullptr, nullptr, blocks, false, true));
+  if (dbg_scores && !aligned(dbg_scores, 4)) return fail(MS_ERR_INVALID_ARG, "dbg_scores must be 4-byte aligned");
+  MS_TRY(check_ws(ws, ws_bytes, P.est_bytes, "ws"));
+  return run_estimate_block(P, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), blocks, dbg_scores,
+                            static_cast<char*>(ws), stream);
+}
+
+ms_status ms_build_index(const ms_problem* prob, const ms_head_params* params, const int32_t* vert,
+                         const int32_t* slash, const int32_t* blocks, void* index, size_t index_bytes,
+                         hipStream_t stream) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  MS_TRY(check_selection_ptrs(P, vert, slash, blocks, true, true));
+  MS_TRY(check_ws(index, index_bytes, P.index_bytes, "index"));
+  return run_build_index(P, vert, slash, blocks, static_cast<char*>(index), stream);
+}
+
+ms_status ms_sparse_attn_indexed(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                                 const void* v, const void* index, size_t index_bytes, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  MS_TRY(check_tensor(q, "q"));
+  MS_TRY(check_tensor(k, "k"));
+  MS_TRY(check_tensor(v, "v"));
+  MS_TRY(check_tensor(out, "out"));
+  if (lse && !aligned(lse, 4)) return fail(MS_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  MS_TRY(check_ws(index, index_bytes, P.index_bytes, "index"));
+  MS_TRY(check_ws(ws, ws_bytes, P.attn_bytes, "ws"));
+  return run_attention(P, q, k, v, static_cast<const char*>(index), out, lse, static_cast<char*>(ws), stream);
+}
+
+ms_status ms_sparse_attn(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                         const void* v, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  MS_TRY(check_tensor(q, "q"));
+  MS_TRY(check_tensor(k, "k"));
+  MS_TRY(check_tensor(v, "v"));
+  MS_TRY(check_tensor(out, "out"));
+  if (lse && !aligned(lse, 4)) return fail(MS_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  MS_TRY(check_ws(ws, ws_bytes, P.o_total, "ws"));
+  char* w = static_cast<char*>(ws);
+  int32_t* vert = reinterpret_cast<int32_t*>(w + P.o_vert);
+  int32_t* slash = reinterpret_cast<int32_t*>(w + P.o_slash);
+  int32_t* blocks = reinterpret_cast<int32_t*>(w + P.o_blocks);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  MS_TRY(run_estimate_vs(P, qq, kk, vert, slash, nullptr, nullptr, w + P.o_est, stream));
+  MS_TRY(run_estimate_block(P, qq, kk, blocks, nullptr, w + P.o_est, stream));
+  MS_TRY(run_build_index(P, vert, slash, blocks, w + P.o_index, stream));
+  return run_attention(P, q, k, v, w + P.o_index, out, lse, w + P.o_attn, stream);
+}
+
+ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, const void* v, void* out, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err.clear();
+  Plan P;
+  MS_TRY(make_plan(prob, nullptr, P));
+  MS_TRY(check_tensor(q, "q"));
+  MS_TRY(check_tensor(k, "k"));
+  MS_TRY(check_tensor(v, "v"));
+  MS_TRY(check_tensor(out, "out"));
+  if (lse && !aligned(lse, 4)) return fail(MS_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  MS_TRY(check_ws(ws, ws_bytes, P.attn_bytes, "ws"));
+  _Float16* v16 = reinterpret_cast<_Float16*>(ws);
+  HIP_TRY(launch_v_to_f16(static_cast<const uint16_t*>(v), v16, (int64_t)P.hkv * P.n * kD, stream),
+          "V conversion launch");
+  AttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v16 = v16;
+  a.out = out;
+  a.lse = lse;
+  a.table = nullptr;
+  a.arena = nullptr;
+  a.n = P.n;
+  a.hq = P.hq;
+  a.hkv = P.hkv;
+  a.grp = P.grp;
+  a.nb = (int)P.nb;
+  a.scale_log2 = P.scale_log2;
+  a.out_f32 = P.out_f32;
+  HIP_TRY(launch_sparse_attn(a, stream), "attention launch");
+  return MS_OK;
+}
+
+ms_status ms_topk_f32(const float* x, int64_t n, int32_t k, int32_t* idx, hipStream_t stream) {
+  g_err.clear();
+  if (!x || !idx) return fail(MS_ERR_INVALID_ARG, "x and idx must be non-null");
+  if (n < 1 || n > (int64_t{1} << 30)) return fail(MS_ERR_INVALID_ARG, "n = %lld out of 1..2^30", (long long)n);
+  if (k < 0) return fail(MS_ERR_INVALID_ARG, "k = %d is negative", k);
+  if (!aligned(x, 4) || !aligned(idx, 4)) return fail(MS_ERR_INVALID_ARG, "x and idx must be 4-byte aligned");
+  TopkJobs j{};
+  j.count = 1;
+  j.src_off[0] = 0;
+  j.dst_off[0] = 0;
+  j.k[0] = k;
+  HIP_TRY(launch_topk_rows(x, n, j, idx, stream), "top-k launch");
+  return MS_OK;
+}
+
+}  // extern "C"

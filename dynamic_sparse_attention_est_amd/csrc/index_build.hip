@@ -1,0 +1,258 @@
+// Index conversion for gfx950: selected verticals / slashes / key blocks ->
+// per-query-block key ranges plus gathered column lists (the MInference
+// abstract: sparse indices built from each head's pattern; the PIT fragment:
+// sparse shapes do not line up with GPU tiles, so each 64-row query tile gets
+// the exact key spans it covers).
+//
+// Per head the index is a CSR over the n/64 query blocks:
+//   rng_ptr[NB+1], rng[] = (lo, hi) half-open key ranges, sorted, disjoint,
+//   non-touching; col_ptr[NB+1], col[] = ascending single keys in no range.
+// Query block b (rows 64b .. 64b+63, last = 64b+63):
+//   Vertical-Slash: slash o <= last keeps [max(0, 64b-o), 64b+64-o).  Sorted
+//     offsets whose gaps are <= 64 form runs; a run's spans merge into one
+//     range and different runs never touch, so per head the runs are found
+//     once (vs_template) and each block reads its ranges off them.  Vertical j
+//     <= last is a column unless some offset lies in [max(0, 64b-j), 64b+63-j].
+//   Block-Sparse: selected block c keeps [64c, 64c+64); consecutive c merge.
+//   A-shape: [0, min(sink, 64b+64)) and [max(0, 64b-window+1), 64b+64), merged
+//     when they touch (the per-row window is applied by the attention kernel).
+//   Dense: [0, 64b+64).
+// Three launches over (query block, head): count -> per-head scan -> fill.
+// Counts are clamped to per-block capacities that the host also uses to size
+// the arena, so malformed selections can never write past it, and every value
+// written is clamped into [0, 64b+64).
+#include "block_scan.h"
+#include "internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kT = 256;
+
+struct TableArgs {
+  HeadDesc d[32];
+};
+
+__global__ void write_table(HeadDesc* table, TableArgs ta, int count) {
+  const int i = threadIdx.x;
+  if (i < count) table[i] = ta.d[i];
+}
+
+__device__ __forceinline__ int upper_bound(const int32_t* a, int n, int x) {  // # of a[i] <= x
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int lower_bound(const int32_t* a, int n, int x) {  // # of a[i] < x
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Per-block capacities (same formulas as the host's arena sizing).
+__device__ __forceinline__ int cap_ranges(const HeadDesc& d, int b) {
+  const int last = b * kBM + kBM - 1;
+  switch (d.pattern) {
+    case MS_VERTICAL_SLASH: return min(d.p1, last / 65 + 1);
+    case MS_BLOCK_SPARSE: return min(min(d.p0, b + 1), b / 2 + 1);
+    case MS_A_SHAPE: return 2;
+    default: return 1;
+  }
+}
+__device__ __forceinline__ int cap_cols(const HeadDesc& d, int b) {
+  return d.pattern == MS_VERTICAL_SLASH ? min(d.p0, b * kBM + kBM) : 0;
+}
+
+struct IdxArgs {
+  const HeadDesc* table;
+  char* arena;
+  const int32_t* vert;
+  const int32_t* slash;
+  const int32_t* blocks;
+  int32_t nb;
+};
+
+// Runs of the sorted slash offsets (consecutive offsets closer than 65 share a
+// run): run[0] = number of runs, run[1 + r] = index of run r's first offset.
+__global__ __launch_bounds__(kT) void vs_template(IdxArgs a) {
+  __shared__ int warp_sum[kT / 64];
+  const HeadDesc d = a.table[blockIdx.x];
+  if (d.pattern != MS_VERTICAL_SLASH) return;
+  const int32_t* S = a.slash + d.slash_off;
+  int32_t* run = reinterpret_cast<int32_t*>(a.arena + d.run_off);
+  const int ks = d.p1;
+  int base = 0;
+  for (int s0 = 0; s0 < ks; s0 += kT) {
+    const int i = s0 + threadIdx.x;
+    const int start = i < ks && (i == 0 || S[i] - S[i - 1] > kBM);
+    int tot;
+    const int pos = base + block_excl_scan<kT>(start, warp_sum, &tot);
+    if (start) run[1 + pos] = i;
+    base += tot;
+  }
+  if (threadIdx.x == 0) run[0] = base;
+}
+
+// Ranges / columns of one (head, block), counted (kFill = false) or written.
+template <bool kFill>
+__global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
+  __shared__ int warp_sum[kT / 64];
+  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const HeadDesc d = a.table[h];
+  const int row0 = b * kBM, last = row0 + kBM - 1, end = row0 + kBM;
+  int32_t* rng_ptr = reinterpret_cast<int32_t*>(a.arena + d.rng_ptr_off);
+  int32_t* col_ptr = reinterpret_cast<int32_t*>(a.arena + d.col_ptr_off);
+  int2* rng = reinterpret_cast<int2*>(a.arena + d.rng_off);
+  int32_t* col = reinterpret_cast<int32_t*>(a.arena + d.col_off);
+  const int rcap = cap_ranges(d, b), ccap = cap_cols(d, b);
+  int nr = 0, nc = 0;
+  int rbase = 0, cbase = 0, rlim = 0, clim = 0;
+  if (kFill) {
+    rbase = rng_ptr[b];
+    rlim = rng_ptr[b + 1] - rbase;
+    cbase = col_ptr[b];
+    clim = col_ptr[b + 1] - cbase;
+  }
+
+  if (d.pattern == MS_VERTICAL_SLASH) {
+    const int32_t* S = a.slash + d.slash_off;
+    const int32_t* V = a.vert + d.vert_off;
+    const int32_t* run = reinterpret_cast<const int32_t*>(a.arena + d.run_off);
+    const int ks = d.p1, kv = d.p0, nruns = run[0];
+    const int ub = upper_bound(S, ks, last);            // offsets that reach this block
+    nr = ub == 0 ? 0 : upper_bound(run + 1, nruns, ub - 1);
+    nr = min(nr, rcap);
+    if (kFill) {
+      for (int p = tid; p < min(nr, rlim); p += kT) {
+        const int r = nr - 1 - p;  // runs of larger offsets give lower keys
+        const int first = run[1 + r];
+        const int stop = min(r + 1 < nruns ? run[2 + r] : ks, ub);
+        const int lo = min(max(0, row0 - S[stop - 1]), end);
+        const int hi = min(max(lo, row0 + kBM - S[first]), end);
+        rng[rbase + p] = make_int2(lo, hi);
+      }
+    }
+    const int ubv = upper_bound(V, kv, last);
+    int cnt = 0;
+    for (int s0 = 0; s0 < ubv; s0 += kT) {
+      const int i = s0 + tid;
+      int keep = 0;
+      int j = 0;
+      if (i < ubv) {
+        j = V[i];
+        const int lbo = lower_bound(S, ks, max(0, row0 - j));
+        keep = j >= 0 && !(lbo < ks && S[lbo] <= last - j);
+      }
+      int tot;
+      const int pos = cnt + block_excl_scan<kT>(keep, warp_sum, &tot);
+      if (kFill && keep && pos < clim) col[cbase + pos] = j;
+      cnt += tot;
+    }
+    nc = min(cnt, ccap);
+  } else if (d.pattern == MS_BLOCK_SPARSE) {
+    const int k = d.p0;
+    const int32_t* B = a.blocks + d.blk_off + (int64_t)b * k;
+    const int cnt = min(k, b + 1);  // leading entries hold the selection
+    int runs = 0;
+    for (int s0 = 0; s0 < cnt; s0 += kT) {
+      const int i = s0 + tid;
+      int start = 0, stop = 0, c = 0;
+      if (i < cnt) {
+        c = B[i];
+        start = i == 0 || B[i - 1] + 1 != c;
+        stop = i == cnt - 1 || B[i + 1] != c + 1;
+      }
+      int t1, t2;
+      const int ps = runs + block_excl_scan<kT>(start, warp_sum, &t1);
+      const int pe = runs + block_excl_scan<kT>(stop, warp_sum, &t2);
+      if (kFill) {
+        // A run's start and stop share its rank; write each half once.
+        if (start && ps < rlim) rng[rbase + ps].x = min(max(0, c * kBM), end);
+        if (stop && pe < rlim) rng[rbase + pe].y = min(max(0, c * kBM + kBM), end);
+      }
+      runs += t1;
+    }
+    nr = min(runs, rcap);
+  } else if (d.pattern == MS_A_SHAPE) {
+    const int sink = d.p0, window = d.p1;
+    const int wlo = max(0, row0 - window + 1);
+    const int shi = min(sink, end);
+    if (sink > 0 && wlo > shi) {
+      nr = 2;
+      if (kFill && tid == 0 && rlim >= 2) {
+        rng[rbase] = make_int2(0, shi);
+        rng[rbase + 1] = make_int2(wlo, end);
+      }
+    } else {
+      nr = 1;
+      if (kFill && tid == 0 && rlim >= 1) rng[rbase] = make_int2(sink > 0 ? 0 : wlo, end);
+    }
+  } else {  // dense
+    nr = 1;
+    if (kFill && tid == 0 && rlim >= 1) rng[rbase] = make_int2(0, end);
+  }
+
+  if (!kFill && tid == 0) {
+    rng_ptr[b + 1] = nr;
+    col_ptr[b + 1] = nc;
+    if (b == 0) {
+      rng_ptr[0] = 0;
+      col_ptr[0] = 0;
+    }
+  }
+}
+
+// In-place inclusive scan of ptr[1..nb] (ptr[0] = 0) for both CSR pointers.
+__global__ __launch_bounds__(1024) void index_scan(IdxArgs a) {
+  __shared__ int warp_sum[1024 / 64];
+  const HeadDesc d = a.table[blockIdx.x];
+  for (int which = 0; which < 2; ++which) {
+    int32_t* ptr = reinterpret_cast<int32_t*>(a.arena + (which ? d.col_ptr_off : d.rng_ptr_off));
+    int carry = 0;
+    for (int s0 = 0; s0 < a.nb; s0 += 1024) {
+      const int i = s0 + threadIdx.x;
+      const int x = i < a.nb ? ptr[1 + i] : 0;
+      int tot;
+      const int ex = block_excl_scan<1024>(x, warp_sum, &tot);
+      if (i < a.nb) ptr[1 + i] = carry + ex + x;
+      carry += tot;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_write_table(HeadDesc* table, const HeadDesc* host_descs, int first, int count, hipStream_t s) {
+  for (int c0 = 0; c0 < count; c0 += 32) {
+    TableArgs ta;
+    const int m = count - c0 < 32 ? count - c0 : 32;
+    for (int i = 0; i < m; ++i) ta.d[i] = host_descs[c0 + i];
+    hipLaunchKernelGGL(write_table, dim3(1), dim3(32), 0, s, table + first + c0, ta, m);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, const int32_t* vert,
+                              const int32_t* slash, const int32_t* blocks, hipStream_t s) {
+  IdxArgs a{table, arena, vert, slash, blocks, nb};
+  hipLaunchKernelGGL(vs_template, dim3((unsigned)hq), dim3(kT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(index_pass<false>, dim3((unsigned)nb, (unsigned)hq), dim3(kT), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(index_scan, dim3((unsigned)hq), dim3(1024), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(index_pass<true>, dim3((unsigned)nb, (unsigned)hq), dim3(kT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace msa

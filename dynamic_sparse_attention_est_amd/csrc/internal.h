@@ -1,0 +1,103 @@
+// Internal declarations shared by the host dispatcher and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msattn.h"
+
+namespace msa {
+
+constexpr int kD = 128;        // head dimension
+constexpr int kBM = 64;        // query rows per query block; Block-Sparse pooling block
+constexpr int kLastQ = 64;     // rows scored by the Vertical-Slash estimator
+constexpr int kMaxHeads = 128; // Q heads per call
+constexpr int kVsTile = 256;   // keys per workgroup in the Vertical-Slash estimator
+constexpr int kVsDiag = kVsTile + kLastQ - 1;  // diagonals touched by one estimator tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Per-Q-head record at the start of the index arena (written by a small
+// kernel from kernel arguments, read by the index builders and attention).
+struct HeadDesc {
+  int32_t pattern;
+  int32_t p0, p1;    // VS: n_vertical, n_slash.  BS: top_k, -.  A: sink, window
+  int32_t vs_slot;   // rank among VS heads (-1 if not VS)
+  int32_t bs_slot;   // rank among BS heads (-1 if not BS)
+  int32_t pad0, pad1, pad2;
+  int64_t vert_off;  // int32 elements into the packed vert array (VS)
+  int64_t slash_off; // into the packed slash array (VS)
+  int64_t blk_off;   // into the packed blocks array (BS)
+  int64_t rng_ptr_off, rng_off, col_ptr_off, col_off, run_off;  // bytes from arena base
+};
+static_assert(sizeof(HeadDesc) == 96, "HeadDesc layout");
+constexpr int64_t kTableBytes = (int64_t)kMaxHeads * sizeof(HeadDesc);
+
+// ------------------------------------------------------------------ launchers
+// Every launcher enqueues on `s` and returns hipGetLastError().
+
+// Writes `count` descriptors at table[first..first+count).
+hipError_t launch_write_table(HeadDesc* table, const HeadDesc* host_descs, int first, int count, hipStream_t s);
+
+// Vertical-Slash estimation.
+struct VsGroups {
+  int32_t n_groups;                 // KV heads that serve at least one VS head
+  int16_t kv_head[kMaxHeads];       // per group
+  int16_t q_begin[kMaxHeads + 1];   // per group: range into q_head[]
+  int16_t q_head[kMaxHeads];        // VS Q heads, grouped by KV head
+  int16_t q_slot[kMaxHeads];        // their VS slot
+};
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int hq, float scale_log2,
+                              const VsGroups& groups, int n_vs, float* part_mz, float* stats, float* diag_part,
+                              float* v_scores, float* s_scores, hipStream_t s);
+
+// Block-Sparse estimation.
+hipError_t launch_bs_pool(const uint16_t* src, int64_t n, const int16_t* heads, int nheads, float* pooled,
+                          hipStream_t s);
+hipError_t launch_bs_scores(const float* qpool, const float* kpool, int nb, const int16_t* kv_slot_of_bs,
+                            int n_bs, float* scores, hipStream_t s);
+
+// Exact top-k (ties to the lower index, ascending output).
+struct TopkJobs {            // up to kMaxJobs problems in one launch
+  static constexpr int kMaxJobs = 128;
+  int32_t count;
+  int64_t src_off[kMaxJobs]; // float elements from the source base
+  int64_t dst_off[kMaxJobs]; // int32 elements from the destination base
+  int32_t k[kMaxJobs];
+};
+hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, hipStream_t s);
+// Block-Sparse selection: for every BS slot and query block b, top-min(k, b+1)
+// of scores[slot][b][0..b] into blocks (-1 padded to k).  k_of_slot and
+// dst_off_of_slot are host arrays of n_bs entries.
+hipError_t launch_bs_select(const float* scores, int nb, int n_bs, const int32_t* k_of_slot,
+                            const int64_t* dst_off_of_slot, int32_t* blocks, hipStream_t s);
+
+// Index conversion.
+hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, const int32_t* vert,
+                              const int32_t* slash, const int32_t* blocks, hipStream_t s);
+
+// Attention.
+hipError_t launch_v_to_f16(const uint16_t* v, _Float16* v16, int64_t elems, hipStream_t s);
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const _Float16* v16;
+  void* out;
+  float* lse;
+  const HeadDesc* table;   // null => implicit dense
+  const char* arena;
+  int64_t n;
+  int32_t hq, hkv, grp, nb;
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t out_f32;
+};
+hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+
+}  // namespace msa

@@ -1,0 +1,194 @@
+/*
+ * msattn.h -- C ABI of the MInference-style dynamic sparse pre-filling
+ * attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes (the pages this follows):
+ *   - MInference abstract (taxoreview listing): long-context attention falls
+ *     into three shapes, A-shape, Vertical-Slash and Block-Sparse; a pattern is
+ *     fixed per head offline, sparse indices are built per prompt at inference,
+ *     and attention is computed only over those indices.
+ *   - "MInference 1.0: Accelerating Pre-filling for Long-Context LLMs via
+ *     Dynamic Sparse Attention" (research.elamur.ai summary), section
+ *     "Summary": the three stages (offline pattern search, online index
+ *     estimation, sparse kernels); section "Key points": Vertical-Slash heads
+ *     score the last queries against every key, Block-Sparse heads mean-pool
+ *     queries and keys in 64-token blocks.
+ *   - PIT abstract fragment (same listing): sparse shapes and GPU tiles do not
+ *     line up, so the index must say which keys each query tile covers.
+ *
+ * Conventions for every call:
+ *   Layout.   Q is [H_q][n][128], K and V are [H_kv][n][128], out is
+ *             [H_q][n][128]; bfloat16, row-major, 16-byte aligned base
+ *             pointers.  Batch is 1; attention is causal (pre-filling).  Q head
+ *             h reads KV head h / (H_q / H_kv).
+ *   Memory.   Every tensor pointer is a device pointer owned by the caller.
+ *             The library allocates nothing and keeps no global state besides a
+ *             thread-local error string.  Workspaces and the index arena are
+ *             caller-allocated, sized by the *_bytes queries.
+ *   Errors.   Arguments are validated on the host before anything is enqueued;
+ *             an invalid call returns a status, writes nothing and enqueues
+ *             nothing.  MS_ERR_DEVICE carries the HIP message in ms_last_error().
+ *             Faults inside kernels surface at the caller's next stream sync.
+ *   Streams.  Every call enqueues on the given stream and returns at once; no
+ *             call synchronises the device or copies to the host.
+ *   Results.  Deterministic: identical inputs give bitwise-identical outputs.
+ */
+#ifndef MSATTN_H
+#define MSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MS_OK = 0,
+  MS_ERR_INVALID_ARG = 1, /* null/misaligned pointer, out-of-range parameter */
+  MS_ERR_UNSUPPORTED = 2, /* well-formed but outside this build (head_dim != 128, n % 64 != 0, ...) */
+  MS_ERR_CAPACITY = 3,    /* workspace or index arena smaller than the query returned */
+  MS_ERR_DEVICE = 4       /* a HIP launch failed; see ms_last_error() */
+} ms_status;
+
+/* Per-head sparse pattern (MInference abstract: the three shapes; DENSE is the
+ * full causal baseline). */
+typedef enum { MS_A_SHAPE = 0, MS_VERTICAL_SLASH = 1, MS_BLOCK_SPARSE = 2, MS_DENSE = 3 } ms_pattern;
+
+typedef enum { MS_OUT_BF16 = 0, MS_OUT_F32 = 1 } ms_out_dtype;
+
+/* One attention layer.  Limits of this build: head_dim == 128, n % 64 == 0,
+ * 64 <= n <= 16777216, 1 <= n_q_heads <= 128, n_kv_heads divides n_q_heads. */
+typedef struct {
+  int64_t n;          /* sequence length: rows of Q and of K/V */
+  int32_t n_q_heads;  /* H_q */
+  int32_t n_kv_heads; /* H_kv */
+  int32_t head_dim;   /* must be 128 */
+  float scale;        /* softmax scale on q.k; 0 selects 1/sqrt(head_dim) */
+  int32_t out_dtype;  /* ms_out_dtype */
+  int32_t reserved;   /* must be 0 */
+} ms_problem;
+
+/* Pattern and budgets of one Q head (the offline search's output; MInference
+ * 1.0 summary, "Summary", first stage).  Fields a pattern does not use are
+ * ignored. */
+typedef struct {
+  int32_t pattern;      /* ms_pattern */
+  int32_t last_q;       /* VS: last rows scored against all keys; must be 64 */
+  int32_t n_vertical;   /* VS: key columns kept, 0..n */
+  int32_t n_slash;      /* VS: diagonals kept, 0..n */
+  int32_t block;        /* BS: pooling block; must be 64 */
+  int32_t top_k_blocks; /* BS: key blocks kept per query block, 1..n/64 */
+  int32_t sink;         /* A-shape: initial keys kept, 0..n */
+  int32_t window;       /* A-shape: local causal window in keys, 1..n */
+} ms_head_params;
+
+/* `params` below always points to n_q_heads entries. */
+
+const char* ms_status_string(ms_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* ms_last_error(void);
+int32_t ms_version(void);
+
+/* Host-only check of a problem and its per-head parameters. */
+ms_status ms_validate(const ms_problem* prob, const ms_head_params* params);
+
+/* Sizes (in int32 elements) of the packed selection arrays:
+ *   vert  : for each VS head in head order, n_vertical ascending key indices j;
+ *   slash : for each VS head in head order, n_slash ascending offsets o = i - j;
+ *   blocks: for each BS head in head order, [n/64][top_k_blocks] ascending key
+ *           block indices per query block, padded with -1 (early query blocks
+ *           have fewer than top_k candidates).
+ * Heads of other patterns take no space. */
+ms_status ms_selection_sizes(const ms_problem* prob, const ms_head_params* params,
+                             int64_t* n_vert, int64_t* n_slash, int64_t* n_blocks);
+
+/* Workspace of ms_estimate_vs / ms_estimate_block (same buffer serves both). */
+ms_status ms_estimate_workspace_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes);
+
+/* Index arena of ms_build_index: worst-case size, fixed by the parameters (no
+ * device round trip).  Per head it holds a CSR over the n/64 query blocks:
+ *   rng_ptr[n/64+1] int32, rng[2*R] int32 pairs [lo, hi) of key ranges,
+ *   col_ptr[n/64+1] int32, col[C] int32 single key columns.
+ * ms_index_layout() returns, for each Q head h, the byte offsets
+ *   offsets[4h+0] rng_ptr, [4h+1] rng, [4h+2] col_ptr, [4h+3] col
+ * from the arena base, and the capacities caps[2h+0] = R_max, caps[2h+1] = C_max
+ * (both arrays caller-owned host memory).  Ranges of a query block are sorted,
+ * disjoint and non-touching; columns are ascending and lie in no range. */
+ms_status ms_index_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes);
+ms_status ms_index_layout(const ms_problem* prob, const ms_head_params* params,
+                          int64_t* offsets, int64_t* caps);
+
+/* Workspace of the attention kernels (an fp16 copy of V). */
+ms_status ms_attn_workspace_bytes(const ms_problem* prob, size_t* bytes);
+
+/* Workspace of the one-shot ms_sparse_attn (estimation + index + attention). */
+ms_status ms_workspace_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes);
+
+/* Online Vertical-Slash estimation for every VS head (MInference 1.0 summary,
+ * "Key points": the last queries scored against all keys).  For rows
+ * i in [n-64, n): p_ij = softmax over j <= i of scale * q_i.k_j; vertical
+ * scores v_j = sum_i p_ij; slash scores s_o = sum_i p_{i,i-o}.  The top
+ * n_vertical of v and top n_slash of s are written ascending to vert/slash
+ * (packed, see ms_selection_sizes); equal scores go to the lower index.
+ * dbg_v / dbg_s (nullable, fp32 [H_q][n]) receive the scores of VS heads.
+ * q, k: device bf16.  ws: device, >= ms_estimate_workspace_bytes. */
+ms_status ms_estimate_vs(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                         int32_t* vert, int32_t* slash, float* dbg_v, float* dbg_s,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Online Block-Sparse estimation for every BS head (MInference 1.0 summary,
+ * "Key points": 64-token mean pooling).  S_bc = mean(q over block b) .
+ * mean(k over block c) for c <= b, in fp32; the top min(top_k, b+1) key
+ * blocks per query block go to `blocks` ascending, -1 padded.  dbg_scores
+ * (nullable, fp32 [H_q][n/64][n/64]) receives S of BS heads, -inf above the
+ * diagonal. */
+ms_status ms_estimate_block(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                            int32_t* blocks, float* dbg_scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Index conversion (MInference abstract: sparse indices from the assigned
+ * pattern; PIT fragment: tile coverage).  Per Q head and 64-row query block b:
+ *   VS: each slash o <= 64b+63 keeps keys [max(0, 64b-o), 64b+64-o); spans that
+ *       overlap or touch merge into ranges; verticals j <= 64b+63 outside every
+ *       range become columns.
+ *   BS: selected key blocks c give [64c, 64c+64), consecutive ones merged.
+ *   A-shape: [0, min(sink, 64b+64)) and [max(0, 64b-window+1), 64b+64), merged.
+ *   DENSE: [0, 64b+64).
+ * vert/slash/blocks: device arrays as written by the estimators (may be null
+ * when no head needs them).  index: device arena of >= ms_index_bytes. */
+ms_status ms_build_index(const ms_problem* prob, const ms_head_params* params, const int32_t* vert,
+                         const int32_t* slash, const int32_t* blocks, void* index, size_t index_bytes,
+                         hipStream_t stream);
+
+/* Sparse attention over a built index (MInference 1.0 summary, "Summary",
+ * third stage).  Row i of head h attends key j iff j <= i, j lies in a range
+ * or column of block i/64, and, for A-shape heads, j < sink or i - j < window.
+ * out_i = sum_j softmax_j(scale * q_i.k_j) v_j; a row with no key gives 0.
+ * out: bf16 or fp32 per prob->out_dtype.  lse (nullable, fp32 [H_q][n]):
+ * natural-log log-sum-exp of the scaled logits, -inf for empty rows.
+ * ws: >= ms_attn_workspace_bytes.  Precondition: |v| < 65504 (V is staged as
+ * fp16 for the P.V product). */
+ms_status ms_sparse_attn_indexed(const ms_problem* prob, const ms_head_params* params, const void* q,
+                                 const void* k, const void* v, const void* index, size_t index_bytes, void* out,
+                                 float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One layer end to end: estimation, index conversion and sparse attention.
+ * ws: >= ms_workspace_bytes (holds selections, the index and the V copy). */
+ms_status ms_sparse_attn(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
+                         const void* v, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Full causal attention with the same kernel and no index (the baseline the
+ * speedups are measured against).  ws: >= ms_attn_workspace_bytes. */
+ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, const void* v, void* out,
+                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Test hook of the selection kernel: the k largest of x[0..n) (device fp32),
+ * ties to the lower index, written ascending to idx[0..min(k, n)) (device).
+ * -0.0 ranks equal to +0.0; x must hold no NaN.  1 <= n <= 2^30, 0 <= k. */
+ms_status ms_topk_f32(const float* x, int64_t n, int32_t k, int32_t* idx, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSATTN_H */

@@ -1,0 +1,314 @@
+"""GPU parity against the float64 oracle, stage by stage, through the C ABI.
+
+Protocol (the oracle decides; readings R9 and R11 of the design notes):
+  scores     GPU fp32 scores agree with the oracle's float64 scores to 1e-5
+             relative (with a tiny absolute floor for scores near zero);
+  selection  bit-exact: the oracle's top-k run on the GPU's own scores equals
+             the GPU's selection (checks selection and tie-break exactly), and
+             the oracle's own selection equals the GPU's up to swaps inside the
+             certified near-tie band of the k-th score;
+  index      bit-exact: the oracle's index conversion of the GPU's selections
+             equals the GPU's CSR;
+  attention  the oracle's attention over that index vs the GPU output:
+             max |err| <= 2e-2, sum|err| / sum|ref| <= 1e-3 against the
+             bf16-rounded oracle, every row's relative L2 error <= 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_est_amd as ms
+import oracle
+import workloads as W
+from gpu_common import (Staged, ashape_of, bf16_round, check_attention, f64, kv_of, make, mean_rel,
+                        oracle_index, run_staged, selections)
+
+pytestmark = pytest.mark.gpu
+
+SCORE_RTOL = 1e-5
+
+
+def _score_check(got, ref, what):
+    floor = 1e-7 * max(np.abs(ref).max(), 1e-30)
+    bad = np.abs(got - ref) > SCORE_RTOL * np.abs(ref) + floor
+    assert not bad.any(), f"{what}: {bad.sum()} scores off, worst {np.abs(got - ref)[bad].max():.3e}"
+    return float(np.max(np.abs(got - ref) / (np.abs(ref) + floor)))
+
+
+def _near_tie_ok(gpu_sel, ref_sel, ref_scores, gpu_scores, k):
+    """End-to-end selection: equal, or differing only inside the certified band."""
+    a, b = set(gpu_sel.tolist()), set(ref_sel.tolist())
+    if a == b:
+        return 0
+    delta = 2.0 * float(np.max(np.abs(gpu_scores - ref_scores)))
+    kth = np.sort(ref_scores)[::-1][min(k, len(ref_scores)) - 1]
+    for j in a ^ b:
+        assert abs(ref_scores[j] - kth) <= delta, f"index {j} differs beyond the near-tie band"
+    return len(a ^ b) // 2
+
+
+def _host(st: Staged):
+    return f64(st.q), f64(st.k), f64(st.v)
+
+
+# ---------------------------------------------------------------- top-k hook
+@pytest.mark.parametrize("n,k,seed", [(1, 1, 0), (7, 3, 1), (513, 0, 2), (513, 600, 3), (4096, 256, 4),
+                                      (100003, 1000, 5), (262144, 6096, 6)])
+def test_topk_hook_bit_exact(n, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randint(-50, 50, (n,), generator=g).float() * 0.125     # many exact ties
+    x[torch.randint(0, n, (max(1, n // 10),), generator=g)] = -0.0
+    idx = torch.full((max(k, 1),), -5, dtype=torch.int32, device="cuda")
+    ms.ms_topk_f32(x.cuda(), k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()[:min(k, n)]
+    ref = oracle.topk(x.numpy().astype(np.float64), k)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_topk_hook_continuous_scores():
+    x = torch.rand(1 << 20, generator=torch.Generator().manual_seed(9))
+    idx = torch.empty(6096, dtype=torch.int32, device="cuda")
+    ms.ms_topk_f32(x.cuda(), 6096, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(x.numpy().astype(np.float64), 6096))
+
+
+# ---------------------------------------------------------------- Vertical-Slash estimation
+@pytest.mark.parametrize("n,hq,hkv", [(1024, 4, 2), (832, 2, 1), (2048, 1, 1)])
+def test_vs_estimation(n, hq, hkv):
+    w = W.custom("vs_small", n, hq, hkv, [W.vs(64, 96)] * hq, recipe="vs_planted", n_planted=6, seed=n)
+    st = run_staged(make(w))
+    q, k, _ = _host(st)
+    sel = selections(st)
+    dv, ds = st.dbg_v.cpu().numpy().astype(np.float64), st.dbg_s.cpu().numpy().astype(np.float64)
+    for h in range(hq):
+        v_ref, s_ref = oracle.vs_scores(q[h, n - 64:], k[kv_of(w, h)])
+        _score_check(dv[h], v_ref, f"head {h} vertical scores")
+        _score_check(ds[h], s_ref, f"head {h} slash scores")
+        _, gv, gs = sel[h]
+        np.testing.assert_array_equal(gv, oracle.topk(dv[h], 64))
+        np.testing.assert_array_equal(gs, oracle.topk(ds[h], 96))
+        _near_tie_ok(gv, oracle.topk(v_ref, 64), v_ref, dv[h], 64)
+        _near_tie_ok(gs, oracle.topk(s_ref, 96), s_ref, ds[h], 96)
+
+
+def test_vs_estimation_zero_query_closed_form():
+    # q = 0: p_ij = 1/(i+1); the scores are harmonic partial sums.
+    n = 512
+    w = W.custom("vs_zero", n, 1, 1, [W.vs(16, 16)])
+    q, k, v = W.generate(w, device="cuda")
+    q.zero_()
+    st = run_staged(make(w, qkv=(q, k, v)))
+    rows = np.arange(n - 64, n)
+    v_ref = np.array([np.sum(1.0 / (rows[rows >= j] + 1)) for j in range(n)])
+    s_ref = np.array([np.sum(1.0 / (rows[rows >= o] + 1)) for o in range(n)])
+    _score_check(st.dbg_v[0].cpu().numpy().astype(np.float64), v_ref, "vertical")
+    _score_check(st.dbg_s[0].cpu().numpy().astype(np.float64), s_ref, "slash")
+
+
+# ---------------------------------------------------------------- Block-Sparse estimation
+def test_bs_estimation():
+    n, k = 2048, 5
+    w = W.custom("bs_small", n, 2, 1, [W.bs(k)] * 2, recipe="vs_planted", seed=3)
+    st = run_staged(make(w))
+    q, kk, _ = _host(st)
+    sel = selections(st)
+    sc = st.dbg_scores.cpu().numpy().astype(np.float64)
+    for h in range(2):
+        ref = oracle.bs_scores(q[h], kk[0])
+        lower = np.tril(np.ones_like(ref, dtype=bool))
+        assert np.all(np.isneginf(sc[h][~lower]))
+        # Dot products of pooled means: compare against the size of the terms.
+        scale = np.abs(oracle.bs_pool(q[h])) @ np.abs(oracle.bs_pool(kk[0])).T
+        err = np.abs(sc[h][lower] - ref[lower]) / (scale[lower] + 1e-30)
+        assert err.max() <= 1e-5, err.max()
+        rows = sel[h][2]
+        for b in range(w.nb):
+            np.testing.assert_array_equal(rows[b][: min(k, b + 1)], oracle.topk(sc[h][b, : b + 1], k))
+            assert np.all(rows[b][min(k, b + 1):] == -1)
+
+
+def test_bs_integer_construction_exact():
+    # Pooled means are exact (constant rows a_b e1 plus +-0.25 e2 pairs), so
+    # S[b, c] = a_b a_c exactly and the selection, ties included, is known.
+    a = [1, 2, -1, 2, 0, 3, 1, 1]
+    n = 64 * len(a)
+    blk = np.zeros((n, 128), dtype=np.float32)
+    for b, x in enumerate(a):
+        blk[64 * b:64 * b + 64, 0] = x
+        blk[64 * b:64 * b + 64:2, 1] = 0.25
+        blk[64 * b + 1:64 * b + 64:2, 1] = -0.25
+    t = torch.from_numpy(blk).to(torch.bfloat16)[None].cuda()
+    w = W.custom("bs_int", n, 1, 1, [W.bs(2)])
+    st = run_staged(make(w, qkv=(t.clone(), t.clone(), t.clone())))
+    sc = st.dbg_scores[0].cpu().numpy()
+    for b in range(len(a)):
+        for c in range(b + 1):
+            assert sc[b, c] == a[b] * a[c]
+    rows = selections(st)[0][2]
+    # b=5: S = [3,6,-3,6,0,9] -> 9 at c=5, then the tie 6 at c=1 / c=3 goes to c=1.
+    # b=6, 7: S = [1,2,-1,2,0,3,1(,1)] -> 3 at c=5, then 2 at c=1 (tie with c=3).
+    # b=4: S = 0 everywhere -> the two lowest blocks.  b=0: one candidate, then -1.
+    assert rows[5].tolist() == [1, 5]
+    assert rows[6].tolist() == [1, 5]
+    assert rows[7].tolist() == [1, 5]
+    assert rows[0].tolist() == [0, -1]
+    assert rows[4].tolist() == [0, 1]
+
+
+# ---------------------------------------------------------------- index conversion
+def _upload(x, dtype=torch.int32):
+    return torch.as_tensor(np.asarray(x), dtype=dtype).cuda()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_index_from_given_selections_bit_exact(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = 64 * 37  # ragged against every tile size used on the GPU
+    nb = n // 64
+    heads = [W.vs(40, 60), W.vs(0, 5), W.vs(7, 0), W.bs(9), W.ashape(70, 200), W.ashape(0, 1), W.dense(),
+             W.vs(n, 3)]
+    w = W.custom("idx", n, len(heads), 1, heads)
+    prob, hp = ms.problem(n, len(heads), 1), ms.head_params(heads)
+    verts, slashes, blocks, sels = [], [], [], []
+    for h in heads:
+        if h.pattern == W.VERTICAL_SLASH:
+            vv = np.sort(rng.choice(n, h.n_vertical, replace=False))
+            # half the offsets crowd below 200, so runs, touching spans and
+            # clipping at key 0 all occur; the rest are spread out
+            small = rng.choice(200, min(h.n_slash // 2, 200), replace=False)
+            rest = rng.choice(np.setdiff1d(np.arange(n), small), h.n_slash - len(small), replace=False)
+            ss = np.sort(np.concatenate([small, rest]))
+            verts.append(vv)
+            slashes.append(ss)
+            sels.append(("vs", vv, ss))
+        elif h.pattern == W.BLOCK_SPARSE:
+            rows = np.full((nb, h.top_k_blocks), -1)
+            bl = []
+            for b in range(nb):
+                c = np.sort(rng.choice(b + 1, min(h.top_k_blocks, b + 1), replace=False))
+                rows[b, : len(c)] = c
+                bl.append(c)
+            blocks.append(rows.ravel())
+            sels.append(("bs", bl))
+        else:
+            sels.append(("static",))
+    vert = _upload(np.concatenate(verts)) if verts else None
+    slash = _upload(np.concatenate(slashes)) if slashes else None
+    blk = _upload(np.concatenate(blocks)) if blocks else None
+    index = ms.empty_workspace(ms.ms_index_bytes(prob, hp))
+    ms.ms_build_index(prob, hp, vert, slash, blk, index)
+    torch.cuda.synchronize()
+    got = ms.read_index(prob, hp, index)
+    for h, hd in enumerate(heads):
+        ref = oracle.index_to_csr(oracle.head_index(hd, sels[h], n))
+        for name, g_arr, r_arr in zip(("rng_ptr", "rng", "col_ptr", "col"), got[h], ref):
+            np.testing.assert_array_equal(g_arr, r_arr, err_msg=f"head {h} ({hd.pattern}) {name}")
+
+
+# ---------------------------------------------------------------- attention
+def _attention_check(st: Staged, blocks=None, bf16_out=True):
+    w = st.w
+    q, k, v = _host(st)
+    idx = ms.read_index(st.prob, st.hp, st.index)
+    sel = selections(st)
+    out = f64(st.out)
+    lse = st.lse.cpu().numpy().astype(np.float64) if st.lse is not None else None
+    for h in range(w.n_q_heads):
+        ref_idx = oracle.index_to_csr(oracle_index(w, h, sel[h]))
+        for g_arr, r_arr in zip(idx[h], ref_idx):
+            np.testing.assert_array_equal(g_arr, r_arr)
+        bidx = oracle.csr_to_index(*idx[h])
+        kv = kv_of(w, h)
+        ro, rl = oracle.attention_head(q[h], k[kv], v[kv], bidx, ashape=ashape_of(w.heads[h]), blocks=blocks)
+        rows = np.isfinite(ro[:, 0])
+        check_attention(out[h][rows], ro[rows], f"head {h} pattern {w.heads[h].pattern}", bf16_out)
+        if lse is not None:
+            fin = rows & np.isfinite(rl)
+            assert np.all(np.isneginf(lse[h][rows & ~np.isfinite(rl)]))
+            np.testing.assert_allclose(lse[h][fin], rl[fin], rtol=0, atol=2e-4)
+
+
+def test_attention_mixed_patterns_gqa():
+    n = 1024
+    heads = [W.vs(48, 80), W.bs(6), W.ashape(40, 150), W.dense(), W.vs(5, 2), W.ashape(0, 64), W.bs(1), W.vs(300, 500)]
+    w = W.custom("mixed_small", n, 8, 2, heads, recipe="vs_planted", seed=11)
+    _attention_check(run_staged(make(w)))
+
+
+def test_attention_f32_output_mode_unrounded():
+    n = 768
+    heads = [W.vs(32, 64), W.bs(4), W.ashape(16, 100), W.dense()]
+    w = W.custom("f32_out", n, 4, 4, heads, recipe="vs_planted", seed=12)
+    _attention_check(run_staged(make(w, out_dtype=ms.OUT_F32)), bf16_out=False)
+
+
+def test_empty_rows_give_zero_and_neg_inf_lse():
+    # Slash 300 first reaches block 4 (rows 256..319) and the only vertical is
+    # key 400, so blocks 0..3 keep no key at all.
+    n = 512
+    w = W.custom("empty", n, 1, 1, [W.vs(1, 1)])
+    st = make(w)
+    prob, hp = st.prob, st.hp
+    vert, slash = _upload([400]), _upload([300])
+    index = ms.empty_workspace(ms.ms_index_bytes(prob, hp))
+    ms.ms_build_index(prob, hp, vert, slash, None, index)
+    out = torch.full(st.q.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, n), device="cuda")
+    ms.ms_sparse_attn_indexed(prob, hp, st.q, st.k, st.v, index, out, ms.empty_workspace(ms.ms_attn_workspace_bytes(prob)), lse)
+    torch.cuda.synchronize()
+    o, l = f64(out)[0], lse.cpu().numpy()[0]
+    assert np.all(o[:256] == 0) and np.all(np.isneginf(l[:256]))
+    q, k, v = _host(st)
+    bidx = oracle.vs_index(np.array([400]), np.array([300]), n)
+    ro, rl = oracle.attention_head(q[0], k[0], v[0], bidx)
+    check_attention(o[256:], ro[256:], "later rows")
+
+
+def test_dense_attention():
+    n = 1024
+    w = W.custom("dense", n, 4, 2, [W.dense()] * 4, recipe="vs_planted", seed=13)
+    st = make(w)
+    out = torch.empty_like(st.q)
+    lse = torch.empty((4, n), device="cuda")
+    ms.ms_dense_attn(st.prob, st.q, st.k, st.v, out, ms.empty_workspace(ms.ms_attn_workspace_bytes(st.prob)), lse)
+    torch.cuda.synchronize()
+    q, k, v = _host(st)
+    for h in range(4):
+        ro, rl = oracle.attention_head(q[h], k[h // 2], v[h // 2], oracle.dense_index(n))
+        check_attention(f64(out)[h], ro, f"dense head {h}")
+        np.testing.assert_allclose(lse.cpu().numpy()[h], rl, rtol=0, atol=2e-4)
+
+
+def test_one_shot_equals_staged_and_is_deterministic():
+    n = 1024
+    heads = [W.vs(48, 80), W.bs(6), W.ashape(40, 150), W.vs(100, 30)]
+    w = W.custom("oneshot", n, 4, 2, heads, recipe="vs_planted", seed=14)
+    st = run_staged(make(w), debug=False)
+    ws = ms.empty_workspace(ms.ms_workspace_bytes(st.prob, st.hp))
+    outs = []
+    for _ in range(2):
+        out = torch.empty_like(st.q)
+        lse = torch.empty((4, n), device="cuda")
+        ms.ms_sparse_attn(st.prob, st.hp, st.q, st.k, st.v, out, ws, lse)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][0], st.out.view(torch.int16))
+    assert torch.equal(outs[0][1], st.lse)
+
+
+# ---------------------------------------------------------------- workload 0 end to end
+def test_config0_end_to_end():
+    w = W.config(0)
+    st = run_staged(make(w))
+    q, k, _ = _host(st)
+    v_ref, s_ref = oracle.vs_scores(q[0, w.n - 64:], k[0])
+    dv, ds = st.dbg_v[0].cpu().numpy().astype(np.float64), st.dbg_s[0].cpu().numpy().astype(np.float64)
+    _score_check(dv, v_ref, "vertical")
+    _score_check(ds, s_ref, "slash")
+    _, gv, gs = selections(st)[0]
+    assert _near_tie_ok(gv, oracle.topk(v_ref, 256), v_ref, dv, 256) == 0
+    assert _near_tie_ok(gs, oracle.topk(s_ref, 512), s_ref, ds, 512) == 0
+    _attention_check(st)
