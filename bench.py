@@ -1,0 +1,346 @@
+"""Benchmark: ms per layer of sparse pre-filling attention (estimation + index
+conversion + sparse kernel) on one MI355X, and the speedup over the library's
+own dense causal kernel on the same GPU.
+
+One step = one ms_sparse_attn call on one layer of synthetic inputs already
+resident in HBM.  The headline workload is the 1M-token Vertical-Slash layer
+(32 Q / 8 KV heads, d = 128, 1000 verticals + 6096 slashes per head); the
+128K mixed-pattern layer (24 VS / 6 BS / 2 A-shape heads) is reported beside
+it.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vs_1m|mixed_128k|...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+WORKLOADS = {"vs_4k": 0, "bs_32k": 1, "ashape_128k": 2, "mixed_128k": 3, "vs_1m": 4}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="vs_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--side", default="mixed_128k", help="second workload reported beside the headline ('' = none)")
+    ap.add_argument("--dense-steps", type=int, default=1)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0, help="rough budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- kept entries
+def _pairs_in_block(lo, hi, row0, torch):
+    """Causal pairs (i, j), i in [row0, row0+64), j in [lo, hi), j <= i."""
+    L = hi - lo
+    x = row0 + 1 - lo
+
+    def G(m):
+        m = m.clamp(min=0)
+        tri = m * (m + 1) // 2
+        over = L * (L + 1) // 2 + (m - L) * L
+        return torch.where(m <= L, tri, over)
+
+    return G(x + 63) - G(x - 1)
+
+
+def kept_entries(ms, prob, hp, heads, index, torch):
+    """Exact number of (row, key) pairs the layer attends, summed over heads."""
+    offs, _ = ms.ms_index_layout(prob, hp)
+    nb = prob.n // 64
+    base = index.view(torch.int32)
+    total = 0
+    for h, (o_rp, o_r, o_cp, o_c) in enumerate(offs):
+        rp = base[o_rp // 4:o_rp // 4 + nb + 1].long()
+        cp = base[o_cp // 4:o_cp // 4 + nb + 1].long()
+        nr, nc = int(rp[-1]), int(cp[-1])
+        p = heads[h]
+        if p.pattern == 0:  # A-shape: per-row window applied inside the kernel
+            i = torch.arange(prob.n, device=index.device, dtype=torch.int64)
+            win = torch.minimum(i + 1, torch.full_like(i, p.window))
+            sink = (i - p.window + 1).clamp(min=0).clamp(max=p.sink)
+            total += int((win + sink).sum())
+            continue
+        if nr:
+            rng = base[o_r // 4:o_r // 4 + 2 * nr].long().view(-1, 2)
+            blk = torch.repeat_interleave(torch.arange(nb, device=index.device), rp[1:] - rp[:-1])
+            total += int(_pairs_in_block(rng[:, 0], rng[:, 1], blk * 64, torch).sum())
+        if nc:
+            col = base[o_c // 4:o_c // 4 + nc].long()
+            blk = torch.repeat_interleave(torch.arange(nb, device=index.device), cp[1:] - cp[:-1])
+            total += int((blk * 64 + 64 - col).clamp(min=0, max=64).sum())
+    return total
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, q, k, v, heads, kept_total, budget_s):
+    """The float64 oracle, untuned, on a bounded sample of the same layer:
+    one head's estimation in full, index conversion and attention on sampled
+    query blocks; extrapolated to the layer (estimation x heads of that
+    pattern, index x blocks, attention by kept entries)."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+
+    n, nb = w.n, w.nb
+    rng = np.random.default_rng(0)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    torch.set_num_threads(cores)
+    h = next((i for i, p in enumerate(heads) if p.pattern == W.VERTICAL_SLASH), 0)
+    p = heads[h]
+    kv = h // w.group
+    qh = q[h].float().cpu().numpy().astype(np.float64)
+    kh = k[kv].float().cpu().numpy().astype(np.float64)
+    vh = v[kv].float().cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    sel = oracle.estimate_head(p, qh, kh)
+    t_est = time.perf_counter() - t0
+    n_same = sum(1 for x in heads if x.pattern == p.pattern)
+    # sampled blocks: first, last, and random ones, until the budget is spent
+    order = [0, nb - 1] + list(rng.permutation(np.arange(1, nb - 1)))
+    t_idx = t_att = 0.0
+    kept_s = 0
+    done = 0
+    spent = t_est
+    for b in order:
+        t1 = time.perf_counter()
+        if p.pattern == W.VERTICAL_SLASH:
+            bidx = oracle.vs_block_index(sel[1], sel[2], b)
+        elif p.pattern == W.BLOCK_SPARSE:
+            bidx = oracle.bs_block_index(sel[1][b])
+        else:
+            bidx = oracle.dense_block_index(b)
+        t2 = time.perf_counter()
+        oracle.attention_block(qh[b * 64:(b + 1) * 64], kh, vh, bidx, b)
+        t3 = time.perf_counter()
+        m = oracle.block_mask(bidx, b, n) if n <= 65536 else None
+        kept_s += int(m.sum()) if m is not None else _kept_np(bidx, b)
+        t_idx += t2 - t1
+        t_att += t3 - t2
+        done += 1
+        spent += t3 - t1
+        if done >= 16 and spent > budget_s:
+            break
+        if done >= 256:
+            break
+    est_layer = t_est * n_same
+    idx_layer = t_idx / done * nb * len(heads)
+    att_layer = t_att / max(kept_s, 1) * kept_total
+    total_ms = (est_layer + idx_layer + att_layer) * 1e3
+    return {
+        "value": round(total_ms, 1),
+        "unit": "ms/layer",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 oracle, head {h}: estimation over all {n} keys ({t_est:.1f} s, x{n_same} heads), "
+                   f"index + attention on {done} sampled query blocks of {nb} (first, last, random); "
+                   f"attention extrapolated by kept entries ({kept_s} sampled of {kept_total}); "
+                   f"wall {spent:.1f} s"),
+    }
+
+
+def _kept_np(bidx, b):
+    rng, cols = bidx
+    row0 = b * 64
+    tot = 0
+    for lo, hi in rng.tolist():
+        for r in range(64):
+            tot += max(0, min(hi, row0 + r + 1) - lo)
+    tot += sum(min(64, max(0, row0 + 64 - int(j))) for j in cols)
+    return tot
+
+
+# ---------------------------------------------------------------- main
+def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
+    w = W.config(cid)
+    q, k, v = W.generate(w, device="cuda")
+    prob, hp = ms.problem(w.n, w.n_q_heads, w.n_kv_heads), ms.head_params(w.heads)
+    out = torch.empty_like(q)
+    ws = ms.empty_workspace(ms.ms_workspace_bytes(prob, hp))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ms.ms_sparse_attn(prob, hp, q, k, v, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        ms.ms_sparse_attn(prob, hp, q, k, v, out, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = e0.elapsed_time(e1) / steps
+
+    # Stage split: the attention kernel alone (index already built by the
+    # steps above) and estimation + index conversion.
+    nv, ns, nbk = ms.ms_selection_sizes(prob, hp)
+    vert = torch.empty(max(nv, 1), dtype=torch.int32, device="cuda")
+    slash = torch.empty(max(ns, 1), dtype=torch.int32, device="cuda")
+    blocks = torch.empty(max(nbk, 1), dtype=torch.int32, device="cuda")
+    ews = ms.empty_workspace(ms.ms_estimate_workspace_bytes(prob, hp))
+    index = ms.empty_workspace(ms.ms_index_bytes(prob, hp))
+    aws = ms.empty_workspace(ms.ms_attn_workspace_bytes(prob))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    ms.ms_estimate_vs(prob, hp, q, k, vert, slash, ews)
+    ms.ms_estimate_block(prob, hp, q, k, blocks, ews)
+    ev[1].record(stream)
+    ms.ms_build_index(prob, hp, vert, slash, blocks, index)
+    ev[2].record(stream)
+    ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws)
+    ev[3].record(stream)
+    torch.cuda.synchronize()
+    t_est, t_idx, t_att = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
+    del ews
+    kept = kept_entries(ms, prob, hp, w.heads, index, torch)
+    dense_pairs = w.n * (w.n + 1) // 2 * w.n_q_heads
+    del index
+    res = {"w": w, "q": q, "k": k, "v": v, "ms": ms_step, "wall_s": t_wall, "t_est": t_est, "t_idx": t_idx,
+           "t_att": t_att, "kept": kept, "dense_pairs": dense_pairs}
+    del ws
+    if do_dense:
+        dout = torch.empty_like(q)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ms.ms_dense_attn(prob, q, k, v, dout, aws)   # warm (same kernel as the sparse one)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(dense_steps):
+            ms.ms_dense_attn(prob, q, k, v, dout, aws)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        res["dense_ms"] = d0.elapsed_time(d1) / dense_steps
+        del dout
+    del out, aws
+    return res
+
+
+def summary(r):
+    d = 128
+    kept_tf = 4.0 * d * r["kept"] / 1e12
+    att_tflops = kept_tf / (r["t_att"] / 1e3)
+    s = {
+        "ms_per_layer": round(r["ms"], 3),
+        "stages_ms": {"estimate": round(r["t_est"], 3), "index": round(r["t_idx"], 3),
+                      "attention": round(r["t_att"], 3)},
+        "kept_fraction": round(r["kept"] / r["dense_pairs"], 5),
+        "flop_ratio_bound": round(r["dense_pairs"] / r["kept"], 3),
+        "kept_tflop": round(kept_tf, 3),
+        "attention_tflops": round(att_tflops, 1),
+        "attention_mfma_frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
+        "effective_tflops": round(kept_tf / (r["ms"] / 1e3), 1),
+    }
+    if "dense_ms" in r:
+        dense_tf = 4.0 * d * r["dense_pairs"] / 1e12
+        s["dense_ms"] = round(r["dense_ms"], 3)
+        s["dense_tflops"] = round(dense_tf / (r["dense_ms"] / 1e3), 1)
+        s["dense_mfma_frac"] = round(dense_tf / (r["dense_ms"] / 1e3) / PEAK_BF16_TFLOPS, 4)
+        s["speedup_vs_dense"] = round(r["dense_ms"] / r["ms"], 3)
+    return s
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only (asked for {a.gpus}); the sparse path has no multi-GPU form here.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dynamic_sparse_attention_est_amd as ms
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ms.load()
+    print(f"[bench] headline {a.workload}: warmup {a.warmup}, steps {a.steps}", file=sys.stderr, flush=True)
+    main_r = run_layer(ms, torch, W, WORKLOADS[a.workload], a.steps, a.warmup, a.dense_steps, not a.no_dense)
+    main_s = summary(main_r)
+    print(f"[bench] {a.workload}: {json.dumps(main_s)}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not a.no_cpu:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(main_r["w"], main_r["q"], main_r["k"], main_r["v"], main_r["w"].heads, main_r["kept"],
+                           a.cpu_seconds)
+    for key in ("q", "k", "v"):
+        main_r.pop(key)
+    torch.cuda.empty_cache()
+
+    side = {}
+    if a.side and a.side != a.workload:
+        print(f"[bench] side workload {a.side}", file=sys.stderr, flush=True)
+        r2 = run_layer(ms, torch, W, WORKLOADS[a.side], a.steps, a.warmup, a.dense_steps, not a.no_dense)
+        for key in ("q", "k", "v"):
+            r2.pop(key)
+        side[a.side] = summary(r2)
+        print(f"[bench] {a.side}: {json.dumps(side[a.side])}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    w = main_r["w"]
+    line = {
+        "metric": "ms/layer sparse prefill attn (est+kernel) at 128K & 1M; speedup vs dense",
+        "value": round(main_r["ms"], 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(main_r["ms"], 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generators shaped like the pages' workloads; no datasets or weights)",
+        "config": {"workload": f"{w.name}: {w.n_q_heads} Q / {w.n_kv_heads} KV heads, n={w.n}, d=128, "
+                               + ", ".join(sorted({_head_desc(h) for h in w.heads})),
+                   "seq_len": w.n, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "batch": 1,
+                   "parallelism": "single GPU"},
+        "result": main_s,
+        "side": side,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": main_s["attention_tflops"],
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": main_s["attention_mfma_frac"],
+            "traffic": None,
+            "kernel": "sparse_attn_fwd (timed with the fp16 V copy it consumes)",
+            "work": "4*128 FLOP per kept (row, key) pair",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+def _head_desc(h):
+    if h.pattern == 1:
+        return f"VS {h.n_vertical}v/{h.n_slash}s"
+    if h.pattern == 2:
+        return f"BS top-{h.top_k_blocks}"
+    if h.pattern == 0:
+        return f"A-shape sink {h.sink}/window {h.window}"
+    return "dense"
+
+
+if __name__ == "__main__":
+    main()
