@@ -67,7 +67,7 @@ ms_status validate(const ms_problem* prob, const ms_head_params* params, bool ne
   if (prob->head_dim != kD) return fail(MS_ERR_UNSUPPORTED, "head_dim %d: only 128 is supported", prob->head_dim);
   if (prob->n < kBM || prob->n % kBM != 0)
     return fail(MS_ERR_UNSUPPORTED, "n = %lld: must be a positive multiple of 64", (long long)prob->n);
-  if (prob->n > (int64_t{1} << 24)) return fail(MS_ERR_UNSUPPORTED, "n = %lld exceeds 2^24", (long long)prob->n);
+  if (prob->n > (int64_t{1} << 23)) return fail(MS_ERR_UNSUPPORTED, "n = %lld exceeds 2^23", (long long)prob->n);
   if (prob->n_q_heads < 1 || prob->n_q_heads > kMaxHeads)
     return fail(MS_ERR_INVALID_ARG, "n_q_heads = %d: must be 1..%d", prob->n_q_heads, kMaxHeads);
   if (prob->n_kv_heads < 1 || prob->n_q_heads % prob->n_kv_heads != 0)

@@ -59,7 +59,7 @@ typedef enum { MS_A_SHAPE = 0, MS_VERTICAL_SLASH = 1, MS_BLOCK_SPARSE = 2, MS_DE
 typedef enum { MS_OUT_BF16 = 0, MS_OUT_F32 = 1 } ms_out_dtype;
 
 /* One attention layer.  Limits of this build: head_dim == 128, n % 64 == 0,
- * 64 <= n <= 16777216, 1 <= n_q_heads <= 128, n_kv_heads divides n_q_heads. */
+ * 64 <= n <= 8388608, 1 <= n_q_heads <= 128, n_kv_heads divides n_q_heads. */
 typedef struct {
   int64_t n;          /* sequence length: rows of Q and of K/V */
   int32_t n_q_heads;  /* H_q */

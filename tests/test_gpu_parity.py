@@ -26,6 +26,10 @@ from gpu_common import (Staged, ashape_of, bf16_round, check_attention, f64, kv_
 pytestmark = pytest.mark.gpu
 
 SCORE_RTOL = 1e-5
+# log-sum-exp: the row sum is taken over the fp16-rounded probabilities the PV
+# product consumes (relative rounding <= 2^-11 ~ 4.9e-4 each), so the natural
+# log of the sum is off by at most ~4.9e-4; the bar leaves a factor two.
+LSE_ATOL = 1e-3
 
 
 def _score_check(got, ref, what):
@@ -227,7 +231,7 @@ def _attention_check(st: Staged, blocks=None, bf16_out=True):
         if lse is not None:
             fin = rows & np.isfinite(rl)
             assert np.all(np.isneginf(lse[h][rows & ~np.isfinite(rl)]))
-            np.testing.assert_allclose(lse[h][fin], rl[fin], rtol=0, atol=2e-4)
+            np.testing.assert_allclose(lse[h][fin], rl[fin], rtol=0, atol=LSE_ATOL)
 
 
 def test_attention_mixed_patterns_gqa():
@@ -278,7 +282,7 @@ def test_dense_attention():
     for h in range(4):
         ro, rl = oracle.attention_head(q[h], k[h // 2], v[h // 2], oracle.dense_index(n))
         check_attention(f64(out)[h], ro, f"dense head {h}")
-        np.testing.assert_allclose(lse.cpu().numpy()[h], rl, rtol=0, atol=2e-4)
+        np.testing.assert_allclose(lse.cpu().numpy()[h], rl, rtol=0, atol=LSE_ATOL)
 
 
 def test_one_shot_equals_staged_and_is_deterministic():
