@@ -131,3 +131,27 @@ def kv_of(w: W.Workload, h: int) -> int:
 
 def ashape_of(hp):
     return (hp.sink, hp.window) if hp.pattern == W.A_SHAPE else None
+
+
+def read_index_blocks(prob, hp, index: torch.Tensor, head: int, blocks):
+    """CSR entries of some query blocks of one head, copied from the device:
+    {b: (ranges [r, 2] int64, cols [c] int64)}."""
+    offs, _ = ms.ms_index_layout(prob, hp)
+    o_rp, o_r, o_cp, o_c = offs[head]
+    nb = prob.n // 64
+    base = index.view(torch.int32)
+    rp = base[o_rp // 4:o_rp // 4 + nb + 1].cpu().numpy()
+    cp = base[o_cp // 4:o_cp // 4 + nb + 1].cpu().numpy()
+    out = {}
+    for b in blocks:
+        r = base[o_r // 4 + 2 * int(rp[b]):o_r // 4 + 2 * int(rp[b + 1])].cpu().numpy().reshape(-1, 2).astype(np.int64)
+        c = base[o_c // 4 + int(cp[b]):o_c // 4 + int(cp[b + 1])].cpu().numpy().astype(np.int64)
+        out[b] = (r, c)
+    return out
+
+
+def sample_blocks(nb: int, count: int, seed: int):
+    """First, last and random query blocks."""
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(np.arange(1, nb - 1), size=min(count, nb - 2), replace=False) if nb > 2 else []
+    return sorted({0, nb - 1, *[int(x) for x in extra]})

@@ -1,0 +1,118 @@
+"""Parity on the five workloads at their full sizes, through the C ABI.
+
+Small workload 0 runs end to end in tests/test_gpu_parity.py.  Here the
+GPU runs the whole layer at full size; the float64 oracle checks every
+head's selection against the GPU's own scores (bit-exact), sampled heads'
+scores and oracle selections (near-tie aware), the index of sampled query
+blocks (bit-exact), and attention on sampled query blocks (the bar of
+tests/test_gpu_parity.py).  The one-shot call must reproduce the staged
+output bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_est_amd as ms
+import oracle
+import workloads as W
+from gpu_common import (ashape_of, check_attention, f64, kv_of, make, read_index_blocks, run_staged,
+                        sample_blocks, selections)
+from test_gpu_parity import LSE_ATOL, _near_tie_ok, _score_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_layer(cid, heads_checked, n_blocks, seed, est_heads=()):
+    w = W.config(cid)
+    print(f"[config {cid}] {w.name}: n={w.n} heads={w.n_q_heads}/{w.n_kv_heads}", flush=True)
+    st = run_staged(make(w), debug=True)
+    sel = selections(st)
+    # every head: GPU selection == oracle top-k of the GPU's own scores
+    dv = st.dbg_v.cpu().numpy() if st.dbg_v is not None else None
+    ds = st.dbg_s.cpu().numpy() if st.dbg_s is not None else None
+    sc = st.dbg_scores
+    for h, p in enumerate(w.heads):
+        if p.pattern == W.VERTICAL_SLASH:
+            np.testing.assert_array_equal(sel[h][1], oracle.topk(dv[h].astype(np.float64), p.n_vertical))
+            np.testing.assert_array_equal(sel[h][2], oracle.topk(ds[h].astype(np.float64), p.n_slash))
+        elif p.pattern == W.BLOCK_SPARSE:
+            s_h = sc[h].cpu().numpy().astype(np.float64)
+            rows = sel[h][2]
+            for b in sample_blocks(w.nb, 64, seed + h):
+                np.testing.assert_array_equal(rows[b][: min(p.top_k_blocks, b + 1)],
+                                              oracle.topk(s_h[b, : b + 1], p.top_k_blocks))
+    # sampled heads: scores and end-to-end selections against the oracle
+    for h in est_heads:
+        p = w.heads[h]
+        qh = f64(st.q[h])
+        kh = f64(st.k[kv_of(w, h)])
+        if p.pattern == W.VERTICAL_SLASH:
+            v_ref, s_ref = oracle.vs_scores(qh[w.n - 64:], kh)
+            _score_check(dv[h].astype(np.float64), v_ref, f"head {h} vertical")
+            _score_check(ds[h].astype(np.float64), s_ref, f"head {h} slash")
+            ties = _near_tie_ok(sel[h][1], oracle.topk(v_ref, p.n_vertical), v_ref, dv[h], p.n_vertical)
+            ties += _near_tie_ok(sel[h][2], oracle.topk(s_ref, p.n_slash), s_ref, ds[h], p.n_slash)
+            print(f"  head {h}: near-tie swaps {ties}", flush=True)
+        elif p.pattern == W.BLOCK_SPARSE:
+            ref = oracle.bs_scores(qh, kh)
+            got = sc[h].cpu().numpy().astype(np.float64)
+            low = np.tril(np.ones_like(ref, dtype=bool))
+            scale = np.abs(oracle.bs_pool(qh)) @ np.abs(oracle.bs_pool(kh)).T
+            assert (np.abs(got[low] - ref[low]) / (scale[low] + 1e-30)).max() <= 1e-5
+    del sc
+    # sampled heads and blocks: index and attention
+    out = st.out
+    lse = st.lse
+    for h in heads_checked:
+        p = w.heads[h]
+        blocks = sample_blocks(w.nb, n_blocks, seed + 100 + h)
+        got_idx = read_index_blocks(st.prob, st.hp, st.index, h, blocks)
+        qh = f64(st.q[h])
+        kh, vh = f64(st.k[kv_of(w, h)]), f64(st.v[kv_of(w, h)])
+        for b in blocks:
+            if p.pattern == W.VERTICAL_SLASH:
+                ref_b = oracle.vs_block_index(sel[h][1], sel[h][2], b)
+            elif p.pattern == W.BLOCK_SPARSE:
+                ref_b = oracle.bs_block_index(sel[h][1][b])
+            elif p.pattern == W.A_SHAPE:
+                ref_b = oracle.ashape_block_index(p.sink, p.window, b)
+            else:
+                ref_b = oracle.dense_block_index(b)
+            np.testing.assert_array_equal(got_idx[b][0], ref_b[0], err_msg=f"head {h} block {b} ranges")
+            np.testing.assert_array_equal(got_idx[b][1], ref_b[1], err_msg=f"head {h} block {b} cols")
+            ro, rl = oracle.attention_block(qh[64 * b:64 * b + 64], kh, vh, ref_b, b, ashape=ashape_of(p))
+            rows = slice(64 * b, 64 * b + 64)
+            check_attention(f64(out[h, rows]), ro, f"head {h} block {b}")
+            got_l = lse[h, rows].cpu().numpy().astype(np.float64)
+            fin = np.isfinite(rl)
+            assert np.all(np.isneginf(got_l[~fin]))
+            np.testing.assert_allclose(got_l[fin], rl[fin], rtol=0, atol=LSE_ATOL)
+        print(f"  head {h} ({p.pattern}): {len(blocks)} blocks ok", flush=True)
+    # one-shot call reproduces the staged output bit for bit
+    ws = ms.empty_workspace(ms.ms_workspace_bytes(st.prob, st.hp))
+    out2 = torch.empty_like(out)
+    ms.ms_sparse_attn(st.prob, st.hp, st.q, st.k, st.v, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+
+
+def test_config1_block_sparse_32k():
+    _check_layer(1, heads_checked=[0, 17, 31], n_blocks=8, seed=1, est_heads=[0, 31])
+
+
+def test_config2_ashape_128k():
+    _check_layer(2, heads_checked=[0, 31], n_blocks=6, seed=2)
+
+
+def test_config3_mixed_128k():
+    w = W.config(3)
+    pats = [p.pattern for p in w.heads]
+    vs_h = [i for i, p in enumerate(pats) if p == W.VERTICAL_SLASH]
+    bs_h = [i for i, p in enumerate(pats) if p == W.BLOCK_SPARSE]
+    a_h = [i for i, p in enumerate(pats) if p == W.A_SHAPE]
+    _check_layer(3, heads_checked=[vs_h[0], vs_h[-1], bs_h[0], a_h[0]], n_blocks=4, seed=3,
+                 est_heads=[vs_h[0], bs_h[0]])
+
+
+def test_config4_vertical_slash_1m():
+    _check_layer(4, heads_checked=[0, 29], n_blocks=3, seed=4, est_heads=[0])
