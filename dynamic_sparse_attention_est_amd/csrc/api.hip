@@ -49,7 +49,7 @@ struct Plan {
   int64_t n_vert = 0, n_slash = 0, n_blocks = 0;
   int ntiles = 0;
   // estimation workspace (byte offsets)
-  size_t e_part = 0, e_stats = 0, e_diag = 0, e_v = 0, e_s = 0, e_qpool = 0, e_kpool = 0, e_scores = 0;
+  size_t e_part = 0, e_stats = 0, e_diag = 0, e_v = 0, e_s = 0, e_qpool = 0, e_kpool = 0, e_scores = 0, e_topk = 0;
   size_t est_bytes = 0;
   // index arena
   std::vector<int64_t> cap_r, cap_c;
@@ -184,6 +184,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.e_qpool = take((size_t)P.n_bs * P.nb * kD * f);
   P.e_kpool = take((size_t)P.bs_kv_heads.size() * P.nb * kD * f);
   P.e_scores = take((size_t)P.n_bs * P.nb * P.nb * f);
+  P.e_topk = take(topk_scratch_bytes(P.n, std::max(P.n_vs, 1)));
   P.est_bytes = std::max<size_t>(off, kAlign);
   // Index arena: descriptor table, then each head's CSR.
   off = align_up((size_t)kTableBytes);
@@ -293,15 +294,20 @@ ms_status run_estimate_vs(const Plan& P, const uint16_t* q, const uint16_t* k, i
   TopkJobs jv{}, js{};
   for (int i = 0; i < P.n_vs; ++i) {
     const int h = P.vs_heads[i];
-    jv.src_off[jv.count] = (int64_t)i * P.n;
-    jv.dst_off[jv.count] = P.vert_off[h];
-    jv.k[jv.count++] = P.p[h].n_vertical;
-    js.src_off[js.count] = (int64_t)i * P.n;
-    js.dst_off[js.count] = P.slash_off[h];
-    js.k[js.count++] = P.p[h].n_slash;
+    if (P.p[h].n_vertical > 0) {
+      jv.src_off[jv.count] = (int64_t)i * P.n;
+      jv.dst_off[jv.count] = P.vert_off[h];
+      jv.k[jv.count++] = P.p[h].n_vertical;
+    }
+    if (P.p[h].n_slash > 0) {
+      js.src_off[js.count] = (int64_t)i * P.n;
+      js.dst_off[js.count] = P.slash_off[h];
+      js.k[js.count++] = P.p[h].n_slash;
+    }
   }
-  if (P.n_vert > 0) HIP_TRY(launch_topk_rows(v_sc, P.n, jv, vert, s), "vertical top-k launch");
-  if (P.n_slash > 0) HIP_TRY(launch_topk_rows(s_sc, P.n, js, slash, s), "slash top-k launch");
+  void* tk = ws + P.e_topk;
+  HIP_TRY(launch_topk_chunked(v_sc, P.n, jv, vert, tk, s), "vertical top-k launch");
+  HIP_TRY(launch_topk_chunked(s_sc, P.n, js, slash, tk, s), "slash top-k launch");
   for (int i = 0; i < P.n_vs; ++i) {
     const int h = P.vs_heads[i];
     if (dbg_v)

@@ -73,6 +73,11 @@ struct TopkJobs {            // up to kMaxJobs problems in one launch
   int32_t k[kMaxJobs];
 };
 hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, hipStream_t s);
+// Same selection with many workgroups per problem (for long vectors); every
+// job's k must lie in 1..n.  scratch: device, >= topk_scratch_bytes(n, jobs).
+size_t topk_scratch_bytes(int64_t n, int problems);
+hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, void* scratch,
+                               hipStream_t s);
 // Block-Sparse selection: for every BS slot and query block b, top-min(k, b+1)
 // of scores[slot][b][0..b] into blocks (-1 padded to k).  k_of_slot and
 // dst_off_of_slot are host arrays of n_bs entries.

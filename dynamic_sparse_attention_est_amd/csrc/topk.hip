@@ -114,11 +114,169 @@ __global__ __launch_bounds__(kSelThreads) void bs_select(const float* scores, in
   for (int i = cnt + threadIdx.x; i < k; i += kSelThreads) row[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Many workgroups per problem (long score vectors): the same radix select with
+// chunk histograms merged in a fixed order, then an ordered compaction whose
+// per-chunk output offsets come from a scan over the chunks.
+constexpr int kChunk = 16384;  // elements per workgroup
+constexpr int kMT = 256;
+
+struct TopkState {
+  uint32_t prefix, mask;
+  int rem;   // keys equal to the final prefix still to take
+  int pad;
+};
+
+__global__ void topk_init(TopkJobs jobs, TopkState* st) {
+  const int j = threadIdx.x;
+  if (j < jobs.count) st[j] = TopkState{0u, 0u, jobs.k[j], 0};
+}
+
+__global__ __launch_bounds__(kMT) void topk_hist(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
+                                                 int* hist, int nchunks, int shift) {
+  __shared__ int h[256];
+  const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
+  h[t] = 0;
+  __syncthreads();
+  const float* x = src + jobs.src_off[j];
+  const uint32_t prefix = st[j].prefix, mask = st[j].mask;
+  const int64_t end = min(n, (int64_t)(c + 1) * kChunk);
+  for (int64_t i = (int64_t)c * kChunk + t; i < end; i += kMT) {
+    const uint32_t key = order_key(x[i]);
+    if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
+  }
+  __syncthreads();
+  hist[((int64_t)j * nchunks + c) * 256 + t] = h[t];
+}
+
+__global__ __launch_bounds__(256) void topk_digit(TopkState* st, const int* hist, int nchunks, int shift) {
+  __shared__ int tot[256];
+  const int j = blockIdx.x, t = threadIdx.x;
+  int s = 0;
+  for (int c = 0; c < nchunks; ++c) s += hist[((int64_t)j * nchunks + c) * 256 + t];
+  tot[t] = s;
+  __syncthreads();
+  if (t == 0) {
+    const int rem = st[j].rem;
+    int above = 0, d = 255;
+    for (; d > 0; --d) {
+      if (above + tot[d] >= rem) break;
+      above += tot[d];
+    }
+    st[j].rem = rem - above;
+    st[j].prefix |= (uint32_t)d << shift;
+    st[j].mask |= 255u << shift;
+  }
+}
+
+// Per chunk: how many keys are above the threshold and how many equal it.
+__global__ __launch_bounds__(kMT) void topk_count(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
+                                                  int* counts, int nchunks) {
+  __shared__ int red[2][kMT / 64];
+  const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
+  const float* x = src + jobs.src_off[j];
+  const uint32_t T = st[j].prefix;
+  const int64_t end = min(n, (int64_t)(c + 1) * kChunk);
+  int gt = 0, eq = 0;
+  for (int64_t i = (int64_t)c * kChunk + t; i < end; i += kMT) {
+    const uint32_t key = order_key(x[i]);
+    gt += key > T;
+    eq += key == T;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    gt += __shfl_xor(gt, d);
+    eq += __shfl_xor(eq, d);
+  }
+  if ((t & 63) == 0) {
+    red[0][t >> 6] = gt;
+    red[1][t >> 6] = eq;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int g = 0, e = 0;
+    for (int w = 0; w < kMT / 64; ++w) {
+      g += red[0][w];
+      e += red[1][w];
+    }
+    counts[((int64_t)j * nchunks + c) * 2] = g;
+    counts[((int64_t)j * nchunks + c) * 2 + 1] = e;
+  }
+}
+
+// Per chunk: output offset of its first selected key, and the number of
+// threshold-equal keys in earlier chunks.
+__global__ void topk_bases(const TopkState* st, const int* counts, int* bases, int nchunks) {
+  const int j = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  const int need = st[j].rem;
+  int gtp = 0, eqp = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const int64_t o = ((int64_t)j * nchunks + c) * 2;
+    bases[o] = gtp + min(need, eqp);
+    bases[o + 1] = eqp;
+    gtp += counts[o];
+    eqp += counts[o + 1];
+  }
+}
+
+__global__ __launch_bounds__(kMT) void topk_write(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
+                                                  const int* bases, int32_t* dst, int nchunks) {
+  __shared__ int warp_sum[kMT / 64];
+  const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
+  const float* x = src + jobs.src_off[j];
+  int32_t* out = dst + jobs.dst_off[j];
+  const uint32_t T = st[j].prefix;
+  const int need = st[j].rem;
+  int base = bases[((int64_t)j * nchunks + c) * 2];
+  int eq_base = bases[((int64_t)j * nchunks + c) * 2 + 1];
+  const int64_t end = min(n, (int64_t)(c + 1) * kChunk);
+  for (int64_t start = (int64_t)c * kChunk; start < end; start += kMT) {
+    const int64_t i = start + t;
+    const uint32_t key = i < end ? order_key(x[i]) : 0u;
+    const int gt = (i < end) & (key > T);
+    const int eq = (i < end) & (key == T);
+    int eq_total, sel_total;
+    const int eq_rank = eq_base + block_excl_scan<kMT>(eq, warp_sum, &eq_total);
+    const int sel = gt | (eq & (eq_rank < need));
+    const int pos = base + block_excl_scan<kMT>(sel, warp_sum, &sel_total);
+    if (sel) out[pos] = (int32_t)i;
+    base += sel_total;
+    eq_base += eq_total;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, hipStream_t s) {
   if (jobs.count <= 0) return hipSuccess;
   hipLaunchKernelGGL(topk_rows, dim3((unsigned)jobs.count), dim3(kTopkThreads), 0, s, src, n, jobs, dst);
+  return hipGetLastError();
+}
+
+size_t topk_scratch_bytes(int64_t n, int problems) {
+  const int64_t nchunks = (n + kChunk - 1) / kChunk;
+  return 256 + (size_t)problems * sizeof(TopkState) + (size_t)problems * nchunks * (256 + 4) * sizeof(int);
+}
+
+hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, void* scratch,
+                               hipStream_t s) {
+  if (jobs.count <= 0) return hipSuccess;
+  const int nchunks = (int)((n + kChunk - 1) / kChunk);
+  char* w = static_cast<char*>(scratch);
+  TopkState* st = reinterpret_cast<TopkState*>(w);
+  int* hist = reinterpret_cast<int*>(w + 256 + (size_t)jobs.count * sizeof(TopkState));
+  int* counts = hist + (size_t)jobs.count * nchunks * 256;
+  int* bases = counts + (size_t)jobs.count * nchunks * 2;
+  const dim3 grid((unsigned)nchunks, (unsigned)jobs.count);
+  hipLaunchKernelGGL(topk_init, dim3(1), dim3(TopkJobs::kMaxJobs), 0, s, jobs, st);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(topk_hist, grid, dim3(kMT), 0, s, src, n, jobs, st, hist, nchunks, shift);
+    hipLaunchKernelGGL(topk_digit, dim3((unsigned)jobs.count), dim3(256), 0, s, st, hist, nchunks, shift);
+  }
+  hipLaunchKernelGGL(topk_count, grid, dim3(kMT), 0, s, src, n, jobs, st, counts, nchunks);
+  hipLaunchKernelGGL(topk_bases, dim3((unsigned)jobs.count), dim3(64), 0, s, st, counts, bases, nchunks);
+  hipLaunchKernelGGL(topk_write, grid, dim3(kMT), 0, s, src, n, jobs, st, bases, dst, nchunks);
   return hipGetLastError();
 }
 

@@ -179,18 +179,39 @@ __global__ __launch_bounds__(256) void vs_pass2(VsArgs a) {
   }
 }
 
-__global__ __launch_bounds__(64) void vs_stats(const float* part_mz, float* stats, int ntiles) {
-  const int slot = blockIdx.x, rr = threadIdx.x;
+// Row statistics of the last 64 rows: merge the per-tile partials (m_t, z_t),
+// m in log2 units, into M = max m_t and Z = sum z_t 2^(m_t - M).  One
+// workgroup per (row, head); thread t merges tiles t, t+256, ... online, then
+// the 256 partials are merged pairwise in a fixed tree order.
+__device__ __forceinline__ void merge_mz(float& m, float& z, float m2, float z2) {
+  const float mn = fmaxf(m, m2);
+  if (mn == -INFINITY) return;
+  z = (m == -INFINITY ? 0.f : z * exp2f(m - mn)) + (m2 == -INFINITY ? 0.f : z2 * exp2f(m2 - mn));
+  m = mn;
+}
+
+__global__ __launch_bounds__(256) void vs_stats(const float* part_mz, float* stats, int ntiles) {
+  __shared__ float sm[256], sz[256];
+  const int rr = blockIdx.x, slot = blockIdx.y, tid = threadIdx.x;
   const float* p = part_mz + (int64_t)slot * ntiles * kLastQ * 2 + rr * 2;
-  float m = -INFINITY;
-  for (int t = 0; t < ntiles; ++t) m = fmaxf(m, p[(int64_t)t * kLastQ * 2]);
-  float z = 0.f;
-  for (int t = 0; t < ntiles; ++t) {
-    const float mt = p[(int64_t)t * kLastQ * 2];
-    if (mt != -INFINITY) z += p[(int64_t)t * kLastQ * 2 + 1] * exp2f(mt - m);
+  float m = -INFINITY, z = 0.f;
+  for (int t = tid; t < ntiles; t += 256) merge_mz(m, z, p[(int64_t)t * kLastQ * 2], p[(int64_t)t * kLastQ * 2 + 1]);
+  sm[tid] = m;
+  sz[tid] = z;
+  __syncthreads();
+  for (int half = 128; half > 0; half >>= 1) {
+    if (tid < half) {
+      float m1 = sm[tid], z1 = sz[tid];
+      merge_mz(m1, z1, sm[tid + half], sz[tid + half]);
+      sm[tid] = m1;
+      sz[tid] = z1;
+    }
+    __syncthreads();
   }
-  stats[((int64_t)slot * kLastQ + rr) * 2] = m;
-  stats[((int64_t)slot * kLastQ + rr) * 2 + 1] = z;
+  if (tid == 0) {
+    stats[((int64_t)slot * kLastQ + rr) * 2] = sm[0];
+    stats[((int64_t)slot * kLastQ + rr) * 2 + 1] = sz[0];
+  }
 }
 
 __global__ __launch_bounds__(256) void vs_diag(const float* diag_part, float* s_scores, int64_t n, int ntiles) {
@@ -233,7 +254,7 @@ hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, i
   hipLaunchKernelGGL(vs_pass1, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_stats, dim3((unsigned)n_vs), dim3(64), 0, s, part_mz, stats, a.ntiles);
+  hipLaunchKernelGGL(vs_stats, dim3((unsigned)kLastQ, (unsigned)n_vs), dim3(256), 0, s, part_mz, stats, a.ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(vs_pass2, grid, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
