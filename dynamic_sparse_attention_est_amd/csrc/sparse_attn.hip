@@ -6,40 +6,46 @@
 // Work item: one 64-row query block of one Q head = one workgroup of two
 // wavefronts, each owning 32 rows.  The block's keys are its ranges, cut into
 // pieces of up to 32 consecutive keys, then its column list in pieces of up to
-// 32 gathered keys.  Per piece, both waves share one LDS copy of the piece's
-// K and V rows, double-buffered: the next piece's rows are loaded into
-// registers right after a barrier and written to the other buffer at the end
-// of the iteration, a full piece of compute later.
-//   S^T (32 keys x 32 rows) = K . Q^T         v_mfma_f32_32x32x16_bf16
-//   online softmax in the log2 domain; the running max may lag the true max by
-//   up to 8 (P <= 256), so the O rescale only runs when a row's max grows by
-//   more than that
-//   O^T (128 x 32 rows) += V^T . P^T           v_mfma_f32_32x32x16_f16
-// K and V rows are fetched with buffer loads whose range check (one KV head's
-// rows) turns reads past the sequence into zeros, so piece tails need no
-// clamping.  V is read transposed out of its row-major LDS tile with
-// ds_read_b64_tr_b16.  P and V enter the second product as fp16 (V from an
-// exact fp16 copy).
+// 32 gathered keys.  Both waves share one LDS copy of a piece's K and V rows,
+// written by buffer loads that go straight to LDS (no staging registers).
+// Software pipeline, per iteration i:
+//   - loads issued: K rows of piece i+2, V rows of piece i+1;
+//   - S^T of piece i+1 (32 keys x 32 rows) = K . Q^T   v_mfma_f32_32x32x16_bf16
+//     interleaved with the exponentials of piece i, whose S^T the previous
+//     iteration produced;
+//   - O^T (128 x 32 rows) += V^T . P^T of piece i       v_mfma_f32_32x32x16_f16
+//   - one barrier.
+// The online softmax works in the log2 domain; the running max may lag the
+// true max by up to 8 (P <= 256), so the O rescale only runs when a row's max
+// grows by more than that.  Buffer-load range checks (one KV head's rows) turn
+// reads past the sequence into zeros, so piece tails need no clamping.
+//
+// LDS tiles are row-major (one 256-byte row per key) with the 16-byte chunks
+// of row r XOR-swizzled: chunk c sits at chunk slot c ^ swz(r).  One
+// load-to-LDS instruction fills four whole rows (1 KiB of contiguous memory
+// per four keys), and both the K fragment reads and the transposed V reads
+// (ds_read_b64_tr_b16) are free of bank conflicts; the per-lane read offsets
+// are precomputed, so LDS addresses cost no VALU work in the loop.  P and V
+// enter the second product as fp16 (V from an exact fp16 copy).
 #include "internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kKP = 32;            // keys per piece
-constexpr int kKS = 136;           // K tile row stride, 16-bit elements (272 B)
-constexpr int kVS = 160;           // V tile row stride, 16-bit elements (320 B)
-constexpr int kKTile = kKP * kKS;
-constexpr int kVTile = kKP * kVS;
-constexpr int kRowBytes = kD * 2;  // one K or V row in HBM
-constexpr float kLag = 8.f;        // allowed lag of the running max (log2 units)
+constexpr int kKP = 32;                       // keys per piece
+constexpr int kRowBytes = kD * 2;             // one K or V row
+constexpr int kTileBytes = kKP * kRowBytes;   // one K or V tile (8 KiB)
+constexpr float kLag = 8.f;                   // allowed lag of the running max (log2 units)
 constexpr int kThreads = 128;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const int global_int;
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Transposed LDS read (gfx950): within each group of 16 lanes, lane i gets
 // element i%4 of the 8-byte chunks addressed by lanes i/4, 4+i/4, 8+i/4, 12+i/4.
-__device__ __forceinline__ f16x4 lds_read_tr(const _Float16* p) {
+__device__ __forceinline__ f16x4 lds_read_tr(const char* p) {
   return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
@@ -104,47 +110,36 @@ struct PieceIter {
   }
 };
 
-// Staging registers of one piece: thread t owns 16-byte chunk t%16 of rows
-// t/16 + 8i (i = 0..3) of both the K tile and the V tile.
-struct Stage {
-  u32x4 k[4];
-  u32x4 v[4];
-  int key[4];  // column pieces only
-};
+// Chunk slot of 16-byte chunk c of tile row r is c ^ swz(r).  For 16
+// consecutive rows swz takes 16 distinct values, and for 4 consecutive rows
+// starting at a multiple of 4 it takes 4 values that differ in bits 2-3.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-__device__ __forceinline__ void load_piece(const Piece& p, const int* col, __amdgpu_buffer_rsrc_t kr,
-                                           __amdgpu_buffer_rsrc_t vr, int row_off, int tid, Stage& st) {
-  int off[4];
-  if (p.is_col) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.key[i] = col[p.start + min((tid >> 4) + 8 * i, p.count - 1)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) off[i] = st.key[i] * kRowBytes + (row_off & (kRowBytes - 1));
-  } else {
-    // rows past the piece hold keys that the mask drops; rows past the
-    // sequence lie outside the buffer and read as zero
-#pragma unroll
-    for (int i = 0; i < 4; ++i) off[i] = p.start * kRowBytes + row_off + i * 8 * kRowBytes;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.k[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, off[i], 0, 0);
-    st.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, off[i], 0, 0);
-  }
+// Loads to LDS: load j (0..3) of wave w fills tile rows 16w + 4j + lane/16;
+// lane writes chunk slot lane%16 and so fetches chunk (lane%16) ^ swz(row).
+// lofs[j] is that chunk's byte offset within a four-row group of keys plus
+// the row's offset, so the address is key_of_row0 * 256 + lofs[j] for a range
+// piece.
+
+// Column pieces: the key of a tile row (rows past the piece repeat its last
+// key; the mask drops them).  Global (not flat) loads, which only vmcnt
+// tracks, so LDS waits do not stall on them.
+__device__ __forceinline__ int col_key(const Piece& p, global_int* col, int row) {
+  return col[p.start + min(row, p.count - 1)];
 }
 
-__device__ __forceinline__ void store_piece(const Stage& st, bool is_col, uint16_t* kt, _Float16* vt, int* keys,
-                                            int tid) {
-  const int c16 = tid & 15;
+struct ColKeys {
+  int k[4];  // keys of rows 16w + 4j + lane/16
+};
+
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int w, const uint32_t* lofs,
+                                          const uint32_t* cofs, const Piece& p, const ColKeys& ck) {
+  char* const base = tile + 4096 * w;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 4) + 8 * i;
-    *reinterpret_cast<u32x4*>(kt + row * kKS + 8 * c16) = st.k[i];
-    *reinterpret_cast<u32x4*>(vt + row * kVS + 8 * c16) = st.v[i];
-  }
-  if (is_col && c16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) keys[(tid >> 4) + 8 * i] = st.key[i];
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t off = p.is_col ? (uint32_t)ck.k[j] * (uint32_t)kRowBytes + cofs[j]
+                                  : (uint32_t)p.start * (uint32_t)kRowBytes + lofs[j];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16, off, 0, 0, 0);
   }
 }
 
@@ -163,12 +158,15 @@ __device__ __forceinline__ void map_work(int x, int hq, int nb, int& h, int& b) 
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTile];
-  __shared__ __attribute__((aligned(16))) _Float16 v_lds[2][kVTile];
-  __shared__ int key_lds[2][kKP];
+  __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char vb1[kTileBytes];
+  __shared__ int key_lds[4][kKP];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   int h, b;
   map_work(blockIdx.x, a.hq, a.nb, h, b);
@@ -177,7 +175,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int row0 = b * kBM;
 
   PieceIter it{};
-  const int* col = nullptr;
+  global_int* col = nullptr;
   bool ashape = false;
   int sink = 0, window = 0;
   if (a.table) {
@@ -189,7 +187,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     it.r_end = rng_ptr[b + 1];
     it.c = col_ptr[b];
     it.c_end = col_ptr[b + 1];
-    col = reinterpret_cast<const int*>(a.arena + d.col_off);
+    col = reinterpret_cast<global_int*>(reinterpret_cast<uint64_t>(a.arena + d.col_off));
     if (d.pattern == MS_A_SHAPE) {
       ashape = true;
       sink = d.p0;
@@ -201,12 +199,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 
   const uint16_t* qh = a.q + ((int64_t)h * n + row0 + 32 * w) * kD;
-  const int nbytes = (int)(n * kRowBytes);
+  // Byte size of one KV head (<= 2^31 for n <= 2^23), taken as unsigned by the
+  // range check.
+  const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
   const __amdgpu_buffer_rsrc_t kr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
-  const int row_off = (tid >> 4) * kRowBytes + (tid & 15) * 16;  // this thread's staging rows / chunk
 
   // Q fragments: B operand of S^T = K Q^T; lane holds row l32 of this wave's
   // 32 rows and d = 16t + 8g .. +8.
@@ -215,120 +214,206 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int t = 0; t < 8; ++t)
     qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + l32 * kD + 16 * t + 8 * g));
 
+  // Per-lane constants.  Loads: this lane's row rw_j = 16w + 4j + lane/16
+  // and chunk (lane%16) ^ swz(rw_j); lofs = row offset + chunk offset,
+  // cofs = chunk offset alone (column pieces add key * 256).
+  const int rq = lane >> 4;
+  uint32_t lofs[4], cofs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rw = 16 * w + 4 * j + rq;
+    cofs[j] = 16u * (uint32_t)((lane & 15) ^ swz(rw));
+    lofs[j] = (uint32_t)rw * (uint32_t)kRowBytes + cofs[j];
+  }
+  // K fragment t: row l32, chunk 2t + g.
+  int kofs[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) kofs[t] = l32 * kRowBytes + 16 * ((2 * t + g) ^ swz(l32));
+  // V^T fragment (kh2, dt, hi): row 16kh2 + 8hi + 4g + (lane%16)/4, chunk
+  // 4dt + 2((lane/16)%2) + (lane%4)/2, byte half lane%2; swz ignores the
+  // 16kh2 part, which becomes an immediate.
+  int vofs[2][4];
+  {
+    const int s16 = lane & 15;
+    const int vc = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int ra = 8 * hi + 4 * g + (s16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) vofs[hi][dt] = ra * kRowBytes + 16 * ((4 * dt + vc) ^ swz(ra)) + 8 * (s16 & 1);
+    }
+  }
+
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int row = row0 + 32 * w + l32;     // this lane's query row
+  const int row = row0 + 32 * w + l32;  // this lane's query row
   const float sl2 = a.scale_log2;
   const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 
-  Piece cur, nxt;
-  Stage stg;
+  // Pieces i (cur), i+1, i+2, i+3.  Column keys (this lane's four rows):
+  // ck1 of piece i+1 (its V tile is loaded this iteration), ck2 of piece i+2
+  // (K tile this iteration, V tile next), ck3 fetched this iteration.
+  Piece cur{}, p1{}, p2{}, p3{};
+  ColKeys ck0{}, ck1{}, ck2{}, ck3{};
+  auto fetch_keys = [&](const Piece& p, ColKeys& ck) {
+    if (p.is_col) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ck.k[j] = col_key(p, col, 16 * w + 4 * j + rq);
+    }
+  };
+  // Mask keys of a column piece: lanes with lane%16 == 0 hold rows 16w + 4j.
+  auto store_keys = [&](int* dst, const ColKeys& ck) {
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[16 * w + 4 * j + rq] = ck.k[j];
+    }
+  };
   it.start();
-  const bool have0 = it.next(cur);
-  if (have0) {
-    load_piece(cur, col, kr, vr, row_off, tid, stg);
-    store_piece(stg, cur.is_col, k_lds[0], v_lds[0], key_lds[0], tid);
+  const bool h0 = it.next(cur);
+  bool h1 = h0 && it.next(p1);
+  bool h2 = h1 && it.next(p2);
+  if (h0) fetch_keys(cur, ck0);
+  if (h1) fetch_keys(p1, ck1);
+  if (h2) fetch_keys(p2, ck2);
+  __builtin_amdgcn_s_waitcnt(0);
+  if (h0) {
+    load_tile(kr, kb0, w, lofs, cofs, cur, ck0);
+    load_tile(vr, vb0, w, lofs, cofs, cur, ck0);
+    if (cur.is_col) store_keys(key_lds[0], ck0);
   }
-  // Settle every outstanding load (Q fragments, first piece) here, so the
-  // wait for them is not placed at the top of the loop, where it would also
-  // stall on the prefetch of the next piece in every iteration.
+  if (h1) {
+    load_tile(kr, kb1, w, lofs, cofs, p1, ck1);
+    if (p1.is_col) store_keys(key_lds[1], ck1);
+  }
+  // Settle every outstanding load (Q fragments, first tiles) here, so the
+  // wait for them is not placed inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
   for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(qf[t]));  // defined here, not by a load
-  bool have_n = have0 && it.next(nxt);
-  if (have_n) load_piece(nxt, col, kr, vr, row_off, tid, stg);
   __syncthreads();
-  int buf = 0;
-  if (have0) {
-    do {
-      const uint16_t* kt = k_lds[buf];
-      const _Float16* vt = v_lds[buf];
+  f32x16 s_cur = f32x16{};
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb0 + kofs[t]));
+    s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s_cur, 0, 0, 0);
+  }
+  __syncthreads();  // kb0 is refilled in the first iteration
 
-      // S^T = K Q^T.  Lane: row l32, keys 8(r/4) + 4g + r%4.
-      f32x16 s = f32x16{};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + l32 * kKS + 16 * t + 8 * g));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[t], s, 0, 0, 0);
-      }
+  int i = 0;
+  // One pipeline iteration; PAR = i & 1 picks the buffers at compile time, so
+  // the compiler sees that the tiles being loaded are not the ones being read.
+  auto step = [&](auto par) -> bool {
+    constexpr int PAR = decltype(par)::value;
+    char* const kfill = PAR ? kb1 : kb0;        // K of piece i+2 (piece i's buffer)
+    const char* const kread = PAR ? kb0 : kb1;  // K of piece i+1
+    char* const vfill = PAR ? vb0 : vb1;        // V of piece i+1
+    const char* const vread = PAR ? vb1 : vb0;  // V of piece i
 
-      // Masks (causal, piece tail, A-shape window); whether any is needed is
-      // decided per piece, the mask itself per element without branches.
-      const int* keys = key_lds[buf];
-      const int kmin = cur.is_col ? keys[0] : cur.start;
-      const int kmax = cur.is_col ? keys[cur.count - 1] : cur.start + cur.count - 1;
-      const bool far = ashape && kmax >= sink && row0 + kBM - 1 - max(kmin, sink) >= window;
-      if (cur.count < kKP || kmax > row0 || far) {
-        int key[16];
-        if (cur.is_col) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) key[r] = keys[8 * (r >> 2) + 4 * g + (r & 3)];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) key[r] = cur.start + 8 * (r >> 2) + 4 * g + (r & 3);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int slot = 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = (slot < cur.count) & (key[r] <= row) &
-                          !(ashape & (key[r] >= sink) & (row - key[r] >= window));
-          s[r] = ok ? s[r] : -INFINITY;
-        }
-      }
+    if (h2) {
+      load_tile(kr, kfill, w, lofs, cofs, p2, ck2);
+      if (p2.is_col) store_keys(key_lds[(i + 2) & 3], ck2);
+    }
+    if (h1) load_tile(vr, vfill, w, lofs, cofs, p1, ck1);
+    const bool h3 = h2 && it.next(p3);
+    if (h3) fetch_keys(p3, ck3);
 
-      // Online softmax with a lazily updated max (log2 units).
-      float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
-                           fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-      mx = max_halves(mx) * sl2;
-      if (__any(mx > m_run + kLag)) {
-        const float mn = fmaxf(m_run, mx);
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
-        m_run = mn;
-        l_run *= alpha;
+    // Softmax of piece i.  Masks (causal, piece tail, A-shape window): whether
+    // any is needed is decided per piece, the mask itself per element without
+    // branches.
+    f32x16 s = s_cur;
+    const int* keys = key_lds[i & 3];
+    const int kmin = cur.is_col ? keys[0] : cur.start;
+    const int kmax = cur.is_col ? keys[cur.count - 1] : cur.start + cur.count - 1;
+    const bool far = ashape && kmax >= sink && row0 + kBM - 1 - max(kmin, sink) >= window;
+    if (cur.count < kKP || kmax > row0 || far) {
+      int key[16];
+      if (cur.is_col) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
-      f16x8 pb[2];
-      float sum = 0.f;
+        for (int r = 0; r < 16; ++r) key[r] = keys[8 * (r >> 2) + 4 * g + (r & 3)];
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -msub));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -msub));
-        const f16x2 e = {(_Float16)e0, (_Float16)e1};
-        sum = __builtin_amdgcn_fdot2(e, ones, sum, false);  // the row sum of the fp16 P fed to the MFMA
-        pb[r >> 3][r & 7] = e[0];
-        pb[r >> 3][(r & 7) + 1] = e[1];
+        for (int r = 0; r < 16; ++r) key[r] = cur.start + 8 * (r >> 2) + 4 * g + (r & 3);
       }
-      l_run += sum;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int slot = 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = (slot < cur.count) & (key[r] <= row) &
+                        !(ashape & (key[r] >= sink) & (row - key[r] >= window));
+        s[r] = ok ? s[r] : -INFINITY;
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                         fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    mx = max_halves(mx) * sl2;
+    if (__any(mx > m_run + kLag)) {
+      const float mn = fmaxf(m_run, mx);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
 
-      // O^T += V^T P^T.  A operand: lane holds d = 32dt + l32 and keys
-      // 16kh + 8(e/4) + 4g + e%4; B operand: P^T from the S registers.
-      const int s16 = lane & 15, dh = (lane >> 4) & 1;
+    // S^T of the next piece (its K tile arrived during the previous
+    // iteration) = 8 MFMAs; P = exp2(s - m) of this piece; O^T += V^T P^T of
+    // this piece = 8 MFMAs.  Issued in groups of one or two MFMAs with the
+    // exponentials, LDS reads and row sums that fit beside them, so the wave
+    // issues VALU work while the matrix core runs.  V^T fragment (kh2, dt) is
+    // the A operand of the second product: lane holds d = 32dt + l32 and keys
+    // 16kh2 + 8(e/4) + 4g + e%4; its B operand is P^T from the S registers.
+    auto kfrag = [&](int t) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kread + kofs[t]));
+    };
+    auto vfrag = [&](int kh2, int dt) {
+      const f16x4 lo = lds_read_tr(vread + vofs[0][dt] + 4096 * kh2);
+      const f16x4 hi = lds_read_tr(vread + vofs[1][dt] + 4096 * kh2);
+      return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    f32x16 s_nxt = f32x16{};
+    f16x8 pb[2];
+    bf16x8 kf[8];
+    f16x8 va[8];
+    float sum = 0.f;
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
 #pragma unroll
-      for (int kh2 = 0; kh2 < 2; ++kh2) {
-        const int ra = 16 * kh2 + 4 * g + (s16 >> 2);
+    for (int t = 0; t < 8; ++t) {
+      if (t + 2 < 8) kf[t + 2] = kfrag(t + 2);
+      va[t] = vfrag(t >> 2, t & 3);
+      s_nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[t], s_nxt, 0, 0, 0);
+      const int r = 2 * t;
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -msub));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -msub));
+      pb[r >> 3][r & 7] = (_Float16)e0;
+      pb[r >> 3][(r & 7) + 1] = (_Float16)e1;
+      const f16x2 e = {(_Float16)e0, (_Float16)e1};
+      sum = __builtin_amdgcn_fdot2(e, ones, sum, false);  // row sum of the fp16 P the MFMA consumes
+      if (t >= 4) o[t - 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[t - 4], pb[0], o[t - 4], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int ch = 32 * dt + 16 * dh + 4 * (s16 & 3);
-          const f16x4 lo = lds_read_tr(vt + ra * kVS + ch);
-          const f16x4 hi = lds_read_tr(vt + (ra + 8) * kVS + ch);
-          const f16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kh2], o[dt], 0, 0, 0);
-        }
-      }
-      const bool more = have_n;
-      if (more) store_piece(stg, nxt.is_col, k_lds[buf ^ 1], v_lds[buf ^ 1], key_lds[buf ^ 1], tid);
-      __syncthreads();
-      cur = nxt;
-      buf ^= 1;
-      have_n = more && it.next(nxt);
-      if (have_n) load_piece(nxt, col, kr, vr, row_off, tid, stg);
-      if (!more) break;
-    } while (true);
+    for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[4 + dt], pb[1], o[dt], 0, 0, 0);
+    l_run += sum;
+    __syncthreads();
+    if (!h1) return false;
+    s_cur = s_nxt;
+    cur = p1;
+    p1 = p2;
+    p2 = p3;
+    h1 = h2;
+    h2 = h3;
+    ck1 = ck2;
+    ck2 = ck3;
+    ++i;
+    return true;
+  };
+  if (h0) {
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
   }
 
   // Epilogue: out = O / l, lse = m ln2 + ln l.
