@@ -39,6 +39,7 @@ FLAGS = [
 # reductions may skip the NaN-quieting copies of their operands.
 FILE_FLAGS = {
     "sparse_attn.hip": ["-fno-honor-nans"],
+    "group_attn.hip": ["-fno-honor-nans"],
 }
 
 

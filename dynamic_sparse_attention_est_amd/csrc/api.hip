@@ -54,6 +54,9 @@ struct Plan {
   // index arena
   std::vector<int64_t> cap_r, cap_c;
   std::vector<HeadDesc> desc;
+  int hpw = 1, n_groups = 0;
+  std::vector<GroupDesc> gdesc;  // chunk u = chunk index * hkv + KV head
+  bool union_attn = false;       // attention through the chunks' union index
   size_t index_bytes = 0;
   // attention workspace
   size_t attn_bytes = 0;
@@ -128,6 +131,28 @@ std::pair<int64_t, int64_t> head_caps(const ms_head_params& q, int64_t nb) {
   return {r, c};
 }
 
+// Expected fraction of the causal (row, key) pairs a head keeps, from its
+// parameters alone: Vertical-Slash spans of 64 keys at scattered offsets cover
+// 1 - exp(-64 n_slash / n) of a row; Block-Sparse keeps min(1, k / (b + 1))
+// of block b; A-shape about (sink + window) keys of a row.
+double expected_density(const ms_head_params& q, int64_t n) {
+  const double nd = (double)n;
+  switch (q.pattern) {
+    case MS_VERTICAL_SLASH:
+      return std::min(1.0, 1.0 - std::exp(-64.0 * q.n_slash / nd) + q.n_vertical / nd);
+    case MS_BLOCK_SPARSE: {
+      const int64_t nb = n / kBM;
+      double s = 0.0;
+      for (int64_t b = 0; b < nb; ++b) s += std::min(1.0, (double)q.top_k_blocks / (double)(b + 1));
+      return s / (double)nb;
+    }
+    case MS_A_SHAPE:
+      return std::min(1.0, ((double)q.sink + (double)q.window) / (0.5 * nd));
+    default:
+      return 1.0;
+  }
+}
+
 ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& P) {
   const bool have_params = params != nullptr;
   ms_status st = validate(prob, params, have_params);
@@ -186,8 +211,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.e_scores = take((size_t)P.n_bs * P.nb * P.nb * f);
   P.e_topk = take(topk_scratch_bytes(P.n, std::max(P.n_vs, 1)));
   P.est_bytes = std::max<size_t>(off, kAlign);
-  // Index arena: descriptor table, then each head's CSR.
-  off = align_up((size_t)kTableBytes);
+  // Index arena: head table, chunk table, then each head's CSR, then each
+  // chunk's union CSR.
+  off = align_up((size_t)(kTableBytes + kGroupTableBytes));
   P.cap_r.assign(P.hq, 0);
   P.cap_c.assign(P.hq, 0);
   P.desc.assign(P.hq, HeadDesc{});
@@ -224,6 +250,43 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     d.col_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
     d.col_off = (int64_t)take((size_t)P.cap_c[h] * 4);
     d.run_off = (int64_t)take(q.pattern == MS_VERTICAL_SLASH ? (size_t)(q.n_slash + 1) * 4 : 4);
+  }
+  // Serving the heads of a KV head together pays when their key sets overlap
+  // enough that the union is at most half the keys they read one by one.
+  P.hpw = hpw_of(P.grp);
+  P.n_groups = P.hkv * (P.grp / P.hpw);
+  if (P.hpw > 1) {
+    double sum_d = 0.0, sum_u = 0.0;
+    for (int u = 0; u < P.n_groups; ++u) {
+      const int head0 = (u % P.hkv) * P.grp + (u / P.hkv) * P.hpw;
+      double miss = 1.0;
+      for (int j = 0; j < P.hpw; ++j) {
+        const double d = expected_density(P.p[head0 + j], P.n);
+        sum_d += d;
+        miss *= 1.0 - d;
+      }
+      sum_u += 1.0 - miss;
+    }
+    P.union_attn = sum_d >= 2.0 * sum_u;
+  }
+  P.gdesc.assign(P.union_attn ? P.n_groups : 0, GroupDesc{});
+  for (int u = 0; u < (int)P.gdesc.size(); ++u) {
+    const int kvh = u % P.hkv, chunk = u / P.hkv;
+    GroupDesc& g = P.gdesc[u];
+    g.head0 = kvh * P.grp + chunk * P.hpw;
+    g.nheads = P.hpw;
+    int64_t ur = 0, uc = 0;
+    for (int j = 0; j < P.hpw; ++j) {
+      ur += P.cap_r[g.head0 + j];
+      uc += P.cap_c[g.head0 + j];
+    }
+    if (ur >= (int64_t{1} << 31) || uc >= (int64_t{1} << 31))
+      return fail(MS_ERR_UNSUPPORTED, "heads %d..%d: union index capacity exceeds int32", g.head0, g.head0 + P.hpw - 1);
+    g.urng_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    g.urng_off = (int64_t)take((size_t)ur * 8);
+    g.ucol_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    g.ucol_off = (int64_t)take((size_t)uc * 4);
+    g.umask_off = (int64_t)take((size_t)uc);
   }
   P.index_bytes = off;
   // One-shot workspace.
@@ -349,6 +412,11 @@ ms_status run_build_index(const Plan& P, const int32_t* vert, const int32_t* sla
   HIP_TRY(launch_write_table(reinterpret_cast<HeadDesc*>(index), P.desc.data(), 0, P.hq, s), "index table launch");
   HIP_TRY(launch_index_build(reinterpret_cast<const HeadDesc*>(index), index, P.hq, (int)P.nb, vert, slash, blocks, s),
           "index build launch");
+  if (P.union_attn)
+    HIP_TRY(launch_union_build(reinterpret_cast<const HeadDesc*>(index),
+                               reinterpret_cast<GroupDesc*>(index + kTableBytes), P.gdesc.data(), index, P.n_groups,
+                               (int)P.nb, s),
+            "union index launch");
   return MS_OK;
 }
 
@@ -371,7 +439,10 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
   a.nb = (int)P.nb;
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
-  HIP_TRY(launch_sparse_attn(a, s), "attention launch");
+  if (P.union_attn)
+    HIP_TRY(launch_group_sparse(a, reinterpret_cast<const GroupDesc*>(index + kTableBytes), s), "attention launch");
+  else
+    HIP_TRY(launch_sparse_attn(a, s), "attention launch");
   return MS_OK;
 }
 
@@ -593,7 +664,7 @@ ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, co
   a.nb = (int)P.nb;
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
-  HIP_TRY(launch_sparse_attn(a, stream), "attention launch");
+  HIP_TRY(launch_group_dense(a, stream), "attention launch");
   return MS_OK;
 }
 

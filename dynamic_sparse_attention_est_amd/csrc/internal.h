@@ -40,6 +40,25 @@ struct HeadDesc {
 static_assert(sizeof(HeadDesc) == 96, "HeadDesc layout");
 constexpr int64_t kTableBytes = (int64_t)kMaxHeads * sizeof(HeadDesc);
 
+// Query heads per attention workgroup: the heads of one KV head are served
+// together in chunks of hpw_of(group size) heads.
+inline __host__ __device__ int hpw_of(int grp) { return grp % 4 == 0 ? 4 : grp % 2 == 0 ? 2 : 1; }
+
+// Per-chunk record (after the head table in the index arena): the union of the
+// chunk's heads' index (union_index.hip).
+struct GroupDesc {
+  int32_t head0, nheads;  // Q heads head0 .. head0 + nheads - 1
+  int32_t pad0, pad1;
+  int64_t urng_ptr_off, urng_off, ucol_ptr_off, ucol_off, umask_off;  // bytes from arena base
+  int64_t pad2;
+};
+static_assert(sizeof(GroupDesc) == 64, "GroupDesc layout");
+constexpr int64_t kGroupTableBytes = (int64_t)kMaxHeads * sizeof(GroupDesc);
+struct GroupTableArgs {
+  static constexpr int kMax = 32;
+  GroupDesc g[kMax];
+};
+
 // ------------------------------------------------------------------ launchers
 // Every launcher enqueues on `s` and returns hipGetLastError().
 
@@ -104,5 +123,12 @@ struct AttnArgs {
   int32_t out_f32;
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+// Full causal attention, query heads that share a KV head served together.
+hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s);
+// Sparse attention over the union index (groups: device table of the chunks).
+hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, hipStream_t s);
+// Union index of every chunk (after the per-head index is complete).
+hipError_t launch_union_build(const HeadDesc* table, GroupDesc* groups, const GroupDesc* host_groups, char* arena,
+                              int n_groups, int nb, hipStream_t s);
 
 }  // namespace msa
