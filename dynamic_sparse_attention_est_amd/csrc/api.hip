@@ -54,9 +54,9 @@ struct Plan {
   // index arena
   std::vector<int64_t> cap_r, cap_c;
   std::vector<HeadDesc> desc;
-  int hpw = 1, n_groups = 0;
-  std::vector<GroupDesc> gdesc;  // chunk u = chunk index * hkv + KV head
-  bool union_attn = false;       // attention through the chunks' union index
+  int hpw = 1;
+  std::vector<GroupDesc> gdesc;  // chunks served by the grouped sparse kernel
+  std::vector<int16_t> solo;     // heads served one by one
   size_t index_bytes = 0;
   // attention workspace
   size_t attn_bytes = 0;
@@ -251,42 +251,55 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     d.col_off = (int64_t)take((size_t)P.cap_c[h] * 4);
     d.run_off = (int64_t)take(q.pattern == MS_VERTICAL_SLASH ? (size_t)(q.n_slash + 1) * 4 : 4);
   }
-  // Serving the heads of a KV head together pays when their key sets overlap
-  // enough that the union is at most half the keys they read one by one.
+  // Heads of one KV head whose key sets are dense enough to overlap heavily
+  // (expected density >= 1/2) are served together, up to hpw per chunk, by the
+  // grouped kernel over the union of their index; the rest one by one.
   P.hpw = hpw_of(P.grp);
-  P.n_groups = P.hkv * (P.grp / P.hpw);
-  if (P.hpw > 1) {
-    double sum_d = 0.0, sum_u = 0.0;
-    for (int u = 0; u < P.n_groups; ++u) {
-      const int head0 = (u % P.hkv) * P.grp + (u / P.hkv) * P.hpw;
-      double miss = 1.0;
-      for (int j = 0; j < P.hpw; ++j) {
-        const double d = expected_density(P.p[head0 + j], P.n);
-        sum_d += d;
-        miss *= 1.0 - d;
-      }
-      sum_u += 1.0 - miss;
+  P.gdesc.clear();
+  P.solo.clear();
+  for (int kv = 0; kv < P.hkv; ++kv) {
+    std::vector<int> dense_heads;
+    for (int j = 0; j < P.grp; ++j) {
+      const int h = kv * P.grp + j;
+      if (P.hpw > 1 && expected_density(P.p[h], P.n) >= 0.5)
+        dense_heads.push_back(h);
+      else
+        P.solo.push_back((int16_t)h);
     }
-    P.union_attn = sum_d >= 2.0 * sum_u;
+    for (size_t c = 0; c < dense_heads.size(); c += P.hpw) {
+      const size_t m = std::min<size_t>(P.hpw, dense_heads.size() - c);
+      if (m < 2) {
+        P.solo.push_back((int16_t)dense_heads[c]);
+        continue;
+      }
+      GroupDesc g{};
+      g.kvh = kv;
+      g.nheads = (int)m;
+      for (size_t j = 0; j < m; ++j) g.head[j] = (int16_t)dense_heads[c + j];
+      P.gdesc.push_back(g);
+    }
   }
-  P.gdesc.assign(P.union_attn ? P.n_groups : 0, GroupDesc{});
-  for (int u = 0; u < (int)P.gdesc.size(); ++u) {
-    const int kvh = u % P.hkv, chunk = u / P.hkv;
-    GroupDesc& g = P.gdesc[u];
-    g.head0 = kvh * P.grp + chunk * P.hpw;
-    g.nheads = P.hpw;
+  for (GroupDesc& g : P.gdesc) {
     int64_t ur = 0, uc = 0;
-    for (int j = 0; j < P.hpw; ++j) {
-      ur += P.cap_r[g.head0 + j];
-      uc += P.cap_c[g.head0 + j];
+    for (int j = 0; j < g.nheads; ++j) {
+      ur += P.cap_r[g.head[j]];
+      uc += P.cap_c[g.head[j]];
     }
     if (ur >= (int64_t{1} << 31) || uc >= (int64_t{1} << 31))
-      return fail(MS_ERR_UNSUPPORTED, "heads %d..%d: union index capacity exceeds int32", g.head0, g.head0 + P.hpw - 1);
+      return fail(MS_ERR_UNSUPPORTED, "KV head %d: union index capacity exceeds int32", g.kvh);
     g.urng_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
     g.urng_off = (int64_t)take((size_t)ur * 8);
     g.ucol_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
     g.ucol_off = (int64_t)take((size_t)uc * 4);
     g.umask_off = (int64_t)take((size_t)uc);
+  }
+  // Solo heads: workgroups go round-robin over the 8 XCDs, so order the list
+  // to keep the heads of one KV head on one XCD when the count allows.
+  if (P.solo.size() % 8 == 0 && !P.solo.empty()) {
+    const size_t per = P.solo.size() / 8;
+    std::vector<int16_t> ordered(P.solo.size());
+    for (size_t i = 0; i < P.solo.size(); ++i) ordered[i] = P.solo[(i % 8) * per + i / 8];
+    P.solo = ordered;
   }
   P.index_bytes = off;
   // One-shot workspace.
@@ -412,10 +425,10 @@ ms_status run_build_index(const Plan& P, const int32_t* vert, const int32_t* sla
   HIP_TRY(launch_write_table(reinterpret_cast<HeadDesc*>(index), P.desc.data(), 0, P.hq, s), "index table launch");
   HIP_TRY(launch_index_build(reinterpret_cast<const HeadDesc*>(index), index, P.hq, (int)P.nb, vert, slash, blocks, s),
           "index build launch");
-  if (P.union_attn)
+  if (!P.gdesc.empty())
     HIP_TRY(launch_union_build(reinterpret_cast<const HeadDesc*>(index),
-                               reinterpret_cast<GroupDesc*>(index + kTableBytes), P.gdesc.data(), index, P.n_groups,
-                               (int)P.nb, s),
+                               reinterpret_cast<GroupDesc*>(index + kTableBytes), P.gdesc.data(), index,
+                               (int)P.gdesc.size(), (int)P.nb, s),
             "union index launch");
   return MS_OK;
 }
@@ -439,10 +452,15 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
   a.nb = (int)P.nb;
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
-  if (P.union_attn)
+  if (!P.gdesc.empty()) {
+    a.n_list = (int)P.gdesc.size();
     HIP_TRY(launch_group_sparse(a, reinterpret_cast<const GroupDesc*>(index + kTableBytes), s), "attention launch");
-  else
+  }
+  if (!P.solo.empty()) {
+    a.n_list = (int)P.solo.size();
+    for (size_t i = 0; i < P.solo.size(); ++i) a.list[i] = P.solo[i];
     HIP_TRY(launch_sparse_attn(a, s), "attention launch");
+  }
   return MS_OK;
 }
 

@@ -45,20 +45,45 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // not change during the kernel, and uniform loads from it become scalar loads
 // (tracked by lgkmcnt, so they never wait on the ring's loads to LDS).
 typedef __attribute__((address_space(4))) const int32_t c_i32;
-typedef __attribute__((address_space(4))) const u32x2 c_int2;
 typedef __attribute__((address_space(4))) const GroupDesc c_group;
 typedef __attribute__((address_space(4))) const HeadDesc c_head;
 template <class T>
 __device__ __forceinline__ T* as_const(const void* p) {
   return reinterpret_cast<T*>(reinterpret_cast<uint64_t>(p));
 }
-// Range record i ([lo, hi)) of a constant-space list, or the empty sentinel
-// past its end.
-__device__ __forceinline__ int2 range_at(c_int2* p, int i, int end) {
-  if (i >= end) return make_int2(0x7fffffff, 0x7fffffff);
-  const u32x2 v = p[i];
-  return make_int2((int)v[0], (int)v[1]);
-}
+// A window of 64 consecutive [lo, hi) range records of one list in VGPRs
+// (lane k holds record base + k; records past the list end are empty
+// sentinels).  The walks of the sparse kernel read it with readlane, so a
+// record costs no memory latency; the window is reloaded (a coalesced 512-byte
+// load) only when a walk leaves it.
+struct RangeWindow {
+  const int2* list;
+  int base, end;
+  int lo, hi;  // this lane's record
+  __device__ __forceinline__ void load(int first) {
+    typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+    base = first;
+    const int k = first + (int)(threadIdx.x & 63);
+    if (k < end) {
+      const u32x2 v = *reinterpret_cast<g_u32x2*>(reinterpret_cast<uint64_t>(list + k));
+      lo = (int)v[0];
+      hi = (int)v[1];
+    } else {
+      lo = hi = 0x7fffffff;
+    }
+  }
+  __device__ __forceinline__ void init(const int2* l, int first, int end_) {
+    list = l;
+    end = end_;
+    load(first);
+  }
+  // Record i (uniform; i >= base), or the sentinel past the end.
+  __device__ __forceinline__ int2 at(int i) {
+    if (i >= end) return make_int2(0x7fffffff, 0x7fffffff);
+    if (i - base >= 64) load(i);
+    return make_int2(__builtin_amdgcn_readlane(lo, i - base), __builtin_amdgcn_readlane(hi, i - base));
+  }
+};
 
 // One LDS array per ring stage, so that the compiler can tell the stage being
 // filled from the stages being read.
@@ -465,13 +490,19 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int jh = wv >> 1;  // head within the chunk
-  const int chunks = a.grp / HPW;
-  int pair, b;
-  map_group(blockIdx.x, a.hkv * chunks, a.nb, pair, b);
-  const int kvh = pair % a.hkv, chunk = pair / a.hkv;
-  const int h = kvh * a.grp + chunk * HPW + jh;
-  c_group* gd = as_const<c_group>(groups) + chunk * a.hkv + kvh;
+  const int jh = wv >> 1;  // head slot within the chunk
+  // Workgroup x: chunk x % n_list, query block nb - 1 - x / n_list (longest
+  // blocks first).
+  const int bi = (int)blockIdx.x / a.n_list;
+  const int u = (int)blockIdx.x - bi * a.n_list;
+  const int b = a.nb - 1 - bi;
+  c_group* gd = as_const<c_group>(groups) + u;
+  const int kvh = gd->kvh;
+  // A chunk with fewer than HPW heads leaves the waves of the missing slots
+  // idle: they load their share of the tiles and keep the barriers, nothing
+  // else.
+  const bool active = jh < gd->nheads;
+  const int h = gd->head[active ? jh : 0];
   c_head* hd = as_const<c_head>(arena) + h;
   const int64_t n = a.n;
   const int row0 = b * kBM;
@@ -491,17 +522,17 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
 
   // Union range walk (identical in every wave): pieces of <= 32 keys.
   c_i32* urp = as_const<c_i32>(arena + gd->urng_ptr_off);
-  c_int2* urng = as_const<c_int2>(arena + gd->urng_off);
   int ur = urp[b];
   const int ur_end = urp[b + 1];
+  RangeWindow uwin;
+  uwin.init(reinterpret_cast<const int2*>(arena + gd->urng_off), ur, ur_end);
   int uhi = 0, pos = 0;
-  int2 unext = range_at(urng, ur, ur_end);
   auto next_piece = [&](int& start, int& count) {
     while (pos >= uhi && ur < ur_end) {
-      pos = unext.x;
-      uhi = unext.y;
+      const int2 x = uwin.at(ur);
+      pos = x.x;
+      uhi = x.y;
       ++ur;
-      unext = range_at(urng, ur, ur_end);
     }
     if (pos < uhi) {
       start = pos;
@@ -514,20 +545,20 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
   };
   // This head's range walk: the keys of a piece that are the head's.
   c_i32* hrp = as_const<c_i32>(arena + hd->rng_ptr_off);
-  c_int2* hrng = as_const<c_int2>(arena + hd->rng_off);
   int hri = hrp[b];
   const int hr_end = hrp[b + 1];
+  RangeWindow hwin;
+  hwin.init(reinterpret_cast<const int2*>(arena + hd->rng_off), hri, hr_end);
   int hlo = kNone, hhi = kNone;
-  int2 hnext = range_at(hrng, hri, hr_end);
   auto head_advance = [&]() {
-    hlo = hnext.x;
-    hhi = hnext.y;
+    const int2 x = hwin.at(hri);
+    hlo = x.x;
+    hhi = x.y;
     if (hri < hr_end) ++hri;
-    hnext = range_at(hrng, hri, hr_end);
   };
   head_advance();
   auto head_bits = [&](int start, int count) -> uint32_t {
-    if (count == 0) return 0u;
+    if (count == 0 || !active) return 0u;
     const int e = start + count;
     while (hhi <= start) head_advance();
     uint32_t bits = 0u;
@@ -588,7 +619,7 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
 #pragma unroll
     for (int d = 0; d < kD16; ++d) key[d] = ucol[c + min(ld.lrow[d], cnt - 1)];
     const int mk = umask[c + min(lane & 31, cnt - 1)];
-    const uint32_t bits = (uint32_t)__ballot(lane < cnt && ((mk >> jh) & 1));
+    const uint32_t bits = active ? (uint32_t)__ballot(lane < cnt && ((mk >> jh) & 1)) : 0u;
     if (wv == 0 && lane < kKP) g_col_keys[lane] = ucol[c + min(lane, cnt - 1)];
     ld.gather(stage<0>(), key);
     wait_vm_lgkm0<0>();
@@ -601,7 +632,7 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
     }
     barrier_only();
   }
-  hr.store(a, h);
+  if (active) hr.store(a, h);
 }
 
 // Heads per workgroup (HPW) and ring stages: 4 heads when the group size
@@ -626,7 +657,7 @@ __global__ __launch_bounds__(128) void group_sparse_h1(AttnArgs a, const GroupDe
 
 hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, hipStream_t s) {
   const int hpw = hpw_of(a.grp);
-  const dim3 grid((unsigned)((int64_t)a.nb * a.hkv * (a.grp / hpw)));
+  const dim3 grid((unsigned)((int64_t)a.nb * a.n_list));
   if (hpw == 4)
     hipLaunchKernelGGL(group_sparse_h4, grid, dim3(512), 0, s, a, groups, a.arena);
   else if (hpw == 2)

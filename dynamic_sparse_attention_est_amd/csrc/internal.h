@@ -44,13 +44,14 @@ constexpr int64_t kTableBytes = (int64_t)kMaxHeads * sizeof(HeadDesc);
 // together in chunks of hpw_of(group size) heads.
 inline __host__ __device__ int hpw_of(int grp) { return grp % 4 == 0 ? 4 : grp % 2 == 0 ? 2 : 1; }
 
-// Per-chunk record (after the head table in the index arena): the union of the
-// chunk's heads' index (union_index.hip).
+// Per-chunk record (after the head table in the index arena): up to four Q
+// heads of one KV head that attention serves together, and the union of
+// their index (union_index.hip).
 struct GroupDesc {
-  int32_t head0, nheads;  // Q heads head0 .. head0 + nheads - 1
-  int32_t pad0, pad1;
+  int16_t head[4];   // Q heads head[0 .. nheads)
+  int32_t kvh, nheads;
   int64_t urng_ptr_off, urng_off, ucol_ptr_off, ucol_off, umask_off;  // bytes from arena base
-  int64_t pad2;
+  int64_t pad;
 };
 static_assert(sizeof(GroupDesc) == 64, "GroupDesc layout");
 constexpr int64_t kGroupTableBytes = (int64_t)kMaxHeads * sizeof(GroupDesc);
@@ -121,6 +122,10 @@ struct AttnArgs {
   int32_t hq, hkv, grp, nb;
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
+  // Work list: the Q heads (per-head sparse kernel) or the number of chunks
+  // (grouped sparse kernel) of this launch.
+  int32_t n_list;
+  int16_t list[kMaxHeads];
 };
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 // Full causal attention, query heads that share a KV head served together.

@@ -143,18 +143,14 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile,
   }
 }
 
-// Longest query blocks first (causal work grows with b); Q heads that share a
-// KV head are kept on one XCD (workgroups are dealt round-robin over the 8
-// XCDs), so that XCD's L2 serves their common K/V rows.
-__device__ __forceinline__ void map_work(int x, int hq, int nb, int& h, int& b) {
-  const int bi = x / hq, hi = x - bi * hq;
-  b = nb - 1 - bi;
-  if ((hq & 7) == 0) {
-    const int per = hq >> 3;
-    h = (hi & 7) * per + (hi >> 3);
-  } else {
-    h = hi;
-  }
+// Longest query blocks first (causal work grows with b); within a block
+// index, workgroup x takes head list[x % n_list].  Workgroups are dealt
+// round-robin over the 8 XCDs, so the host orders the list to keep the Q
+// heads of one KV head on one XCD, whose L2 then serves their common K/V rows.
+__device__ __forceinline__ void map_work(int x, const AttnArgs& a, int& h, int& b) {
+  const int bi = x / a.n_list, hi = x - bi * a.n_list;
+  b = a.nb - 1 - bi;
+  h = a.list[hi];
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
@@ -169,7 +165,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   int h, b;
-  map_work(blockIdx.x, a.hq, a.nb, h, b);
+  map_work(blockIdx.x, a, h, b);
   const int kvh = h / a.grp;
   const int64_t n = a.n;
   const int row0 = b * kBM;
@@ -466,7 +462,7 @@ hipError_t launch_v_to_f16(const uint16_t* v, _Float16* v16, int64_t elems, hipS
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.hq * a.nb;
+  const int64_t blocks = (int64_t)a.n_list * a.nb;
   hipLaunchKernelGGL(sparse_attn_fwd, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -1,7 +1,7 @@
-// Per-group union of the sparse index for the grouped attention kernel
-// (gfx950).  Query heads that share a KV head are served by one workgroup
-// (hpw_of: up to four of them); that workgroup streams each key it needs
-// through LDS once, so it walks the union of its heads' key sets:
+// Per-chunk union of the sparse index for the grouped attention kernel
+// (gfx950).  A chunk is up to four query heads of one KV head that one
+// workgroup serves together; that workgroup streams each key it needs through
+// LDS once, so it walks the union of its heads' key sets:
 //   urng: the union of the heads' ranges of query block b (sorted, disjoint,
 //         non-touching half-open ranges), CSR over the blocks;
 //   ucol: the union of the heads' column lists (ascending, no repeats), CSR,
@@ -41,7 +41,7 @@ __device__ __forceinline__ void open_lists(const UnionArgs& a, const GroupDesc& 
     L.rng[j] = nullptr;
     L.col[j] = nullptr;
     if (j >= L.nh) continue;
-    const HeadDesc& d = a.table[gd.head0 + j];
+    const HeadDesc& d = a.table[gd.head[j]];
     const int32_t* rp = reinterpret_cast<const int32_t*>(a.arena + d.rng_ptr_off);
     const int32_t* cp = reinterpret_cast<const int32_t*>(a.arena + d.col_ptr_off);
     L.rng[j] = reinterpret_cast<const int2*>(a.arena + d.rng_off);
