@@ -256,14 +256,17 @@ struct HeadRows {
     }
   }
 
-  // Running-max update for a masked S^T; returns the max to subtract.
+  // Running-max update for a masked S^T; returns the max to subtract.  The
+  // check runs on each lane's own 16 elements (a wave-wide vote); only a
+  // rescale, which is rare once the max has settled, needs the row max
+  // across the two half-waves that hold a row.
   __device__ __forceinline__ float prep(const f32x16& s) {
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                          fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-    mx = max_halves(mx) * sl2;
+    mx *= sl2;
     if (__any(mx > m_run + kLag)) {
-      const float mn = fmaxf(m_run, mx);
+      const float mn = fmaxf(m_run, max_halves(mx));
       const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
@@ -318,6 +321,9 @@ struct HeadRows {
       pb[r >> 3][r & 7] = e[0];
       pb[r >> 3][(r & 7) + 1] = e[1];
       sum = __builtin_amdgcn_fdot2(e, ones, sum, false);
+      // keep this group's exponentials here (the compiler would otherwise
+      // sink those only the last products need to the end of the block)
+      asm volatile("" : "+v"(sum));
       if (t >= 4) o[t - 4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[t - 4], pb[0], o[t - 4], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
