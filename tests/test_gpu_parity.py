@@ -270,19 +270,38 @@ def test_empty_rows_give_zero_and_neg_inf_lse():
     check_attention(o[256:], ro[256:], "later rows")
 
 
-def test_dense_attention():
-    n = 1024
-    w = W.custom("dense", n, 4, 2, [W.dense()] * 4, recipe="vs_planted", seed=13)
+# Group sizes 1, 2, 4 and 8 take the grouped dense kernel with 1, 2, 4 and 4
+# heads per workgroup (3-, 4-, 8- and 8-stage rings; two chunks per KV head for
+# 8); n = 64 is a single query block, 64 * 37 an odd block count.
+@pytest.mark.parametrize("n,hq,hkv", [(1024, 4, 2), (64, 2, 2), (64 * 37, 3, 3), (1024, 4, 1), (640, 8, 1),
+                                      (576, 16, 2)])
+def test_dense_attention(n, hq, hkv):
+    w = W.custom("dense", n, hq, hkv, [W.dense()] * hq, recipe="vs_planted", seed=13 + n + hq)
     st = make(w)
     out = torch.empty_like(st.q)
-    lse = torch.empty((4, n), device="cuda")
+    lse = torch.empty((hq, n), device="cuda")
     ms.ms_dense_attn(st.prob, st.q, st.k, st.v, out, ms.empty_workspace(ms.ms_attn_workspace_bytes(st.prob)), lse)
     torch.cuda.synchronize()
     q, k, v = _host(st)
-    for h in range(4):
-        ro, rl = oracle.attention_head(q[h], k[h // 2], v[h // 2], oracle.dense_index(n))
+    grp = hq // hkv
+    for h in range(hq):
+        ro, rl = oracle.attention_head(q[h], k[h // grp], v[h // grp], oracle.dense_index(n))
         check_attention(f64(out)[h], ro, f"dense head {h}")
         np.testing.assert_allclose(lse.cpu().numpy()[h], rl, rtol=0, atol=LSE_ATOL)
+
+
+# Heads dense enough to be served together over their union index: group
+# sizes 2 (two heads per workgroup) and 8 (two chunks of four per KV head),
+# with A-shape heads whose per-row window cuts through the shared pieces,
+# Block-Sparse heads and columns of the Vertical-Slash heads.
+@pytest.mark.parametrize("hq,hkv,seed", [(4, 2, 21), (8, 1, 22), (16, 4, 23)])
+def test_attention_grouped_union(hq, hkv, seed):
+    n = 1280
+    pool = [W.vs(60, 120), W.ashape(64, 700), W.bs(12), W.vs(200, 90), W.dense(), W.ashape(0, 900),
+            W.vs(30, 200), W.bs(16)]
+    heads = [pool[(i + seed) % len(pool)] for i in range(hq)]
+    w = W.custom("union", n, hq, hkv, heads, recipe="vs_planted", seed=seed)
+    _attention_check(run_staged(make(w)))
 
 
 def test_one_shot_equals_staged_and_is_deterministic():
