@@ -8,9 +8,14 @@
 //         with umask[k] = bit j set when head j of the group lists column k.
 // Every head still attends only to its own keys: the attention kernel masks
 // per head (from the head's own ranges for range pieces, from umask for
-// column pieces).  One thread merges the lists of one (group, block): count
-// pass, per-group scan, fill pass; counts never exceed the sums of the heads'
-// per-block counts, which bound the arrays.
+// column pieces).  One workgroup merges the lists of one (chunk, block): each
+// entry's place in the merged order is its index in its own list plus, by
+// binary search, the number of entries of the other lists that come before it
+// (equal starts or keys ordered by list); a prefix maximum of the range ends
+// then marks where a new union range starts, and equal keys sit next to each
+// other.  Count pass, per-chunk scan, fill pass; counts never exceed the sums
+// of the heads' per-block counts, which bound the arrays.  A block whose lists
+// do not fit in LDS is merged by one thread, list by list.
 #include "block_scan.h"
 #include "internal.h"
 
@@ -53,90 +58,229 @@ __device__ __forceinline__ void open_lists(const UnionArgs& a, const GroupDesc& 
   }
 }
 
+// One thread's merge of a block's lists (blocks too large for LDS).
 template <bool kFill>
-__global__ __launch_bounds__(256) void union_pass(UnionArgs a) {
-  const int64_t items = (int64_t)a.n_groups * a.nb;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items;
-       it += (int64_t)gridDim.x * blockDim.x) {
-    const int u = (int)(it / a.nb), b = (int)(it - (int64_t)u * a.nb);
-    const GroupDesc gd = a.groups[u];
-    int32_t* urp = reinterpret_cast<int32_t*>(a.arena + gd.urng_ptr_off);
-    int32_t* ucp = reinterpret_cast<int32_t*>(a.arena + gd.ucol_ptr_off);
-    int2* urng = reinterpret_cast<int2*>(a.arena + gd.urng_off);
-    int32_t* ucol = reinterpret_cast<int32_t*>(a.arena + gd.ucol_off);
-    uint8_t* umask = reinterpret_cast<uint8_t*>(a.arena + gd.umask_off);
-    Lists L;
-    open_lists(a, gd, b, L);
-    int rbase = 0, rlim = 0, cbase = 0, clim = 0;
-    if (kFill) {
-      rbase = urp[b];
-      rlim = urp[b + 1] - rbase;
-      cbase = ucp[b];
-      clim = ucp[b + 1] - cbase;
-    }
-
-    // Ranges: repeatedly take the lowest start among the heads' cursors.
-    int nr = 0;
-    int lo = 0, hi = -1;  // current union range (none while hi < 0)
-    for (;;) {
-      int best = -1, blo = 0, bhi = 0;
-      for (int j = 0; j < L.nh; ++j) {
-        if (L.r[j] < L.r_end[j]) {
-          const int2 x = L.rng[j][L.r[j]];
-          if (best < 0 || x.x < blo) {
-            best = j;
-            blo = x.x;
-            bhi = x.y;
-          }
+__device__ int merge_ranges_seq(Lists L, int2* out, int lim) {
+  int nr = 0;
+  int lo = 0, hi = -1;  // current union range (none while hi < 0)
+  for (;;) {
+    int best = -1, blo = 0, bhi = 0;
+    for (int j = 0; j < L.nh; ++j) {
+      if (L.r[j] < L.r_end[j]) {
+        const int2 x = L.rng[j][L.r[j]];
+        if (best < 0 || x.x < blo) {
+          best = j;
+          blo = x.x;
+          bhi = x.y;
         }
       }
-      if (best < 0) break;
-      ++L.r[best];
-      if (bhi <= blo) continue;  // empty range
-      if (hi >= 0 && blo <= hi) {
-        hi = max(hi, bhi);
-      } else {
-        if (hi >= 0) {
-          if (kFill && nr < rlim) urng[rbase + nr] = make_int2(lo, hi);
-          ++nr;
-        }
-        lo = blo;
-        hi = bhi;
+    }
+    if (best < 0) break;
+    ++L.r[best];
+    if (bhi <= blo) continue;  // empty range
+    if (hi >= 0 && blo <= hi) {
+      hi = max(hi, bhi);
+    } else {
+      if (hi >= 0) {
+        if (kFill && nr < lim) out[nr] = make_int2(lo, hi);
+        ++nr;
       }
+      lo = blo;
+      hi = bhi;
     }
-    if (hi >= 0) {
-      if (kFill && nr < rlim) urng[rbase + nr] = make_int2(lo, hi);
-      ++nr;
-    }
+  }
+  if (hi >= 0) {
+    if (kFill && nr < lim) out[nr] = make_int2(lo, hi);
+    ++nr;
+  }
+  return nr;
+}
 
-    // Columns: merge, one entry per distinct key, with the mask of its heads.
-    int nc = 0;
-    for (;;) {
-      int key = 0x7fffffff;
-      for (int j = 0; j < L.nh; ++j)
-        if (L.c[j] < L.c_end[j]) key = min(key, L.col[j][L.c[j]]);
-      if (key == 0x7fffffff) break;
-      int m = 0;
-      for (int j = 0; j < L.nh; ++j) {
-        if (L.c[j] < L.c_end[j] && L.col[j][L.c[j]] == key) {
-          m |= 1 << j;
-          ++L.c[j];
-        }
+template <bool kFill>
+__device__ int merge_cols_seq(Lists L, int32_t* out, uint8_t* mask, int lim) {
+  int nc = 0;
+  for (;;) {
+    int key = 0x7fffffff;
+    for (int j = 0; j < L.nh; ++j)
+      if (L.c[j] < L.c_end[j]) key = min(key, L.col[j][L.c[j]]);
+    if (key == 0x7fffffff) break;
+    int m = 0;
+    for (int j = 0; j < L.nh; ++j) {
+      if (L.c[j] < L.c_end[j] && L.col[j][L.c[j]] == key) {
+        m |= 1 << j;
+        ++L.c[j];
       }
-      if (kFill && nc < clim) {
-        ucol[cbase + nc] = key;
-        umask[cbase + nc] = (uint8_t)m;
-      }
-      ++nc;
     }
+    if (kFill && nc < lim) {
+      out[nc] = key;
+      mask[nc] = (uint8_t)m;
+    }
+    ++nc;
+  }
+  return nc;
+}
 
-    if (!kFill) {
-      urp[b + 1] = nr;
-      ucp[b + 1] = nc;
-      if (b == 0) {
-        urp[0] = 0;
-        ucp[0] = 0;
+constexpr int kUT = 256;
+constexpr int kCapR = 4096;  // ranges of one (chunk, block) merged in LDS
+constexpr int kCapC = 8192;  // columns of one (chunk, block) merged in LDS
+
+// Entries of the other lists that precede x: for lists before `mine`, entries
+// <= x; for lists after it, entries < x (ties ordered by list).
+__device__ __forceinline__ int preceding(const int* keys, const int* off, int nh, int mine, int x) {
+  int r = 0;
+  for (int j = 0; j < nh; ++j) {
+    if (j == mine) continue;
+    int lo = off[j], hi = off[j + 1];
+    const bool le = j < mine;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (le ? keys[mid] <= x : keys[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    r += lo - off[j];
+  }
+  return r;
+}
+
+// Whether the ascending keys[lo, hi) hold x.
+__device__ __forceinline__ bool contains(const int* keys, int lo, int hi, int x) {
+  const int end = hi;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (keys[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo < end && keys[lo] == x;
+}
+
+template <bool kFill>
+__global__ __launch_bounds__(kUT) void union_block(UnionArgs a) {
+  __shared__ int s_key[kCapC];   // list entries (range starts / columns), lists one after another
+  __shared__ int s_aux[kCapC];   // range ends (ranges), merged keys (columns)
+  __shared__ int s_end[kCapR];   // merged range ends
+  __shared__ int s_off[5], s_coff[5];
+  __shared__ int s_wbuf[kUT / 64];
+  const int b = blockIdx.x, u = blockIdx.y, t = threadIdx.x;
+  const GroupDesc gd = a.groups[u];
+  int32_t* urp = reinterpret_cast<int32_t*>(a.arena + gd.urng_ptr_off);
+  int32_t* ucp = reinterpret_cast<int32_t*>(a.arena + gd.ucol_ptr_off);
+  int2* urng = reinterpret_cast<int2*>(a.arena + gd.urng_off);
+  int32_t* ucol = reinterpret_cast<int32_t*>(a.arena + gd.ucol_off);
+  uint8_t* umask = reinterpret_cast<uint8_t*>(a.arena + gd.umask_off);
+  Lists L;
+  open_lists(a, gd, b, L);
+  const int nh = L.nh;
+  if (t == 0) {
+    s_off[0] = s_coff[0] = 0;
+    for (int j = 0; j < nh; ++j) {
+      s_off[j + 1] = s_off[j] + (L.r_end[j] - L.r[j]);
+      s_coff[j + 1] = s_coff[j] + (L.c_end[j] - L.c[j]);
+    }
+  }
+  __syncthreads();
+  const int R = s_off[nh], C = s_coff[nh];
+  int rbase = 0, rlim = 0, cbase = 0, clim = 0;
+  if (kFill) {
+    rbase = urp[b];
+    rlim = urp[b + 1] - rbase;
+    cbase = ucp[b];
+    clim = ucp[b + 1] - cbase;
+  }
+  int nr = 0, nc = 0;
+
+  // ---- ranges
+  if (R > kCapR) {
+    if (t == 0) nr = merge_ranges_seq<kFill>(L, urng + rbase, rlim);
+  } else if (R > 0) {
+    for (int e = t; e < R; e += kUT) {
+      int j = 0;
+      while (e >= s_off[j + 1]) ++j;
+      const int2 x = L.rng[j][L.r[j] + e - s_off[j]];
+      s_key[e] = x.x;
+      s_aux[e] = x.y;
+    }
+    __syncthreads();
+    for (int e = t; e < R; e += kUT) {
+      int j = 0;
+      while (e >= s_off[j + 1]) ++j;
+      const int x = s_key[e];
+      const int rank = (e - s_off[j]) + preceding(s_key, s_off, nh, j, x);
+      s_end[rank] = s_aux[e];
+      s_aux[kCapR + rank] = x;  // merged starts in the upper half of s_aux
+    }
+    __syncthreads();
+    int carry_max = -1, carry_n = 0;
+    for (int c0 = 0; c0 < R; c0 += kUT) {
+      const int e = c0 + t;
+      const bool valid = e < R;
+      const int lo = valid ? s_aux[kCapR + e] : 0x7fffffff;
+      const int hi = valid ? s_end[e] : -1;
+      const bool empty = valid && hi <= lo;
+      int incl, excl, tot;
+      block_scan_max<kUT>(valid && !empty ? hi : -1, -1, s_wbuf, &incl, &excl, &tot);
+      incl = max(incl, carry_max);
+      excl = max(excl, carry_max);
+      // a range starts a union range when it begins after every end before it
+      const bool is_new = valid && !empty && (lo > excl || excl < 0);
+      int ntot;
+      const int gid = carry_n + block_excl_scan<kUT>(is_new ? 1 : 0, s_wbuf, &ntot);
+      if (kFill && is_new && gid < rlim) urng[rbase + gid].x = lo;
+      // ... and ends one when the next non-empty range begins after incl
+      if (kFill && valid && !empty) {
+        int nx = e + 1;
+        while (nx < R && s_end[nx] <= s_aux[kCapR + nx]) ++nx;  // skip empty ranges
+        const bool is_last = nx >= R || s_aux[kCapR + nx] > incl;
+        const int g = gid + (is_new ? 1 : 0) - 1;
+        if (is_last && g >= 0 && g < rlim) urng[rbase + g].y = incl;
       }
+      carry_max = max(carry_max, tot);
+      carry_n += ntot;
+    }
+    nr = carry_n;
+  }
+  __syncthreads();
+
+  // ---- columns
+  if (C > kCapC) {
+    if (t == 0) nc = merge_cols_seq<kFill>(L, ucol + cbase, umask + cbase, clim);
+  } else if (C > 0) {
+    for (int e = t; e < C; e += kUT) {
+      int j = 0;
+      while (e >= s_coff[j + 1]) ++j;
+      s_key[e] = L.col[j][L.c[j] + e - s_coff[j]];
+    }
+    __syncthreads();
+    for (int e = t; e < C; e += kUT) {
+      int j = 0;
+      while (e >= s_coff[j + 1]) ++j;
+      const int x = s_key[e];
+      s_aux[(e - s_coff[j]) + preceding(s_key, s_coff, nh, j, x)] = x;
+    }
+    __syncthreads();
+    int carry_n = 0;
+    for (int c0 = 0; c0 < C; c0 += kUT) {
+      const int e = c0 + t;
+      const bool valid = e < C;
+      const int x = valid ? s_aux[e] : 0;
+      const bool first = valid && (e == 0 || s_aux[e - 1] != x);
+      int ntot;
+      const int pos = carry_n + block_excl_scan<kUT>(first ? 1 : 0, s_wbuf, &ntot);
+      if (kFill && first && pos < clim) {
+        int m = 0;
+        for (int j = 0; j < nh; ++j)
+          if (contains(s_key, s_coff[j], s_coff[j + 1], x)) m |= 1 << j;
+        ucol[cbase + pos] = x;
+        umask[cbase + pos] = (uint8_t)m;
+      }
+      carry_n += ntot;
+    }
+    nc = carry_n;
+  }
+
+  if (!kFill && t == 0) {
+    urp[b + 1] = nr;
+    ucp[b + 1] = nc;
+    if (b == 0) {
+      urp[0] = 0;
+      ucp[0] = 0;
     }
   }
 }
@@ -177,14 +321,13 @@ hipError_t launch_union_build(const HeadDesc* table, GroupDesc* groups, const Gr
     if (e != hipSuccess) return e;
   }
   UnionArgs a{table, groups, arena, n_groups, nb};
-  const int64_t items = (int64_t)n_groups * nb;
-  const unsigned grid = (unsigned)((items + 255) / 256);
-  hipLaunchKernelGGL(union_pass<false>, dim3(grid), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)nb, (unsigned)n_groups);
+  hipLaunchKernelGGL(union_block<false>, grid, dim3(kUT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(union_scan, dim3((unsigned)n_groups), dim3(1024), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(union_pass<true>, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(union_block<true>, grid, dim3(kUT), 0, s, a);
   return hipGetLastError();
 }
 

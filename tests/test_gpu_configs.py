@@ -116,3 +116,28 @@ def test_config3_mixed_128k():
 
 def test_config4_vertical_slash_1m():
     _check_layer(4, heads_checked=[0, 29], n_blocks=3, seed=4, est_heads=[0])
+
+
+def test_union_of_many_ranges_per_block():
+    """Four Vertical-Slash heads of one KV head, dense enough (4096 slashes at
+    n = 262144, expected density 0.63) to be served over their union index,
+    with scattered slashes: the late query blocks hold more ranges across the
+    four heads than the union builder merges in LDS, so it takes the one-thread
+    merge there.  Sampled late and early blocks against the oracle."""
+    n = 262144
+    heads = [W.vs(50, 4096)] * 4
+    w = W.custom("union_many", n, 4, 1, heads, recipe="vs_planted", seed=31)
+    st = run_staged(make(w), debug=False)
+    sel = selections(st)
+    nb = n // 64
+    blocks = [0, 5, nb // 2, nb - 3, nb - 1]
+    per_head = [read_index_blocks(st.prob, st.hp, st.index, h, blocks) for h in range(4)]
+    assert sum(len(per_head[h][nb - 1][0]) for h in range(4)) > 4096, "late blocks should exceed the LDS merge"
+    q, k, v = f64(st.q), f64(st.k[0]), f64(st.v[0])
+    for h in range(4):
+        for b in blocks:
+            ref_b = oracle.vs_block_index(sel[h][1], sel[h][2], b)
+            np.testing.assert_array_equal(per_head[h][b][0], ref_b[0])
+            np.testing.assert_array_equal(per_head[h][b][1], ref_b[1])
+            ro, rl = oracle.attention_block(q[h, 64 * b:64 * b + 64], k, v, ref_b, b)
+            check_attention(f64(st.out[h, 64 * b:64 * b + 64]), ro, f"head {h} block {b}")
