@@ -255,8 +255,9 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
     ms.ms_estimate_block(prob, hp, q, k, blocks, ews)
     ev[1].record(stream)
     ms.ms_build_index(prob, hp, vert, slash, blocks, index)
+    lse_s = torch.empty((w.n_q_heads, w.n), dtype=torch.float32, device="cuda")
     ev[2].record(stream)
-    ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws)
+    ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws, lse_s)
     ev[3].record(stream)
     torch.cuda.synchronize()
     t_est, t_idx, t_att = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
@@ -264,7 +265,7 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
     if reps:
         ev[2].record(stream)
         for _ in range(reps):
-            ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws)
+            ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws, lse_s)
         ev[3].record(stream)
         torch.cuda.synchronize()
         t_att = ev[2].elapsed_time(ev[3]) / reps
@@ -279,8 +280,15 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
     if do_dense:
         dout = torch.empty_like(q)
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ms.ms_dense_attn(prob, q, k, v, dout, aws)   # warm (same kernel as the sparse one)
+        # untimed first call: warms the kernel and gives the dense log-sum-exps
+        # for the index-quality instrument
+        lse_d = torch.empty_like(lse_s)
+        ms.ms_dense_attn(prob, q, k, v, dout, aws, lse_d)
+        rec = torch.empty(w.n_q_heads, dtype=torch.float32, device="cuda")
+        ms.ms_attention_recall(prob, lse_s, lse_d, rec)
         torch.cuda.synchronize()
+        res["recall"] = rec.cpu().tolist()
+        del lse_d
         d0.record(stream)
         for _ in range(dense_steps):
             ms.ms_dense_attn(prob, q, k, v, dout, aws)
@@ -317,6 +325,16 @@ def summary(r):
     eb = estimate_bytes(r["w"])
     s["estimate_gbs"] = round(eb / (r["t_est"] / 1e3) / 1e9, 1)
     s["estimate_hbm_frac"] = round(s["estimate_gbs"] / PEAK_HBM_GBS, 4)
+    if "recall" in r:
+        # share of the full causal attention mass the estimated index keeps
+        # (mean over rows, per head), summarised over heads and per pattern
+        rec = r["recall"]
+        names = {0: "a_shape", 1: "vertical_slash", 2: "block_sparse", 3: "dense"}
+        s["attention_mass_recall"] = {"mean": round(sum(rec) / len(rec), 5), "min": round(min(rec), 5)}
+        for pat, name in names.items():
+            vals = [x for x, p in zip(rec, r["w"].heads) if p.pattern == pat]
+            if vals:
+                s["attention_mass_recall"][name] = round(sum(vals) / len(vals), 5)
     if "dense_ms" in r:
         dense_tf = 4.0 * d * r["dense_pairs"] / 1e12
         s["dense_ms"] = round(r["dense_ms"], 3)

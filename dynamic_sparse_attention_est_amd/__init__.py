@@ -87,6 +87,7 @@ def load():
         "ms_sparse_attn": (ctypes.c_int, [P, H, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ms_dense_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ms_topk_f32": (ctypes.c_int, [vp, i64, i32, vp, vp]),
+        "ms_attention_recall": (ctypes.c_int, [P, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -220,6 +221,15 @@ def ms_dense_attn(prob, q, k, v, out, ws, lse=None, stream=None) -> None:
 
 def ms_topk_f32(x: torch.Tensor, k: int, idx: torch.Tensor, stream=None) -> None:
     _check(load().ms_topk_f32(_ptr(x), x.numel(), int(k), _ptr(idx), _stream(stream)))
+
+
+def ms_attention_recall(prob, lse_sparse: torch.Tensor, lse_dense: torch.Tensor, recall: torch.Tensor,
+                        stream=None) -> None:
+    """recall[h] = mean over rows of exp(lse_sparse - lse_dense): the share of
+    the full attention mass that the sparse index keeps (fp32 tensors on the
+    device: [H_q, n], [H_q, n], [H_q])."""
+    _check(load().ms_attention_recall(ctypes.byref(prob), _ptr(lse_sparse), _ptr(lse_dense), _ptr(recall),
+                                      _stream(stream)))
 
 
 def read_index(prob, heads, index: torch.Tensor):

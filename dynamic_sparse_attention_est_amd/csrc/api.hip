@@ -701,4 +701,16 @@ ms_status ms_topk_f32(const float* x, int64_t n, int32_t k, int32_t* idx, hipStr
   return MS_OK;
 }
 
+ms_status ms_attention_recall(const ms_problem* prob, const float* lse_sparse, const float* lse_dense,
+                              float* recall, hipStream_t stream) {
+  g_err.clear();
+  Plan P;
+  MS_TRY(make_plan(prob, nullptr, P));
+  if (!lse_sparse || !lse_dense || !recall) return fail(MS_ERR_INVALID_ARG, "lse_sparse, lse_dense and recall must be non-null");
+  if (!aligned(lse_sparse, 4) || !aligned(lse_dense, 4) || !aligned(recall, 4))
+    return fail(MS_ERR_INVALID_ARG, "lse_sparse, lse_dense and recall must be 4-byte aligned");
+  HIP_TRY(launch_recall(lse_sparse, lse_dense, P.n, P.hq, recall, stream), "recall launch");
+  return MS_OK;
+}
+
 }  // extern "C"

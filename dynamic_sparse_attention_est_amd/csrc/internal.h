@@ -104,6 +104,10 @@ hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs
 hipError_t launch_bs_select(const float* scores, int nb, int n_bs, const int32_t* k_of_slot,
                             const int64_t* dst_off_of_slot, int32_t* blocks, hipStream_t s);
 
+// Attention-mass recall per head from the sparse and dense log-sum-exps.
+hipError_t launch_recall(const float* lse_sparse, const float* lse_dense, int64_t n, int hq, float* recall,
+                         hipStream_t s);
+
 // Index conversion.
 hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, const int32_t* vert,
                               const int32_t* slash, const int32_t* blocks, hipStream_t s);

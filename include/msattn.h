@@ -183,6 +183,17 @@ ms_status ms_sparse_attn(const ms_problem* prob, const ms_head_params* params, c
 ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, const void* v, void* out,
                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Index-quality instrument (MInference 1.0 summary, "Key points": the share
+ * of the attention mass that the kept entries capture).  With lse_sparse from
+ * ms_sparse_attn / ms_sparse_attn_indexed and lse_dense from ms_dense_attn on
+ * the same q, k and scale (device fp32 [H_q][n] each), the full causal
+ * attention of row i puts mass exp(lse_sparse_i - lse_dense_i) on the kept
+ * keys of that row; recall[h] (device fp32 [H_q]) receives the mean of that
+ * mass over the n rows of head h (an empty sparse row counts 0).  The sum is
+ * taken in float64 in a fixed order (deterministic). */
+ms_status ms_attention_recall(const ms_problem* prob, const float* lse_sparse, const float* lse_dense,
+                              float* recall, hipStream_t stream);
+
 /* Test hook of the selection kernel: the k largest of x[0..n) (device fp32),
  * ties to the lower index, written ascending to idx[0..min(k, n)) (device).
  * -0.0 ranks equal to +0.0; x must hold no NaN.  1 <= n <= 2^30, 0 <= k. */

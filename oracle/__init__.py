@@ -64,6 +64,8 @@ from .core import (  # noqa: F401
     block_mask,
     attention_block,
     attention_head,
+    attention_recall,
+    topk_mass,
     estimate_head,
     head_index,
 )

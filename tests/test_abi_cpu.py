@@ -172,5 +172,10 @@ def test_calls_reject_bad_arguments_before_launch():
     # top-k hook: empty input, negative k
     lib = ms.load()
     assert lib.ms_topk_f32(ctypes.c_void_p(1 << 20), 0, 1, ctypes.c_void_p(1 << 20), None) == 1
+    pr = ms.problem(1024, 4, 2)
+    assert lib.ms_attention_recall(ctypes.byref(pr), None, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
+                                   None) == 1
+    assert lib.ms_attention_recall(ctypes.byref(pr), ctypes.c_void_p((1 << 20) + 2), ctypes.c_void_p(1 << 20),
+                                   ctypes.c_void_p(1 << 20), None) == 1
     assert lib.ms_topk_f32(ctypes.c_void_p(1 << 20), 10, -1, ctypes.c_void_p(1 << 20), None) == 1
     assert b"negative" in lib.ms_last_error()

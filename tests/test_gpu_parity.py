@@ -335,3 +335,27 @@ def test_config0_end_to_end():
     assert _near_tie_ok(gv, oracle.topk(v_ref, 256), v_ref, dv, 256) == 0
     assert _near_tie_ok(gs, oracle.topk(s_ref, 512), s_ref, ds, 512) == 0
     _attention_check(st)
+
+
+# ---------------------------------------------------------------- index quality instrument
+def test_attention_recall_instrument():
+    n = 1024
+    heads = [W.vs(48, 80), W.bs(3), W.ashape(16, 100), W.dense(), W.vs(5, 2), W.ashape(0, 64), W.bs(1), W.vs(30, 50)]
+    w = W.custom("recall", n, 8, 2, heads, recipe="vs_planted", seed=41)
+    st = run_staged(make(w))
+    lse_d = torch.empty((8, n), device="cuda")
+    ms.ms_dense_attn(st.prob, st.q, st.k, st.v, torch.empty_like(st.q),
+                     ms.empty_workspace(ms.ms_attn_workspace_bytes(st.prob)), lse_d)
+    rec = torch.empty(8, device="cuda")
+    ms.ms_attention_recall(st.prob, st.lse, lse_d, rec)
+    torch.cuda.synchronize()
+    got = rec.cpu().numpy().astype(np.float64)
+    q, k, _ = _host(st)
+    idx = ms.read_index(st.prob, st.hp, st.index)
+    for h in range(8):
+        ref = oracle.attention_recall(q[h], k[kv_of(w, h)], oracle.csr_to_index(*idx[h]),
+                                      ashape=ashape_of(w.heads[h])).mean()
+        # each log-sum-exp is within LSE_ATOL, so each row's exp(difference)
+        # is within about 2 LSE_ATOL relative
+        assert abs(got[h] - ref) <= 2.5 * LSE_ATOL, f"head {h}: recall {got[h]:.6f} vs {ref:.6f}"
+    assert abs(got[3] - 1.0) <= 2.5 * LSE_ATOL  # the dense head keeps all of its mass

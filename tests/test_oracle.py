@@ -326,3 +326,78 @@ def test_attention_invariant_to_range_and_column_order():
     a, _ = oracle.attention_head(q, k, v, idx)
     b, _ = oracle.attention_head(q, k, v, shuffled)
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- index quality (attention-mass recall)
+def test_recall_of_dense_index_is_one():
+    r = rng(40)
+    n, d = 256, 128
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    m = oracle.attention_recall(q, k, oracle.dense_index(n))
+    assert np.all(np.abs(m - 1.0) <= 1e-12)
+
+
+def test_recall_zero_query_closed_form():
+    # q = 0: row i spreads its mass evenly over keys 0..i, so keeping key 0
+    # alone (one vertical, no slash) captures 1 / (i + 1) of it.
+    n, d = 320, 128
+    q = np.zeros((n, d))
+    k = rng(41).standard_normal((n, d))
+    idx = oracle.vs_index(np.array([0]), np.zeros(0, dtype=np.int64), n)
+    m = oracle.attention_recall(q, k, idx)
+    np.testing.assert_allclose(m, 1.0 / (np.arange(n) + 1.0), rtol=0, atol=1e-14)
+
+
+def test_recall_is_ratio_of_normalisers():
+    # The identity the GPU instrument uses: kept mass = exp(lse_kept - lse_all),
+    # with both log-sum-exps from torch on a different code path.
+    r = rng(42)
+    n, d = 256, 128
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    heads = [(oracle.vs_index(np.array([3, 90]), np.array([0, 17, 64]), n), None),
+             (oracle.ashape_index(8, 40, n), (8, 40))]
+    for idx, ash in heads:
+        m = oracle.attention_recall(q, k, idx, ashape=ash)
+        z = torch.from_numpy(q @ k.T / math.sqrt(d))
+        causal = torch.ones(n, n, dtype=torch.bool).tril()
+        kept = torch.from_numpy(np.concatenate([oracle.block_mask(idx[b], b, n, ash) for b in range(n // BM)]))
+        lse_all = torch.logsumexp(z.masked_fill(~causal, -math.inf), dim=1)
+        lse_kept = torch.logsumexp(z.masked_fill(~kept, -math.inf), dim=1)
+        np.testing.assert_allclose(m, torch.exp(lse_kept - lse_all).numpy(), rtol=1e-12, atol=1e-15)
+
+
+def test_recall_brute_force_tiny():
+    r = rng(43)
+    n, d = 128, 4
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    idx = oracle.bs_index([np.array([0])] + [np.array([1])])
+    m = oracle.attention_recall(q, k, idx)
+    for i in range(0, n, 7):
+        w = [math.exp(float(q[i] @ k[j]) / 2.0) for j in range(i + 1)]   # 1/sqrt(4) = 1/2
+        kept = [j for j in range(i + 1) if (i < 64 and j < 64) or (i >= 64 and 64 <= j < 128)]
+        assert abs(m[i] - sum(w[j] for j in kept) / sum(w)) <= 1e-12
+
+
+def test_topk_mass_exhaustive_and_bounds_any_index():
+    import itertools
+    r = rng(44)
+    n, d = 8, 3
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    rows = list(range(n))
+    for kk in range(0, 5):
+        got = oracle.topk_mass(q, k, rows, [min(kk, i + 1) for i in rows])
+        for i in rows:
+            z = np.array([float(q[i] @ k[j]) / math.sqrt(d) for j in range(i + 1)])
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            best = max((sum(p[list(c)]) for c in itertools.combinations(range(i + 1), min(kk, i + 1))), default=0.0)
+            assert abs(got[i] - best) <= 1e-12
+    # no index keeps more mass per row than the top entries with its own budget
+    n, d = 256, 128
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    idx = oracle.vs_index(np.array([5, 77]), np.array([0, 3, 40]), n)
+    m = oracle.attention_recall(q, k, idx)
+    budget = np.concatenate([oracle.block_mask(idx[b], b, n).sum(axis=1) for b in range(n // BM)])
+    rows = list(range(0, n, 5))
+    best = oracle.topk_mass(q, k, rows, budget[rows])
+    assert np.all(m[rows] <= best + 1e-12)
