@@ -240,19 +240,32 @@ struct HeadRows {
 
   // Element r of S^T is key slot 8(r/4) + 4g + r%4.  keys: the piece's key
   // list (column pieces) or null (key = kstart + slot).  bits: the piece's
-  // keys that belong to this head.
+  // keys that belong to this head.  Away from the diagonal and the A-shape
+  // window only the key set matters; slot 8(r/4) + r%4 (+4 in the upper half
+  // of the wave) is kept iff its bit is set, so each element costs one select
+  // on a lane mask built with scalar instructions.
   __device__ __forceinline__ void mask(f32x16& s, int kstart, const int* keys, int cnt, uint32_t bits) const {
     const int kmin = keys ? keys[0] : kstart;
     const int kmax = keys ? keys[cnt - 1] : kstart + cnt - 1;
     const bool far = ashape && kmax >= sink && row0 + kBM - 1 - max(kmin, sink) >= window;
-    if (bits != 0xffffffffu || kmax > row0 || far) {
+    if (kmax <= row0 && !far) {
+      if (bits != 0xffffffffu) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int slot = 8 * (r >> 2) + 4 * g + (r & 3);
-        const int key = keys ? keys[slot] : kstart + slot;
-        const bool ok = ((bits >> slot) & 1u) & (key <= row) & !(ashape & (key >= sink) & (row - key >= window));
-        s[r] = ok ? s[r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          const uint64_t lanes = (((bits >> c) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                                 (((bits >> (c + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+          s[r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? s[r] : -INFINITY;
+        }
       }
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int slot = 8 * (r >> 2) + 4 * g + (r & 3);
+      const int key = keys ? keys[slot] : kstart + slot;
+      const bool ok = ((bits >> slot) & 1u) & (key <= row) & !(ashape & (key >= sink) & (row - key >= window));
+      s[r] = ok ? s[r] : -INFINITY;
     }
   }
 
@@ -656,20 +669,17 @@ __global__ __launch_bounds__(256) void group_sparse_h2(AttnArgs a, const GroupDe
                                                       const char* __restrict__ arena) {
   group_sparse_body<2, 4>(a, groups, arena);
 }
-__global__ __launch_bounds__(128) void group_sparse_h1(AttnArgs a, const GroupDesc* __restrict__ groups,
-                                                      const char* __restrict__ arena) {
-  group_sparse_body<1, 3>(a, groups, arena);
-}
 
 hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, hipStream_t s) {
   const int hpw = hpw_of(a.grp);
   const dim3 grid((unsigned)((int64_t)a.nb * a.n_list));
+  // chunks exist only for group sizes with two or four heads per workgroup
   if (hpw == 4)
     hipLaunchKernelGGL(group_sparse_h4, grid, dim3(512), 0, s, a, groups, a.arena);
   else if (hpw == 2)
     hipLaunchKernelGGL(group_sparse_h2, grid, dim3(256), 0, s, a, groups, a.arena);
   else
-    hipLaunchKernelGGL(group_sparse_h1, grid, dim3(128), 0, s, a, groups, a.arena);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
