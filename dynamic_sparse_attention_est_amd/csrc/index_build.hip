@@ -160,7 +160,10 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
     const int k = d.p0;
     const int32_t* B = a.blocks + d.blk_off + (int64_t)b * k;
     const int cnt = min(k, b + 1);  // leading entries hold the selection
-    int runs = 0;
+    // Run r starts at the r-th start and ends at the r-th stop; a run may
+    // start in one pass of kT entries and stop in a later one, so starts and
+    // stops are ranked with counters of their own.
+    int runs = 0, stops = 0;
     for (int s0 = 0; s0 < cnt; s0 += kT) {
       const int i = s0 + tid;
       int start = 0, stop = 0, c = 0;
@@ -171,13 +174,13 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
       }
       int t1, t2;
       const int ps = runs + block_excl_scan<kT>(start, warp_sum, &t1);
-      const int pe = runs + block_excl_scan<kT>(stop, warp_sum, &t2);
+      const int pe = stops + block_excl_scan<kT>(stop, warp_sum, &t2);
       if (kFill) {
-        // A run's start and stop share its rank; write each half once.
         if (start && ps < rlim) rng[rbase + ps].x = min(max(0, c * kBM), end);
         if (stop && pe < rlim) rng[rbase + pe].y = min(max(0, c * kBM + kBM), end);
       }
       runs += t1;
+      stops += t2;
     }
     nr = min(runs, rcap);
   } else if (d.pattern == MS_A_SHAPE) {

@@ -211,6 +211,41 @@ def test_index_from_given_selections_bit_exact(seed):
             np.testing.assert_array_equal(g_arr, r_arr, err_msg=f"head {h} ({hd.pattern}) {name}")
 
 
+def test_block_sparse_runs_span_selection_passes():
+    """Block-Sparse budgets above the index builder's 256-entry pass: a run of
+    consecutive key blocks may start in one pass over the sorted selection and
+    stop in the next.  Given dense random selections (so such runs occur in
+    most rows), every block's CSR equals the oracle's."""
+    rng = np.random.default_rng(7)
+    n = 64 * 700
+    nb = n // 64
+    heads = [W.bs(300), W.bs(600), W.bs(257)]
+    prob, hp = ms.problem(n, len(heads), 1), ms.head_params(heads)
+    blocks, sels = [], []
+    for h in heads:
+        rows = np.full((nb, h.top_k_blocks), -1)
+        bl = []
+        for b in range(nb):
+            c = np.sort(rng.choice(b + 1, min(h.top_k_blocks, b + 1), replace=False))
+            rows[b, : len(c)] = c
+            bl.append(c)
+        blocks.append(rows.ravel())
+        sels.append(("bs", bl))
+    index = ms.empty_workspace(ms.ms_index_bytes(prob, hp))
+    ms.ms_build_index(prob, hp, None, None, _upload(np.concatenate(blocks)), index)
+    torch.cuda.synchronize()
+    got = ms.read_index(prob, hp, index)
+    spans = 0
+    for h, hd in enumerate(heads):
+        for b in range(256, nb):
+            c = sels[h][1][b]
+            spans += int(len(c) > 256 and c[256] == c[255] + 1)
+        ref = oracle.index_to_csr(oracle.head_index(hd, sels[h], n))
+        for name, g_arr, r_arr in zip(("rng_ptr", "rng", "col_ptr", "col"), got[h], ref):
+            np.testing.assert_array_equal(g_arr, r_arr, err_msg=f"head {h} (top {hd.top_k_blocks}) {name}")
+    assert spans > 100, "the selections should hold runs across the pass boundary"
+
+
 # ---------------------------------------------------------------- attention
 def _attention_check(st: Staged, blocks=None, bf16_out=True):
     w = st.w
