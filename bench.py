@@ -25,6 +25,10 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
+# Sources that decide the attention kernels of a call and their launches
+# (a recorded traffic figure is reported only while these are unchanged).
+ATTN_SOURCES = ("sparse_attn.hip", "group_attn.hip", "api.hip", "internal.h")
+
 WORKLOADS = {"vs_4k": 0, "bs_32k": 1, "ashape_128k": 2, "mixed_128k": 3, "vs_1m": 4}
 
 
@@ -121,23 +125,24 @@ def estimate_bytes(w):
     return b
 
 
-def recorded_traffic(kernel, workload, src):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 counter summary (profiles/traffic_<kernel>_<workload>.md), or
-    None when there is none or the kernel source changed since it was taken."""
+def recorded_traffic(workload, srcs):
+    """HBM bytes of one attention call on `workload` from the committed
+    rocprofv3 counter summary (profiles/traffic_attention_<workload>.md), or
+    None when there is none or the sources that decide the attention kernels
+    and their launches changed since it was taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_attention_{workload}.md")
     if not os.path.exists(path):
         return None, None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
         return None, None
     rec = json.loads(m.group(1))
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = hashlib.sha256(b"".join(open(s, "rb").read() for s in srcs)).hexdigest()
     if rec.get("source_sha256") != digest:
         return None, rec
-    return rec["traffic_bytes_per_launch"], rec
+    return rec["traffic_bytes_per_call"], rec
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -394,8 +399,8 @@ def main():
     # binds (ridge = 2.5 PFLOP/s / 8 TB/s = 312.5 FLOP/byte).
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     att_bytes = 512.0 * main_r["block_keys"]
-    src = os.path.join(ROOT, "dynamic_sparse_attention_est_amd", "csrc", "sparse_attn.hip")
-    traffic, trec = recorded_traffic("sparse_attn_fwd", a.workload, src)
+    csrc = os.path.join(ROOT, "dynamic_sparse_attention_est_amd", "csrc")
+    traffic, trec = recorded_traffic(a.workload, [os.path.join(csrc, f) for f in ATTN_SOURCES])
     hbm_view = {"achieved": main_s["attention_kv_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": main_s["attention_kv_hbm_frac"],
                 "work": "512 B per kept (64-row query block, key) pair: one bf16 K row + one fp16 V row",
@@ -406,12 +411,15 @@ def main():
     view = hbm_view if bound == "hbm" else mfma_view
     roof = {"bound": bound, "achieved": view["achieved"], "peak": view["peak"], "unit": view["unit"],
             "frac": view["frac"], "traffic": traffic,
-            "kernel": "attention stage (timed with the fp16 V copy it consumes, < 0.1% of it)",
+            "kernel": "attention stage: the sparse attention kernels of one call (on long sequences the "
+                      "per-head kernel by key segments and the combination of its records), timed with the "
+                      "fp16 V copy they consume (< 0.1% of it)",
             "work": view["work"], "flop_per_byte": main_s["attention_flop_per_byte"], "ridge": ridge,
             "hbm_view": hbm_view, "mfma_view": mfma_view}
     if traffic is not None:
         roof["traffic_over_algorithmic"] = round(traffic / att_bytes, 3)
-        roof["traffic_source"] = f"profiles/traffic_sparse_attn_fwd_{a.workload}.md"
+        roof["measured_hbm_gbs"] = round(traffic / (main_r["t_att"] / 1e3) / 1e9, 1)
+        roof["traffic_source"] = f"profiles/traffic_attention_{a.workload}.md"
     elif trec is not None:
         roof["traffic_note"] = "recorded counters are for an older kernel source; not reported"
     line = {

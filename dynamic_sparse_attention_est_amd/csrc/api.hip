@@ -34,6 +34,31 @@ ms_status device_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Key-segment mode of the per-head attention kernel (sequences of at least
+// kSegMinN keys): segments of 2^kSegShift keys, partial records in at most
+// kSegPartCap bytes of the attention workspace.
+#ifndef MSA_SEG_SHIFT
+#define MSA_SEG_SHIFT 15
+#endif
+#ifndef MSA_SEG_MIN_N
+#define MSA_SEG_MIN_N 131072
+#endif
+#ifndef MSA_SEG_CAP_MB
+#define MSA_SEG_CAP_MB 4096
+#endif
+constexpr int kSegShift = MSA_SEG_SHIFT;
+constexpr int64_t kSegMinN = MSA_SEG_MIN_N;
+constexpr size_t kSegPartCap = (size_t)MSA_SEG_CAP_MB << 20;
+
+// Record space for `heads` heads in key-segment mode: every block's records,
+// or kSegPartCap when that is less (the blocks then run in chunks), but at
+// least one block's.
+size_t seg_record_bytes(int64_t n, int64_t nb, int heads) {
+  const int64_t nseg = ((n - 1) >> kSegShift) + 1;
+  const size_t per_block = (size_t)nseg * heads * kSegRecFloats * 4;
+  return std::max(per_block, std::min(kSegPartCap, per_block * (size_t)nb));
+}
+
 struct Plan {
   int64_t n = 0, nb = 0;
   int hq = 0, hkv = 0, grp = 0;
@@ -58,8 +83,12 @@ struct Plan {
   std::vector<GroupDesc> gdesc;  // chunks served by the grouped sparse kernel
   std::vector<int16_t> solo;     // heads served one by one
   size_t index_bytes = 0;
-  // attention workspace
-  size_t attn_bytes = 0;
+  // attention workspace: fp16 V copy, then the key-segment records (without
+  // params: the most any head set needs)
+  size_t v16_bytes = 0, attn_bytes = 0;
+  std::vector<int16_t> solo_seg;  // heads served one by one, by key segments
+  int seg_shift = 0;
+  size_t seg_part_off = 0, seg_part_bytes = 0;
   // one-shot workspace
   size_t o_vert = 0, o_slash = 0, o_blocks = 0, o_est = 0, o_index = 0, o_attn = 0, o_total = 0;
 };
@@ -165,7 +194,8 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   const float scale = prob->scale == 0.f ? 1.f / std::sqrt((float)kD) : prob->scale;
   P.scale_log2 = scale * 1.4426950408889634f;
   P.out_f32 = prob->out_dtype == MS_OUT_F32;
-  P.attn_bytes = align_up((size_t)P.hkv * (size_t)P.n * kD * 2);
+  P.v16_bytes = align_up((size_t)P.hkv * (size_t)P.n * kD * 2);
+  P.attn_bytes = P.v16_bytes + (P.n >= kSegMinN ? align_up(seg_record_bytes(P.n, P.nb, P.hq)) : 0);
   if (!have_params) return MS_OK;
   P.p.assign(params, params + P.hq);
   P.vs_slot.assign(P.hq, -1);
@@ -293,13 +323,34 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     g.ucol_off = (int64_t)take((size_t)uc * 4);
     g.umask_off = (int64_t)take((size_t)uc);
   }
-  // Solo heads: workgroups go round-robin over the 8 XCDs, so order the list
-  // to keep the heads of one KV head on one XCD when the count allows.
-  if (P.solo.size() % 8 == 0 && !P.solo.empty()) {
-    const size_t per = P.solo.size() / 8;
-    std::vector<int16_t> ordered(P.solo.size());
-    for (size_t i = 0; i < P.solo.size(); ++i) ordered[i] = P.solo[(i % 8) * per + i / 8];
-    P.solo = ordered;
+  // Solo heads with long key sets (on average at least one segment per query
+  // block) on long sequences run by key segments: the workgroups in flight
+  // then share one segment of K/V in L2 instead of streaming every block's
+  // keys from HBM.  Short, local key sets (A-shape, small Block-Sparse
+  // budgets) stay whole.
+  P.solo_seg.clear();
+  if (P.n >= kSegMinN) {
+    std::vector<int16_t> keep;
+    for (int16_t h : P.solo)
+      (expected_density(P.p[h], P.n) * 0.5 * (double)P.n >= (double)(int64_t{1} << kSegShift) ? P.solo_seg : keep)
+          .push_back(h);
+    P.solo = keep;
+  }
+  // Workgroups go round-robin over the 8 XCDs, so order each list to keep
+  // the heads of one KV head on one XCD when the count allows.
+  for (std::vector<int16_t>* l : {&P.solo, &P.solo_seg}) {
+    if (l->size() % 8 != 0 || l->empty()) continue;
+    const size_t per = l->size() / 8;
+    std::vector<int16_t> ordered(l->size());
+    for (size_t i = 0; i < l->size(); ++i) ordered[i] = (*l)[(i % 8) * per + i / 8];
+    *l = ordered;
+  }
+  P.attn_bytes = P.v16_bytes;
+  if (!P.solo_seg.empty()) {
+    P.seg_shift = kSegShift;
+    P.seg_part_off = P.v16_bytes;
+    P.seg_part_bytes = seg_record_bytes(P.n, P.nb, (int)P.solo_seg.size());
+    P.attn_bytes += align_up(P.seg_part_bytes);
   }
   P.index_bytes = off;
   // One-shot workspace.
@@ -460,6 +511,25 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
     a.n_list = (int)P.solo.size();
     for (size_t i = 0; i < P.solo.size(); ++i) a.list[i] = P.solo[i];
     HIP_TRY(launch_sparse_attn(a, s), "attention launch");
+  }
+  if (!P.solo_seg.empty()) {
+    a.n_list = (int)P.solo_seg.size();
+    for (size_t i = 0; i < P.solo_seg.size(); ++i) a.list[i] = P.solo_seg[i];
+    {
+      // Chunks of query blocks whose records fit the workspace, each
+      // followed by the combination of its records.
+      const int64_t nseg = ((P.n - 1) >> P.seg_shift) + 1;
+      const size_t per_block = (size_t)nseg * a.n_list * kSegRecFloats * 4;
+      const int64_t cb = std::min<int64_t>(P.nb, (int64_t)(P.seg_part_bytes / per_block));
+      a.part = reinterpret_cast<float*>(attn_ws + P.seg_part_off);
+      a.seg_shift = P.seg_shift;
+      a.seg_n = (int)nseg;
+      for (int64_t b0 = 0; b0 < P.nb; b0 += cb) {
+        a.seg_b0 = (int)b0;
+        a.seg_nb = (int)std::min<int64_t>(cb, P.nb - b0);
+        HIP_TRY(launch_sparse_attn_seg(a, s), "attention launch");
+      }
+    }
   }
   return MS_OK;
 }
@@ -663,7 +733,7 @@ ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, co
   MS_TRY(check_tensor(v, "v"));
   MS_TRY(check_tensor(out, "out"));
   if (lse && !aligned(lse, 4)) return fail(MS_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  MS_TRY(check_ws(ws, ws_bytes, P.attn_bytes, "ws"));
+  MS_TRY(check_ws(ws, ws_bytes, P.v16_bytes, "ws"));
   _Float16* v16 = reinterpret_cast<_Float16*>(ws);
   HIP_TRY(launch_v_to_f16(static_cast<const uint16_t*>(v), v16, (int64_t)P.hkv * P.n * kD, stream),
           "V conversion launch");

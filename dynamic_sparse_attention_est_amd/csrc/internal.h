@@ -130,8 +130,22 @@ struct AttnArgs {
   // (grouped sparse kernel) of this launch.
   int32_t n_list;
   int16_t list[kMaxHeads];
+  // Key-segment mode of the per-head kernel: query blocks [seg_b0, seg_b0 +
+  // seg_nb) of every listed head, each split into key segments of
+  // 2^seg_shift keys; seg_n record slots per (head, block); partial results
+  // (kSegRecFloats floats per record) go to part.
+  float* part;
+  int32_t seg_shift, seg_b0, seg_nb, seg_n;
 };
+// Partial record of one (head, query block, key segment): the segment's
+// normalised output O_s / l_s as 64 fp32 rows of 128, then its log-sum-exp
+// per row (-inf for a row with no key in the segment).
+constexpr int kSegRowFloats = kBM * kD;
+constexpr int kSegRecFloats = kSegRowFloats + kBM;
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+// Key-segment mode: partial records of the chunk, then their combination
+// into out / lse.
+hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s);
 // Full causal attention, query heads that share a KV head served together.
 hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s);
 // Sparse attention over the union index (groups: device table of the chunks).

@@ -20,6 +20,15 @@
 // grows by more than that.  Buffer-load range checks (one KV head's rows) turn
 // reads past the sequence into zeros, so piece tails need no clamping.
 //
+// Key-segment variant (sparse_attn_seg + seg_combine), for long sequences:
+// a workgroup takes the keys of one query block that fall in one segment of
+// 2^seg_shift keys (its share of the block's ranges, cut at the segment
+// edges, and of its columns, found by a wave-wide search of the CSR) and
+// writes O / l and the log-sum-exp of that share; the combine kernel merges a
+// block's segment records in segment order.  Workgroups are numbered segment
+// first, so the ones in flight read the same segment of K/V and L2 serves
+// most of their rows; per (query block, key) the work is unchanged.
+//
 // LDS tiles are row-major (one 256-byte row per key) with the 16-byte chunks
 // of row r XOR-swizzled: chunk c sits at chunk slot c ^ swz(r).  One
 // load-to-LDS instruction fills four whole rows (1 KiB of contiguous memory
@@ -60,37 +69,49 @@ struct Piece {
   int is_col;
 };
 
-// A load the compiler keeps on the vector memory path (its address is moved
-// into VGPRs first), so it is ordered with the K/V loads by vmcnt instead of
-// sharing lgkmcnt with every LDS access.
-__device__ __forceinline__ int2 vector_load_int2(const int2* p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  uint32_t lo = (uint32_t)a, hi = (uint32_t)(a >> 32);
-  asm volatile("v_mov_b32 %0, %0" : "+v"(lo));
-  asm volatile("v_mov_b32 %0, %0" : "+v"(hi));
-  typedef __attribute__((address_space(1))) const u32x2 global_u32x2;
-  const u32x2 v = *reinterpret_cast<global_u32x2*>(((uint64_t)hi << 32) | lo);
-  return make_int2((int)v[0], (int)v[1]);
-}
-
 // Walks a query block's ranges in pieces of <= 32 consecutive keys, then its
-// column list in pieces of <= 32 listed keys.  The position is uniform; the
-// descriptor of the next range is fetched one range ahead.
+// column list in pieces of <= 32 listed keys.  The position is uniform.  Range
+// descriptors come 64 at a time, one per lane (lane l holds range wbase + l),
+// and are read with readlane: a wait for memory happens once per 64 ranges,
+// not at every range (a wait there would also wait for the K/V tiles in
+// flight).
+template <bool kClip>
 struct PieceIter {
   const int2* rng;
   int r, r_end;
   int lo, hi;
   int c, c_end;
-  int2 pre;  // descriptor of range r (valid while r < r_end)
+  int clo, chi;  // kClip: ranges are cut to the key segment [clo, chi)
+  int wbase;     // first range of the window
+  int wlo, whi;  // this lane's range of the window
+  __device__ __forceinline__ void load_window(int first) {
+    typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+    wbase = first;
+    const int k = first + (int)(threadIdx.x & 63);
+    wlo = whi = 0;
+    if (k < r_end) {
+      const u32x2 v = *reinterpret_cast<g_u32x2*>(reinterpret_cast<uint64_t>(rng + k));
+      wlo = (int)v[0];
+      whi = (int)v[1];
+    }
+    // The window is settled here (the compiler waits for the load before this
+    // use) and from then on counts as defined by this statement, so later
+    // reads of it wait for nothing.
+    asm volatile("" : "+v"(wlo), "+v"(whi));
+  }
   __device__ __forceinline__ void start() {
-    if (r < r_end) pre = vector_load_int2(rng + r);
+    if (r < r_end) load_window(r);
   }
   __device__ __forceinline__ bool next(Piece& p) {
     while (lo >= hi && r < r_end) {
-      lo = __builtin_amdgcn_readfirstlane(pre.x);
-      hi = __builtin_amdgcn_readfirstlane(pre.y);
+      if (r - wbase >= 64) load_window(r);
+      lo = __builtin_amdgcn_readlane(wlo, r - wbase);
+      hi = __builtin_amdgcn_readlane(whi, r - wbase);
+      if (kClip) {
+        lo = max(lo, clo);
+        hi = min(hi, chi);
+      }
       ++r;
-      if (r < r_end) pre = vector_load_int2(rng + r);
     }
     if (lo < hi) {
       p.start = lo;
@@ -153,7 +174,70 @@ __device__ __forceinline__ void map_work(int x, const AttnArgs& a, int& h, int& 
   h = a.list[hi];
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
+// Key-segment mode: workgroup x takes segment x / (seg_nb * n_list) of block
+// seg_b0 + seg_nb - 1 - bl and head list[hi], (bl, hi) from the rest, so the
+// workgroups in flight share one segment of every KV head's K/V rows; slot is
+// its partial record.
+__device__ __forceinline__ void map_work_seg(int x, const AttnArgs& a, int& h, int& b, int& sg, int& slot) {
+  const int per = a.seg_nb * a.n_list;
+  sg = __builtin_amdgcn_readfirstlane(x / per);
+  const int y = x - sg * per;
+  const int bl = __builtin_amdgcn_readfirstlane(y / a.n_list);
+  const int hi = y - bl * a.n_list;
+  b = a.seg_b0 + a.seg_nb - 1 - bl;
+  h = a.list[hi];
+  slot = (bl * a.n_list + hi) * a.seg_n + sg;
+}
+
+// Four lower bounds at once: for search j, the first i in [lo_j, hi_j) with
+// key_j(i) >= x_j (hi_j if none), every key nondecreasing in i.  All lanes of
+// the wave probe together, 64 probes per search and round, and the four
+// searches' probes of a round are issued together so they share one memory
+// latency.  Keys: j = 0 range ends, 1 range starts, 2 and 3 columns.
+struct Bound {
+  int lo, hi, x;
+};
+__device__ __forceinline__ void wave_lower_bounds(Bound (&s)[4], const int2* rng, global_int* col, int lane) {
+  bool done[4] = {false, false, false, false};
+  for (;;) {
+    int probe[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int size = s[j].hi - s[j].lo;
+      const int step = size > 64 ? (size + 63) >> 6 : 1;
+      const int i = s[j].lo + lane * step;
+      probe[j] = 0x7fffffff;
+      if (!done[j] && i < s[j].hi) probe[j] = j == 0 ? rng[i].y : j == 1 ? rng[i].x : col[i];
+    }
+    bool all = true;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (done[j]) continue;
+      const int size = s[j].hi - s[j].lo;
+      if (size <= 64) {
+        s[j].lo += __popcll(__ballot(probe[j] < s[j].x));
+        s[j].hi = s[j].lo;
+        done[j] = true;
+        continue;
+      }
+      const int step = (size + 63) >> 6;
+      const uint64_t ge = __ballot(probe[j] >= s[j].x);
+      if (ge & 1) {
+        s[j].hi = s[j].lo;
+        done[j] = true;
+        continue;
+      }
+      const int t = ge ? __builtin_ctzll(ge) : 64;  // key(lo + (t-1) step) < x
+      if (t < 64) s[j].hi = min(s[j].hi, s[j].lo + t * step);
+      s[j].lo = s[j].lo + (t - 1) * step + 1;
+      all = false;
+    }
+    if (all) return;
+  }
+}
+
+template <bool kSeg>
+__device__ __forceinline__ void attn_body(const AttnArgs& a) {
   __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
@@ -164,13 +248,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  int h, b;
-  map_work(blockIdx.x, a, h, b);
+  int h, b, sg = 0;
+  if (kSeg) {
+    int slot;
+    map_work_seg(blockIdx.x, a, h, b, sg, slot);
+  } else
+    map_work(blockIdx.x, a, h, b);
   const int kvh = h / a.grp;
   const int64_t n = a.n;
   const int row0 = b * kBM;
+  const int seg_lo = sg << a.seg_shift;
+  if (kSeg && seg_lo > row0 + kBM - 1) return;  // past the block's last key: no record
+  const int seg_hi = seg_lo + (1 << a.seg_shift);
 
-  PieceIter it{};
+  // Q fragments: B operand of S^T = K Q^T; lane holds row l32 of this wave's
+  // 32 rows and d = 16t + 8g .. +8.  The segment variant issues them before
+  // its index search, so the two latencies overlap.
+  const uint16_t* qh = a.q + ((int64_t)h * n + row0 + 32 * w) * kD;
+  bf16x8 qf[8];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + l32 * kD + 16 * t + 8 * g));
+  };
+  if (kSeg) load_q();
+
+  PieceIter<kSeg> it{};
   global_int* col = nullptr;
   bool ashape = false;
   int sink = 0, window = 0;
@@ -189,12 +292,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       sink = d.p0;
       window = d.p1;
     }
+    if (kSeg) {
+      // This segment's share of the block's index: ranges that end after
+      // seg_lo and start before seg_hi (cut to the segment), and columns in
+      // [seg_lo, seg_hi).
+      Bound sb[4] = {{it.r, it.r_end, seg_lo + 1}, {it.r, it.r_end, seg_hi}, {it.c, it.c_end, seg_lo},
+                     {it.c, it.c_end, seg_hi}};
+      wave_lower_bounds(sb, it.rng, col, lane);
+      it.r = __builtin_amdgcn_readfirstlane(sb[0].lo);
+      it.r_end = __builtin_amdgcn_readfirstlane(sb[1].lo);
+      it.c = __builtin_amdgcn_readfirstlane(sb[2].lo);
+      it.c_end = __builtin_amdgcn_readfirstlane(sb[3].lo);
+      it.clo = seg_lo;
+      it.chi = seg_hi;
+    }
   } else {
-    it.lo = 0;
-    it.hi = row0 + kBM;
+    it.lo = kSeg ? seg_lo : 0;
+    it.hi = kSeg ? min(seg_hi, row0 + kBM) : row0 + kBM;
   }
 
-  const uint16_t* qh = a.q + ((int64_t)h * n + row0 + 32 * w) * kD;
   // Byte size of one KV head (<= 2^31 for n <= 2^23), taken as unsigned by the
   // range check.
   const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
@@ -203,12 +319,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const __amdgpu_buffer_rsrc_t vr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
 
-  // Q fragments: B operand of S^T = K Q^T; lane holds row l32 of this wave's
-  // 32 rows and d = 16t + 8g .. +8.
-  bf16x8 qf[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + l32 * kD + 16 * t + 8 * g));
+  if (!kSeg) load_q();
 
   // Per-lane constants.  Loads: this lane's row rw_j = 16w + 4j + lane/16
   // and chunk (lane%16) ^ swz(rw_j); lofs = row offset + chunk offset,
@@ -324,17 +435,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int kmax = cur.is_col ? keys[cur.count - 1] : cur.start + cur.count - 1;
     const bool far = ashape && kmax >= sink && row0 + kBM - 1 - max(kmin, sink) >= window;
     if (cur.count < kKP || kmax > row0 || far) {
+      // Slot of element r: 8 (r / 4) + 4 g + r % 4.  In the segment variant
+      // the base is made opaque here so the sixteen slots are formed inside
+      // the masked path instead of being held in registers across the loop.
+      int g4 = 4 * g;
+      if (kSeg) asm volatile("" : "+v"(g4));
       int key[16];
       if (cur.is_col) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) key[r] = keys[8 * (r >> 2) + 4 * g + (r & 3)];
+        for (int r = 0; r < 16; ++r) key[r] = keys[8 * (r >> 2) + g4 + (r & 3)];
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) key[r] = cur.start + 8 * (r >> 2) + 4 * g + (r & 3);
+        for (int r = 0; r < 16; ++r) key[r] = cur.start + 8 * (r >> 2) + g4 + (r & 3);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int slot = 8 * (r >> 2) + 4 * g + (r & 3);
+        const int slot = 8 * (r >> 2) + g4 + (r & 3);
         const bool ok = (slot < cur.count) & (key[r] <= row) &
                         !(ashape & (key[r] >= sink) & (row - key[r] >= window));
         s[r] = ok ? s[r] : -INFINITY;
@@ -412,10 +528,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // Epilogue: out = O / l, lse = m ln2 + ln l.
   const float lt = sum_halves(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  // Epilogue: out = O / l, lse = m ln2 + ln l.  The segment variant writes
+  // the same two results to its partial record (fp32 rows of 128, then the
+  // 64 lse values), with the base pointers shifted so the row offsets match.
   const int64_t obase = ((int64_t)h * n + row) * kD;
+  float* out_f32 = reinterpret_cast<float*>(a.out);
+  float* lse = a.lse;
+  if (kSeg) {
+    int hh, bb, ss, slot;
+    map_work_seg(blockIdx.x, a, hh, bb, ss, slot);
+    float* rec = a.part + (int64_t)__builtin_amdgcn_readfirstlane(slot) * kSegRecFloats;
+    out_f32 = rec - ((int64_t)h * n + row0) * kD;
+    lse = rec + kSegRowFloats - ((int64_t)h * n + row0);
+  }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -423,8 +550,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const int d0 = 32 * dt + 8 * q4 + 4 * g;
       const float x0 = o[dt][4 * q4 + 0] * inv, x1 = o[dt][4 * q4 + 1] * inv;
       const float x2 = o[dt][4 * q4 + 2] * inv, x3 = o[dt][4 * q4 + 3] * inv;
-      if (a.out_f32) {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + d0) = f32x4{x0, x1, x2, x3};
+      if (kSeg || a.out_f32) {
+        *reinterpret_cast<f32x4*>(out_f32 + obase + d0) = f32x4{x0, x1, x2, x3};
       } else {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         const bf16x4 y = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
@@ -432,8 +559,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
   }
-  if (a.lse && g == 0)
-    a.lse[(int64_t)h * n + row] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
+  if ((kSeg || lse) && g == 0)
+    lse[(int64_t)h * n + row] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
+  attn_body<false>(a);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_seg(AttnArgs a) {
+  attn_body<true>(a);
+}
+
+// Combination of a (head, block)'s segment records (O_s / l_s and lse_s per
+// row): with M the largest lse_s of a row and c_s = e^(lse_s - M), out =
+// sum_s c_s (O_s / l_s) / sum_s c_s and lse = M + ln(sum_s c_s), summed in
+// segment order.  Thread t takes half a row: row t / 2, columns 64 (t % 2)
+// onward.
+__global__ __launch_bounds__(kThreads) void seg_combine(AttnArgs a) {
+  const int t = threadIdx.x;
+  const int rr = t >> 1, c0 = 64 * (t & 1);
+  const int bl = blockIdx.x / a.n_list, hi = blockIdx.x - bl * a.n_list;
+  const int b = a.seg_b0 + a.seg_nb - 1 - bl;
+  const int h = a.list[hi];
+  const int row0 = b * kBM;
+  const int ns = ((row0 + kBM - 1) >> a.seg_shift) + 1;
+  const float* rec0 = a.part + (int64_t)(bl * a.n_list + hi) * a.seg_n * kSegRecFloats;
+  float mx = -INFINITY;
+  for (int sg = 0; sg < ns; ++sg) mx = fmaxf(mx, rec0[(int64_t)sg * kSegRecFloats + kSegRowFloats + rr]);
+  f32x4 acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = f32x4{};
+  float den = 0.f;
+  for (int sg = 0; sg < ns; ++sg) {
+    const float* rec = rec0 + (int64_t)sg * kSegRecFloats;
+    const float ls = rec[kSegRowFloats + rr];
+    const float c = ls == -INFINITY ? 0.f : expf(ls - mx);
+    den += c;
+    const f32x4* src = reinterpret_cast<const f32x4*>(rec + rr * kD + c0);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] += c * src[j];
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  const int row = row0 + rr;
+  const int64_t obase = ((int64_t)h * a.n + row) * kD + c0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const f32x4 x = acc[j] * inv;
+    if (a.out_f32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + 4 * j) = x;
+    } else {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      const bf16x4 y = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(a.out) + obase + 4 * j) = y;
+    }
+  }
+  if (a.lse && (t & 1) == 0) a.lse[(int64_t)h * a.n + row] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
 __global__ __launch_bounds__(256) void v_to_f16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -464,6 +645,18 @@ hipError_t launch_v_to_f16(const uint16_t* v, _Float16* v16, int64_t elems, hipS
 hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_list * a.nb;
   hipLaunchKernelGGL(sparse_attn_fwd, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s) {
+  // Segments that reach the chunk's longest block.
+  const int nseg = (((a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
+  if (nseg > a.seg_n) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)nseg * a.seg_nb * a.n_list;
+  hipLaunchKernelGGL(sparse_attn_seg, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(seg_combine, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

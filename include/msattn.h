@@ -120,7 +120,12 @@ ms_status ms_index_bytes(const ms_problem* prob, const ms_head_params* params, s
 ms_status ms_index_layout(const ms_problem* prob, const ms_head_params* params,
                           int64_t* offsets, int64_t* caps);
 
-/* Workspace of the attention kernels (an fp16 copy of V). */
+/* Workspace of the attention kernels: an fp16 copy of V and, from n = 131072
+ * on, room for the partial results of the per-head kernel's key-segment mode
+ * (fp32, about 33 KB per head, query block and 32768-key segment, at most
+ * 4 GiB plus one block's worth; long query-block ranges run in chunks).  The
+ * size covers every head set of the problem; ms_dense_attn uses only the V
+ * copy. */
 ms_status ms_attn_workspace_bytes(const ms_problem* prob, size_t* bytes);
 
 /* Workspace of the one-shot ms_sparse_attn (estimation + index + attention). */

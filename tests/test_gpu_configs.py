@@ -141,3 +141,53 @@ def test_union_of_many_ranges_per_block():
             np.testing.assert_array_equal(per_head[h][b][1], ref_b[1])
             ro, rl = oracle.attention_block(q[h, 64 * b:64 * b + 64], k, v, ref_b, b)
             check_attention(f64(st.out[h, 64 * b:64 * b + 64]), ro, f"head {h} block {b}")
+
+
+@pytest.mark.parametrize("out_dtype", [ms.OUT_BF16, ms.OUT_F32])
+def test_key_segments_and_chunks(out_dtype):
+    """From n = 131072 on, heads served one by one whose key sets are long (on
+    average a segment or more per query block) run by key segments: each
+    workgroup takes one query block's keys in one segment of 32768, the
+    workgroups of a segment are dispatched together, chunks of query blocks
+    run while their partial records fit the record budget, and a second kernel
+    combines the records.  n = 262144 with five such heads (Vertical-Slash,
+    Block-Sparse and A-shape of density 0.3-0.4) beside three short ones that
+    stay whole; blocks at segment edges (511/512, 1023/1024), at the chunk
+    edge of the default 4 GiB budget, the first and last blocks and random
+    ones against the oracle, with lse; and the one-shot call bit for bit."""
+    n = 262144
+    heads = [W.vs(100, 1500), W.bs(500), W.ashape(1024, 40000), W.vs(30, 60),
+             W.vs(100, 1500), W.bs(3), W.ashape(128, 900), W.vs(500, 2000)]
+    w = W.custom("segments", n, 8, 2, heads, recipe="vs_planted", seed=41)
+    st = run_staged(make(w, out_dtype=out_dtype), debug=False)
+    sel = selections(st)
+    nb = n // 64
+    chunk = (4 << 30) // ((n // 32768) * 5 * (64 * 128 + 64) * 4)
+    edges = [0, 1, 511, 512, 1023, 1024, chunk - 1, chunk, nb - 2, nb - 1]
+    for h, p in enumerate(w.heads):
+        blocks = sorted(set(edges[h % 2::2] + sample_blocks(nb, 2, 500 + h)))
+        got_idx = read_index_blocks(st.prob, st.hp, st.index, h, blocks)
+        qh = f64(st.q[h])
+        kh, vh = f64(st.k[kv_of(w, h)]), f64(st.v[kv_of(w, h)])
+        for b in blocks:
+            if p.pattern == W.VERTICAL_SLASH:
+                ref_b = oracle.vs_block_index(sel[h][1], sel[h][2], b)
+            elif p.pattern == W.BLOCK_SPARSE:
+                ref_b = oracle.bs_block_index(sel[h][1][b])
+            else:
+                ref_b = oracle.ashape_block_index(p.sink, p.window, b)
+            np.testing.assert_array_equal(got_idx[b][0], ref_b[0], err_msg=f"head {h} block {b} ranges")
+            np.testing.assert_array_equal(got_idx[b][1], ref_b[1], err_msg=f"head {h} block {b} cols")
+            ro, rl = oracle.attention_block(qh[64 * b:64 * b + 64], kh, vh, ref_b, b, ashape=ashape_of(p))
+            rows = slice(64 * b, 64 * b + 64)
+            check_attention(f64(st.out[h, rows]), ro, f"head {h} block {b}", bf16_out=out_dtype == ms.OUT_BF16)
+            got_l = st.lse[h, rows].cpu().numpy().astype(np.float64)
+            fin = np.isfinite(rl)
+            assert np.all(np.isneginf(got_l[~fin]))
+            np.testing.assert_allclose(got_l[fin], rl[fin], rtol=0, atol=LSE_ATOL)
+        print(f"  head {h} ({p.pattern}): blocks {blocks} ok", flush=True)
+    ws = ms.empty_workspace(ms.ms_workspace_bytes(st.prob, st.hp))
+    out2 = torch.empty_like(st.out)
+    ms.ms_sparse_attn(st.prob, st.hp, st.q, st.k, st.v, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), st.out.view(torch.int16))
