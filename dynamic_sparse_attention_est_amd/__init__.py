@@ -42,7 +42,7 @@ class MsError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float), ("out_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("q_block0", ctypes.c_int32)]
 
 
 class HeadParams(ctypes.Structure):
@@ -104,8 +104,10 @@ def _check(status: int):
 
 # ---------------------------------------------------------------- structs
 def problem(n: int, n_q_heads: int, n_kv_heads: int, scale: float = 0.0, out_dtype: int = OUT_BF16,
-            head_dim: int = 128) -> Problem:
-    return Problem(n, n_q_heads, n_kv_heads, head_dim, scale, out_dtype, 0)
+            head_dim: int = 128, q_block0: int = 0) -> Problem:
+    """n keys; the call's queries are rows 64*q_block0 .. n-1 (Q, out and lse
+    hold n - 64*q_block0 rows per head)."""
+    return Problem(n, n_q_heads, n_kv_heads, head_dim, scale, out_dtype, q_block0)
 
 
 def head_params(heads: Sequence) -> ctypes.Array:
@@ -234,10 +236,11 @@ def ms_attention_recall(prob, lse_sparse: torch.Tensor, lse_dense: torch.Tensor,
 
 def read_index(prob, heads, index: torch.Tensor):
     """Copies the CSR index of every head to the host: a list over heads of
-    (rng_ptr [NB+1], rng [R, 2], col_ptr [NB+1], col [C]) int32 numpy arrays."""
+    (rng_ptr [NBq+1], rng [R, 2], col_ptr [NBq+1], col [C]) int32 numpy arrays
+    over the call's query blocks (NBq = n/64 - q_block0)."""
     offs, _ = ms_index_layout(prob, heads)
     host = index.cpu().numpy()
-    nb = prob.n // 64
+    nb = prob.n // 64 - prob.q_block0
     out = []
     for (o_rp, o_r, o_cp, o_c) in offs:
         rp = host[o_rp:o_rp + 4 * (nb + 1)].view("int32").copy()

@@ -61,6 +61,7 @@ size_t seg_record_bytes(int64_t n, int64_t nb, int heads) {
 
 struct Plan {
   int64_t n = 0, nb = 0;
+  int64_t qb0 = 0, nbq = 0, qm = 0;  // first query block, query blocks and query rows of the call
   int hq = 0, hkv = 0, grp = 0;
   float scale_log2 = 0.f;
   int out_f32 = 0;
@@ -106,7 +107,8 @@ ms_status validate(const ms_problem* prob, const ms_head_params* params, bool ne
     return fail(MS_ERR_INVALID_ARG, "n_kv_heads = %d must divide n_q_heads = %d", prob->n_kv_heads, prob->n_q_heads);
   if (prob->out_dtype != MS_OUT_BF16 && prob->out_dtype != MS_OUT_F32)
     return fail(MS_ERR_INVALID_ARG, "out_dtype = %d", prob->out_dtype);
-  if (prob->reserved != 0) return fail(MS_ERR_INVALID_ARG, "reserved must be 0");
+  if (prob->q_block0 < 0 || prob->q_block0 >= prob->n / kBM)
+    return fail(MS_ERR_INVALID_ARG, "q_block0 = %d: must be 0..n/64-1", prob->q_block0);
   if (!std::isfinite(prob->scale) || prob->scale < 0.f) return fail(MS_ERR_INVALID_ARG, "scale must be finite and >= 0");
   if (!need_params) return MS_OK;
   const int64_t n = prob->n, nb = n / kBM;
@@ -138,9 +140,9 @@ ms_status validate(const ms_problem* prob, const ms_head_params* params, bool ne
 
 // Per-head capacities of the CSR, the sums over query blocks of the bounds
 // the index kernels clamp to.
-std::pair<int64_t, int64_t> head_caps(const ms_head_params& q, int64_t nb) {
+std::pair<int64_t, int64_t> head_caps(const ms_head_params& q, int64_t qb0, int64_t nb) {
   int64_t r = 0, c = 0;
-  for (int64_t b = 0; b < nb; ++b) {
+  for (int64_t b = qb0; b < nb; ++b) {
     const int64_t last = b * kBM + kBM - 1;
     switch (q.pattern) {
       case MS_VERTICAL_SLASH:
@@ -188,6 +190,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   if (st != MS_OK) return st;
   P.n = prob->n;
   P.nb = P.n / kBM;
+  P.qb0 = prob->q_block0;
+  P.nbq = P.nb - P.qb0;
+  P.qm = P.nbq * kBM;
   P.hq = prob->n_q_heads;
   P.hkv = prob->n_kv_heads;
   P.grp = P.hq / P.hkv;
@@ -195,7 +200,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.scale_log2 = scale * 1.4426950408889634f;
   P.out_f32 = prob->out_dtype == MS_OUT_F32;
   P.v16_bytes = align_up((size_t)P.hkv * (size_t)P.n * kD * 2);
-  P.attn_bytes = P.v16_bytes + (P.n >= kSegMinN ? align_up(seg_record_bytes(P.n, P.nb, P.hq)) : 0);
+  P.attn_bytes = P.v16_bytes + (P.n >= kSegMinN ? align_up(seg_record_bytes(P.n, P.nbq, P.hq)) : 0);
   if (!have_params) return MS_OK;
   P.p.assign(params, params + P.hq);
   P.vs_slot.assign(P.hq, -1);
@@ -217,7 +222,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       P.bs_slot[h] = P.n_bs++;
       P.bs_heads.push_back((int16_t)h);
       P.blk_off[h] = P.n_blocks;
-      P.n_blocks += P.nb * q.top_k_blocks;
+      P.n_blocks += P.nbq * q.top_k_blocks;
       const int kv = h / P.grp;
       if (kv_slot_of[kv] < 0) {
         kv_slot_of[kv] = (int)P.bs_kv_heads.size();
@@ -236,9 +241,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.e_diag = take((size_t)P.n_vs * P.ntiles * 320 * f);
   P.e_v = take((size_t)P.n_vs * P.n * f);
   P.e_s = take((size_t)P.n_vs * P.n * f);
-  P.e_qpool = take((size_t)P.n_bs * P.nb * kD * f);
+  P.e_qpool = take((size_t)P.n_bs * P.nbq * kD * f);
   P.e_kpool = take((size_t)P.bs_kv_heads.size() * P.nb * kD * f);
-  P.e_scores = take((size_t)P.n_bs * P.nb * P.nb * f);
+  P.e_scores = take((size_t)P.n_bs * P.nbq * P.nb * f);
   P.e_topk = take(topk_scratch_bytes(P.n, std::max(P.n_vs, 1)));
   P.est_bytes = std::max<size_t>(off, kAlign);
   // Index arena: head table, chunk table, then each head's CSR, then each
@@ -254,7 +259,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     const int b = q.pattern == MS_VERTICAL_SLASH ? q.n_slash : 0;
     const auto key = std::make_tuple(q.pattern, a, b);
     auto it = memo.find(key);
-    if (it == memo.end()) it = memo.emplace(key, head_caps(q, P.nb)).first;
+    if (it == memo.end()) it = memo.emplace(key, head_caps(q, P.qb0, P.nb)).first;
     P.cap_r[h] = it->second.first;
     P.cap_c[h] = it->second.second;
     if (P.cap_r[h] >= (int64_t{1} << 31) || P.cap_c[h] >= (int64_t{1} << 31))
@@ -275,9 +280,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     d.vert_off = P.vert_off[h];
     d.slash_off = P.slash_off[h];
     d.blk_off = P.blk_off[h];
-    d.rng_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    d.rng_ptr_off = (int64_t)take((size_t)(P.nbq + 1) * 4);
     d.rng_off = (int64_t)take((size_t)P.cap_r[h] * 8);
-    d.col_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    d.col_ptr_off = (int64_t)take((size_t)(P.nbq + 1) * 4);
     d.col_off = (int64_t)take((size_t)P.cap_c[h] * 4);
     d.run_off = (int64_t)take(q.pattern == MS_VERTICAL_SLASH ? (size_t)(q.n_slash + 1) * 4 : 4);
   }
@@ -317,9 +322,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     }
     if (ur >= (int64_t{1} << 31) || uc >= (int64_t{1} << 31))
       return fail(MS_ERR_UNSUPPORTED, "KV head %d: union index capacity exceeds int32", g.kvh);
-    g.urng_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    g.urng_ptr_off = (int64_t)take((size_t)(P.nbq + 1) * 4);
     g.urng_off = (int64_t)take((size_t)ur * 8);
-    g.ucol_ptr_off = (int64_t)take((size_t)(P.nb + 1) * 4);
+    g.ucol_ptr_off = (int64_t)take((size_t)(P.nbq + 1) * 4);
     g.ucol_off = (int64_t)take((size_t)uc * 4);
     g.umask_off = (int64_t)take((size_t)uc);
   }
@@ -349,7 +354,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   if (!P.solo_seg.empty()) {
     P.seg_shift = kSegShift;
     P.seg_part_off = P.v16_bytes;
-    P.seg_part_bytes = seg_record_bytes(P.n, P.nb, (int)P.solo_seg.size());
+    P.seg_part_bytes = seg_record_bytes(P.n, P.nbq, (int)P.solo_seg.size());
     P.attn_bytes += align_up(P.seg_part_bytes);
   }
   P.index_bytes = off;
@@ -414,7 +419,7 @@ ms_status run_estimate_vs(const Plan& P, const uint16_t* q, const uint16_t* k, i
   }
   float* v_sc = reinterpret_cast<float*>(ws + P.e_v);
   float* s_sc = reinterpret_cast<float*>(ws + P.e_s);
-  HIP_TRY(launch_vs_estimate(q, k, P.n, P.hq, P.scale_log2, g, P.n_vs, reinterpret_cast<float*>(ws + P.e_part),
+  HIP_TRY(launch_vs_estimate(q, k, P.n, P.qm, P.scale_log2, g, P.n_vs, reinterpret_cast<float*>(ws + P.e_part),
                              reinterpret_cast<float*>(ws + P.e_stats), reinterpret_cast<float*>(ws + P.e_diag), v_sc,
                              s_sc, s),
           "vertical-slash estimation launch");
@@ -453,20 +458,22 @@ ms_status run_estimate_block(const Plan& P, const uint16_t* q, const uint16_t* k
   float* qpool = reinterpret_cast<float*>(ws + P.e_qpool);
   float* kpool = reinterpret_cast<float*>(ws + P.e_kpool);
   float* scores = reinterpret_cast<float*>(ws + P.e_scores);
-  HIP_TRY(launch_bs_pool(q, P.n, P.bs_heads.data(), P.n_bs, qpool, s), "query pooling launch");
+  HIP_TRY(launch_bs_pool(q, P.qm, P.bs_heads.data(), P.n_bs, qpool, s), "query pooling launch");
   HIP_TRY(launch_bs_pool(k, P.n, P.bs_kv_heads.data(), (int)P.bs_kv_heads.size(), kpool, s), "key pooling launch");
-  HIP_TRY(launch_bs_scores(qpool, kpool, (int)P.nb, P.bs_kv_slot.data(), P.n_bs, scores, s), "block score launch");
+  HIP_TRY(launch_bs_scores(qpool, kpool, (int)P.nb, (int)P.nbq, (int)P.qb0, P.bs_kv_slot.data(), P.n_bs, scores, s),
+          "block score launch");
   std::vector<int32_t> kk(P.n_bs);
   std::vector<int64_t> off(P.n_bs);
   for (int i = 0; i < P.n_bs; ++i) {
     kk[i] = P.p[P.bs_heads[i]].top_k_blocks;
     off[i] = P.blk_off[P.bs_heads[i]];
   }
-  HIP_TRY(launch_bs_select(scores, (int)P.nb, P.n_bs, kk.data(), off.data(), blocks, s), "block selection launch");
+  HIP_TRY(launch_bs_select(scores, (int)P.nb, (int)P.nbq, (int)P.qb0, P.n_bs, kk.data(), off.data(), blocks, s),
+          "block selection launch");
   if (dbg_scores)
     for (int i = 0; i < P.n_bs; ++i)
-      HIP_TRY(hipMemcpyAsync(dbg_scores + (int64_t)P.bs_heads[i] * P.nb * P.nb, scores + (int64_t)i * P.nb * P.nb,
-                             (size_t)P.nb * P.nb * 4, hipMemcpyDeviceToDevice, s),
+      HIP_TRY(hipMemcpyAsync(dbg_scores + (int64_t)P.bs_heads[i] * P.nbq * P.nb, scores + (int64_t)i * P.nbq * P.nb,
+                             (size_t)P.nbq * P.nb * 4, hipMemcpyDeviceToDevice, s),
               "copy of block scores");
   return MS_OK;
 }
@@ -474,12 +481,13 @@ ms_status run_estimate_block(const Plan& P, const uint16_t* q, const uint16_t* k
 ms_status run_build_index(const Plan& P, const int32_t* vert, const int32_t* slash, const int32_t* blocks,
                           char* index, hipStream_t s) {
   HIP_TRY(launch_write_table(reinterpret_cast<HeadDesc*>(index), P.desc.data(), 0, P.hq, s), "index table launch");
-  HIP_TRY(launch_index_build(reinterpret_cast<const HeadDesc*>(index), index, P.hq, (int)P.nb, vert, slash, blocks, s),
+  HIP_TRY(launch_index_build(reinterpret_cast<const HeadDesc*>(index), index, P.hq, (int)P.nbq, (int)P.qb0, vert, slash,
+                             blocks, s),
           "index build launch");
   if (!P.gdesc.empty())
     HIP_TRY(launch_union_build(reinterpret_cast<const HeadDesc*>(index),
                                reinterpret_cast<GroupDesc*>(index + kTableBytes), P.gdesc.data(), index,
-                               (int)P.gdesc.size(), (int)P.nb, s),
+                               (int)P.gdesc.size(), (int)P.nbq, s),
             "union index launch");
   return MS_OK;
 }
@@ -500,7 +508,9 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
   a.hq = P.hq;
   a.hkv = P.hkv;
   a.grp = P.grp;
-  a.nb = (int)P.nb;
+  a.nb = (int)P.nbq;
+  a.qb0 = (int)P.qb0;
+  a.qm = P.qm;
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
   if (!P.gdesc.empty()) {
@@ -520,13 +530,13 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
       // followed by the combination of its records.
       const int64_t nseg = ((P.n - 1) >> P.seg_shift) + 1;
       const size_t per_block = (size_t)nseg * a.n_list * kSegRecFloats * 4;
-      const int64_t cb = std::min<int64_t>(P.nb, (int64_t)(P.seg_part_bytes / per_block));
+      const int64_t cb = std::min<int64_t>(P.nbq, (int64_t)(P.seg_part_bytes / per_block));
       a.part = reinterpret_cast<float*>(attn_ws + P.seg_part_off);
       a.seg_shift = P.seg_shift;
       a.seg_n = (int)nseg;
-      for (int64_t b0 = 0; b0 < P.nb; b0 += cb) {
+      for (int64_t b0 = 0; b0 < P.nbq; b0 += cb) {
         a.seg_b0 = (int)b0;
-        a.seg_nb = (int)std::min<int64_t>(cb, P.nb - b0);
+        a.seg_nb = (int)std::min<int64_t>(cb, P.nbq - b0);
         HIP_TRY(launch_sparse_attn_seg(a, s), "attention launch");
       }
     }
@@ -749,7 +759,9 @@ ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, co
   a.hq = P.hq;
   a.hkv = P.hkv;
   a.grp = P.grp;
-  a.nb = (int)P.nb;
+  a.nb = (int)P.nbq;
+  a.qb0 = (int)P.qb0;
+  a.qm = P.qm;
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
   HIP_TRY(launch_group_dense(a, stream), "attention launch");
@@ -779,7 +791,7 @@ ms_status ms_attention_recall(const ms_problem* prob, const float* lse_sparse, c
   if (!lse_sparse || !lse_dense || !recall) return fail(MS_ERR_INVALID_ARG, "lse_sparse, lse_dense and recall must be non-null");
   if (!aligned(lse_sparse, 4) || !aligned(lse_dense, 4) || !aligned(recall, 4))
     return fail(MS_ERR_INVALID_ARG, "lse_sparse, lse_dense and recall must be 4-byte aligned");
-  HIP_TRY(launch_recall(lse_sparse, lse_dense, P.n, P.hq, recall, stream), "recall launch");
+  HIP_TRY(launch_recall(lse_sparse, lse_dense, P.qm, P.hq, recall, stream), "recall launch");
   return MS_OK;
 }
 

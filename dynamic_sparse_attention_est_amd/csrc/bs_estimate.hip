@@ -7,6 +7,8 @@
 //               HBM-bound step: every Q/K byte of those heads is read once.
 //   bs_scores : S[b][c] = Qpool[b] . Kpool[c] for c <= b (-inf above the
 //               diagonal), a 64x64-tiled fp32 product with a fixed d order.
+//               Rows are the call's query blocks (local bl = b - q_block0);
+//               columns every key block.
 // Selection of the top key blocks per query block lives in topk.hip.
 #include "internal.h"
 
@@ -50,10 +52,10 @@ __global__ __launch_bounds__(256) void bs_pool(PoolArgs a) {
 }
 
 struct ScoreArgs {
-  const float* qpool;    // [n_bs][nb][128]
+  const float* qpool;    // [n_bs][nbq][128]
   const float* kpool;    // [n_kv][nb][128]
-  float* scores;         // [n_bs][nb][nb]
-  int32_t nb;
+  float* scores;         // [n_bs][nbq][nb]
+  int32_t nb, nbq, qb0;  // key blocks, query blocks of the call, first query block
   int16_t kv_slot[kMaxHeads];  // kpool slot of each BS slot
 };
 
@@ -64,22 +66,22 @@ __global__ __launch_bounds__(256) void bs_scores(ScoreArgs a) {
   __shared__ float qs[kST * kSP];
   __shared__ float ks[kST * kSP];
   const int ct = blockIdx.x, bt = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
-  const int nb = a.nb;
+  const int nb = a.nb, nbq = a.nbq;
   const int tx = tid & 15, ty = tid >> 4;
-  float* out = a.scores + (int64_t)slot * nb * nb;
-  const int b0 = bt * kST, c0 = ct * kST;
-  if (ct > bt) {  // strictly above the diagonal: no key block is allowed
+  float* out = a.scores + (int64_t)slot * nbq * nb;
+  const int b0 = bt * kST, c0 = ct * kST;  // first local query block, first key block
+  if (c0 > a.qb0 + b0 + kST - 1) {  // strictly above the diagonal: no key block is allowed
     for (int i = tid; i < kST * kST; i += 256) {
-      const int b = b0 + i / kST, c = c0 + i % kST;
-      if (b < nb && c < nb) out[(int64_t)b * nb + c] = -INFINITY;
+      const int bl = b0 + i / kST, c = c0 + i % kST;
+      if (bl < nbq && c < nb) out[(int64_t)bl * nb + c] = -INFINITY;
     }
     return;
   }
-  const float* qp = a.qpool + (int64_t)slot * nb * kD;
+  const float* qp = a.qpool + (int64_t)slot * nbq * kD;
   const float* kp = a.kpool + (int64_t)a.kv_slot[slot] * nb * kD;
   for (int i = tid; i < kST * kD; i += 256) {
     const int r = i / kD, d = i % kD;
-    qs[r * kSP + d] = b0 + r < nb ? qp[(int64_t)(b0 + r) * kD + d] : 0.f;
+    qs[r * kSP + d] = b0 + r < nbq ? qp[(int64_t)(b0 + r) * kD + d] : 0.f;
     ks[r * kSP + d] = c0 + r < nb ? kp[(int64_t)(c0 + r) * kD + d] : 0.f;
   }
   __syncthreads();
@@ -100,8 +102,8 @@ __global__ __launch_bounds__(256) void bs_scores(ScoreArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int b = b0 + 4 * ty + i, c = c0 + 4 * tx + j;
-      if (b < nb && c < nb) out[(int64_t)b * nb + c] = c <= b ? acc[i][j] : -INFINITY;
+      const int bl = b0 + 4 * ty + i, c = c0 + 4 * tx + j;
+      if (bl < nbq && c < nb) out[(int64_t)bl * nb + c] = c <= a.qb0 + bl ? acc[i][j] : -INFINITY;
     }
 }
 
@@ -119,17 +121,19 @@ hipError_t launch_bs_pool(const uint16_t* src, int64_t n, const int16_t* heads, 
   return hipGetLastError();
 }
 
-hipError_t launch_bs_scores(const float* qpool, const float* kpool, int nb, const int16_t* kv_slot_of_bs,
-                            int n_bs, float* scores, hipStream_t s) {
+hipError_t launch_bs_scores(const float* qpool, const float* kpool, int nb, int nbq, int qb0,
+                            const int16_t* kv_slot_of_bs, int n_bs, float* scores, hipStream_t s) {
   if (n_bs <= 0) return hipSuccess;
   ScoreArgs a;
   a.qpool = qpool;
   a.kpool = kpool;
   a.scores = scores;
   a.nb = nb;
+  a.nbq = nbq;
+  a.qb0 = qb0;
   for (int i = 0; i < n_bs; ++i) a.kv_slot[i] = kv_slot_of_bs[i];
-  const unsigned t = (unsigned)((nb + kST - 1) / kST);
-  hipLaunchKernelGGL(bs_scores, dim3(t, t, (unsigned)n_bs), dim3(256), 0, s, a);
+  const unsigned tc = (unsigned)((nb + kST - 1) / kST), tq = (unsigned)((nbq + kST - 1) / kST);
+  hipLaunchKernelGGL(bs_scores, dim3(tc, tq, (unsigned)n_bs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -365,7 +365,8 @@ struct HeadRows {
   __device__ __forceinline__ void store(const AttnArgs& a, int h) const {
     const float lt = sum_halves(l_run);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int64_t obase = ((int64_t)h * a.n + row) * kD;
+    const int64_t orow = (int64_t)h * a.qm + row - (int64_t)a.qb0 * kBM;  // this lane's row of out and lse
+    const int64_t obase = orow * kD;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -383,7 +384,7 @@ struct HeadRows {
       }
     }
     if (a.lse && g == 0)
-      a.lse[(int64_t)h * a.n + row] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
+      a.lse[orow] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
   }
 };
 
@@ -446,8 +447,8 @@ __device__ __forceinline__ void group_dense_body(const AttnArgs& a) {
   const int kvh = pair % a.hkv, chunk = pair / a.hkv;
   const int h = kvh * a.grp + chunk * HPW + (wv >> 1);
   const int64_t n = a.n;
-  const int row0 = b * kBM;
-  const int npieces = 2 * (b + 1);  // keys [0, 64b + 64)
+  const int row0 = (a.qb0 + b) * kBM;  // b indexes the call's query blocks
+  const int npieces = row0 / kKP + 2;  // keys [0, row0 + 64)
 
   const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
   const __amdgpu_buffer_rsrc_t kr =
@@ -455,7 +456,8 @@ __device__ __forceinline__ void group_dense_body(const AttnArgs& a) {
   const __amdgpu_buffer_rsrc_t vr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
   HeadRows hr;
-  hr.init(a.q + ((int64_t)h * n + row0 + 32 * (wv & 1)) * kD, lane, row0, 32 * (wv & 1), a.scale_log2);
+  hr.init(a.q + ((int64_t)h * a.qm + (int64_t)b * kBM + 32 * (wv & 1)) * kD, lane, row0, 32 * (wv & 1),
+          a.scale_log2);
   Loader<kD16> ld;
   ld.init(kr, vr, wv, lane);
 
@@ -524,7 +526,7 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
   const int h = gd->head[active ? jh : 0];
   c_head* hd = as_const<c_head>(arena) + h;
   const int64_t n = a.n;
-  const int row0 = b * kBM;
+  const int row0 = (a.qb0 + b) * kBM;  // b indexes the call's query blocks and the CSR
 
   const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
   const __amdgpu_buffer_rsrc_t kr =
@@ -532,7 +534,8 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
   const __amdgpu_buffer_rsrc_t vr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
   HeadRows hr;
-  hr.init(a.q + ((int64_t)h * n + row0 + 32 * (wv & 1)) * kD, lane, row0, 32 * (wv & 1), a.scale_log2);
+  hr.init(a.q + ((int64_t)h * a.qm + (int64_t)b * kBM + 32 * (wv & 1)) * kD, lane, row0, 32 * (wv & 1),
+          a.scale_log2);
   hr.ashape = hd->pattern == MS_A_SHAPE;
   hr.sink = hd->p0;
   hr.window = hd->p1;

@@ -4,9 +4,10 @@
 // sparse shapes do not line up with GPU tiles, so each 64-row query tile gets
 // the exact key spans it covers).
 //
-// Per head the index is a CSR over the n/64 query blocks:
-//   rng_ptr[NB+1], rng[] = (lo, hi) half-open key ranges, sorted, disjoint,
-//   non-touching; col_ptr[NB+1], col[] = ascending single keys in no range.
+// Per head the index is a CSR over the call's query blocks (NBq = n/64 -
+// q_block0 of them; local block bl is query block b = q_block0 + bl):
+//   rng_ptr[NBq+1], rng[] = (lo, hi) half-open key ranges, sorted, disjoint,
+//   non-touching; col_ptr[NBq+1], col[] = ascending single keys in no range.
 // Query block b (rows 64b .. 64b+63, last = 64b+63):
 //   Vertical-Slash: slash o <= last keeps [max(0, 64b-o), 64b+64-o).  Sorted
 //     offsets whose gaps are <= 64 form runs; a run's spans merge into one
@@ -75,8 +76,9 @@ struct IdxArgs {
   char* arena;
   const int32_t* vert;
   const int32_t* slash;
-  const int32_t* blocks;
-  int32_t nb;
+  const int32_t* blocks;  // Block-Sparse selections, [NBq][k] per head
+  int32_t nb;             // query blocks of the call (NBq)
+  int32_t qb0;            // first query block
 };
 
 // Runs of the sorted slash offsets (consecutive offsets closer than 65 share a
@@ -104,7 +106,8 @@ __global__ __launch_bounds__(kT) void vs_template(IdxArgs a) {
 template <bool kFill>
 __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
   __shared__ int warp_sum[kT / 64];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int bl = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int b = a.qb0 + bl;  // query block; bl indexes the CSR
   const HeadDesc d = a.table[h];
   const int row0 = b * kBM, last = row0 + kBM - 1, end = row0 + kBM;
   int32_t* rng_ptr = reinterpret_cast<int32_t*>(a.arena + d.rng_ptr_off);
@@ -115,10 +118,10 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
   int nr = 0, nc = 0;
   int rbase = 0, cbase = 0, rlim = 0, clim = 0;
   if (kFill) {
-    rbase = rng_ptr[b];
-    rlim = rng_ptr[b + 1] - rbase;
-    cbase = col_ptr[b];
-    clim = col_ptr[b + 1] - cbase;
+    rbase = rng_ptr[bl];
+    rlim = rng_ptr[bl + 1] - rbase;
+    cbase = col_ptr[bl];
+    clim = col_ptr[bl + 1] - cbase;
   }
 
   if (d.pattern == MS_VERTICAL_SLASH) {
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
     nc = min(cnt, ccap);
   } else if (d.pattern == MS_BLOCK_SPARSE) {
     const int k = d.p0;
-    const int32_t* B = a.blocks + d.blk_off + (int64_t)b * k;
+    const int32_t* B = a.blocks + d.blk_off + (int64_t)bl * k;
     const int cnt = min(k, b + 1);  // leading entries hold the selection
     // Run r starts at the r-th start and ends at the r-th stop; a run may
     // start in one pass of kT entries and stop in a later one, so starts and
@@ -203,9 +206,9 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
   }
 
   if (!kFill && tid == 0) {
-    rng_ptr[b + 1] = nr;
-    col_ptr[b + 1] = nc;
-    if (b == 0) {
+    rng_ptr[bl + 1] = nr;
+    col_ptr[bl + 1] = nc;
+    if (bl == 0) {
       rng_ptr[0] = 0;
       col_ptr[0] = 0;
     }
@@ -244,9 +247,9 @@ hipError_t launch_write_table(HeadDesc* table, const HeadDesc* host_descs, int f
   return hipSuccess;
 }
 
-hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, const int32_t* vert,
+hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, int qb0, const int32_t* vert,
                               const int32_t* slash, const int32_t* blocks, hipStream_t s) {
-  IdxArgs a{table, arena, vert, slash, blocks, nb};
+  IdxArgs a{table, arena, vert, slash, blocks, nb, qb0};
   hipLaunchKernelGGL(vs_template, dim3((unsigned)hq), dim3(kT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

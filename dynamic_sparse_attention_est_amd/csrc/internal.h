@@ -74,14 +74,17 @@ struct VsGroups {
   int16_t q_head[kMaxHeads];        // VS Q heads, grouped by KV head
   int16_t q_slot[kMaxHeads];        // their VS slot
 };
-hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int hq, float scale_log2,
+// q: the call's query rows [H_q][qm][128], the last of them row n - 1.
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int64_t qm, float scale_log2,
                               const VsGroups& groups, int n_vs, float* part_mz, float* stats, float* diag_part,
                               float* v_scores, float* s_scores, hipStream_t s);
 
 // Block-Sparse estimation.
 hipError_t launch_bs_pool(const uint16_t* src, int64_t n, const int16_t* heads, int nheads, float* pooled,
                           hipStream_t s);
-hipError_t launch_bs_scores(const float* qpool, const float* kpool, int nb, const int16_t* kv_slot_of_bs,
+// Rows: the call's nbq query blocks from qb0; columns: the nb key blocks.
+hipError_t launch_bs_scores(const float* qpool, const float* kpool, int nb, int nbq, int qb0,
+                            const int16_t* kv_slot_of_bs,
                             int n_bs, float* scores, hipStream_t s);
 
 // Exact top-k (ties to the lower index, ascending output).
@@ -98,10 +101,11 @@ hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, i
 size_t topk_scratch_bytes(int64_t n, int problems);
 hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, void* scratch,
                                hipStream_t s);
-// Block-Sparse selection: for every BS slot and query block b, top-min(k, b+1)
-// of scores[slot][b][0..b] into blocks (-1 padded to k).  k_of_slot and
-// dst_off_of_slot are host arrays of n_bs entries.
-hipError_t launch_bs_select(const float* scores, int nb, int n_bs, const int32_t* k_of_slot,
+// Block-Sparse selection: for every BS slot and local query block bl (query
+// block b = qb0 + bl), top-min(k, b+1) of scores[slot][bl][0..b] into blocks
+// row bl (-1 padded to k).  k_of_slot and dst_off_of_slot are host arrays of
+// n_bs entries.
+hipError_t launch_bs_select(const float* scores, int nb, int nbq, int qb0, int n_bs, const int32_t* k_of_slot,
                             const int64_t* dst_off_of_slot, int32_t* blocks, hipStream_t s);
 
 // Attention-mass recall per head from the sparse and dense log-sum-exps.
@@ -109,7 +113,8 @@ hipError_t launch_recall(const float* lse_sparse, const float* lse_dense, int64_
                          hipStream_t s);
 
 // Index conversion.
-hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, const int32_t* vert,
+// Over the call's nb query blocks, the first of them query block qb0.
+hipError_t launch_index_build(const HeadDesc* table, char* arena, int hq, int nb, int qb0, const int32_t* vert,
                               const int32_t* slash, const int32_t* blocks, hipStream_t s);
 
 // Attention.
@@ -122,8 +127,10 @@ struct AttnArgs {
   float* lse;
   const HeadDesc* table;   // null => implicit dense
   const char* arena;
-  int64_t n;
-  int32_t hq, hkv, grp, nb;
+  int64_t n;               // keys (rows of K and V)
+  int64_t qm;              // rows of Q, out and lse per head: query rows qb0*64 .. n-1
+  int32_t qb0;             // first query block
+  int32_t hq, hkv, grp, nb;  // nb: query blocks of the call (the index's blocks)
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
   // Work list: the Q heads (per-head sparse kernel) or the number of chunks

@@ -256,7 +256,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     map_work(blockIdx.x, a, h, b);
   const int kvh = h / a.grp;
   const int64_t n = a.n;
-  const int row0 = b * kBM;
+  // b indexes the call's query blocks (and the CSR); row0 is the block's
+  // first query row in the sequence, qrow0 its row in Q and out.
+  const int row0 = (a.qb0 + b) * kBM;
+  const int64_t qrow0 = (int64_t)b * kBM;
   const int seg_lo = sg << a.seg_shift;
   if (kSeg && seg_lo > row0 + kBM - 1) return;  // past the block's last key: no record
   const int seg_hi = seg_lo + (1 << a.seg_shift);
@@ -264,7 +267,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   // Q fragments: B operand of S^T = K Q^T; lane holds row l32 of this wave's
   // 32 rows and d = 16t + 8g .. +8.  The segment variant issues them before
   // its index search, so the two latencies overlap.
-  const uint16_t* qh = a.q + ((int64_t)h * n + row0 + 32 * w) * kD;
+  const uint16_t* qh = a.q + ((int64_t)h * a.qm + qrow0 + 32 * w) * kD;
   bf16x8 qf[8];
   auto load_q = [&]() {
 #pragma unroll
@@ -533,15 +536,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   // Epilogue: out = O / l, lse = m ln2 + ln l.  The segment variant writes
   // the same two results to its partial record (fp32 rows of 128, then the
   // 64 lse values), with the base pointers shifted so the row offsets match.
-  const int64_t obase = ((int64_t)h * n + row) * kD;
+  const int64_t orow = (int64_t)h * a.qm + qrow0 + 32 * w + l32;  // this lane's row of out and lse
+  const int64_t obase = orow * kD;
   float* out_f32 = reinterpret_cast<float*>(a.out);
   float* lse = a.lse;
   if (kSeg) {
     int hh, bb, ss, slot;
     map_work_seg(blockIdx.x, a, hh, bb, ss, slot);
     float* rec = a.part + (int64_t)__builtin_amdgcn_readfirstlane(slot) * kSegRecFloats;
-    out_f32 = rec - ((int64_t)h * n + row0) * kD;
-    lse = rec + kSegRowFloats - ((int64_t)h * n + row0);
+    out_f32 = rec - ((int64_t)h * a.qm + qrow0) * kD;
+    lse = rec + kSegRowFloats - ((int64_t)h * a.qm + qrow0);
   }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
@@ -560,7 +564,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     }
   }
   if ((kSeg || lse) && g == 0)
-    lse[(int64_t)h * n + row] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
+    lse[orow] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
@@ -580,9 +584,9 @@ __global__ __launch_bounds__(kThreads) void seg_combine(AttnArgs a) {
   const int t = threadIdx.x;
   const int rr = t >> 1, c0 = 64 * (t & 1);
   const int bl = blockIdx.x / a.n_list, hi = blockIdx.x - bl * a.n_list;
-  const int b = a.seg_b0 + a.seg_nb - 1 - bl;
+  const int b = a.seg_b0 + a.seg_nb - 1 - bl;  // the call's query block
   const int h = a.list[hi];
-  const int row0 = b * kBM;
+  const int row0 = (a.qb0 + b) * kBM;           // its first query row in the sequence
   const int ns = ((row0 + kBM - 1) >> a.seg_shift) + 1;
   const float* rec0 = a.part + (int64_t)(bl * a.n_list + hi) * a.seg_n * kSegRecFloats;
   float mx = -INFINITY;
@@ -601,8 +605,8 @@ __global__ __launch_bounds__(kThreads) void seg_combine(AttnArgs a) {
     for (int j = 0; j < 16; ++j) acc[j] += c * src[j];
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int row = row0 + rr;
-  const int64_t obase = ((int64_t)h * a.n + row) * kD + c0;
+  const int64_t orow = (int64_t)h * a.qm + (int64_t)b * kBM + rr;  // row of out and lse
+  const int64_t obase = orow * kD + c0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const f32x4 x = acc[j] * inv;
@@ -614,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void seg_combine(AttnArgs a) {
       *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(a.out) + obase + 4 * j) = y;
     }
   }
-  if (a.lse && (t & 1) == 0) a.lse[(int64_t)h * a.n + row] = den > 0.f ? mx + logf(den) : -INFINITY;
+  if (a.lse && (t & 1) == 0) a.lse[orow] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
 __global__ __launch_bounds__(256) void v_to_f16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -650,7 +654,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s) {
   // Segments that reach the chunk's longest block.
-  const int nseg = (((a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
+  const int nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
   if (nseg > a.seg_n) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)nseg * a.seg_nb * a.n_list;
   hipLaunchKernelGGL(sparse_attn_seg, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);

@@ -95,20 +95,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* src, int6
 
 constexpr int kSelThreads = 256;
 
-// Block-Sparse selection: query block b of BS slot `slot` keeps the top
-// min(k, b+1) of scores[slot][b][0..b]; the rest of its k-wide row is -1.
+// Block-Sparse selection: local query block bl (query block b = qb0 + bl) of
+// BS slot `slot` keeps the top min(k, b+1) of scores[slot][bl][0..b]; the
+// rest of its k-wide row is -1.
 struct BsSelArgs {
   int32_t k[kMaxHeads];
   int64_t dst_off[kMaxHeads];
 };
 
-__global__ __launch_bounds__(kSelThreads) void bs_select(const float* scores, int nb, BsSelArgs sa,
-                                                         int32_t* blocks) {
+__global__ __launch_bounds__(kSelThreads) void bs_select(const float* scores, int nb, int nbq, int qb0,
+                                                         BsSelArgs sa, int32_t* blocks) {
   __shared__ TopkSmem<kSelThreads> sm;
-  const int b = blockIdx.x, slot = blockIdx.y;
+  const int bl = blockIdx.x, slot = blockIdx.y;
+  const int b = qb0 + bl;
   const int k = sa.k[slot];
-  int32_t* row = blocks + sa.dst_off[slot] + (int64_t)b * k;
-  const float* x = scores + ((int64_t)slot * nb + b) * nb;
+  int32_t* row = blocks + sa.dst_off[slot] + (int64_t)bl * k;
+  const float* x = scores + ((int64_t)slot * nbq + bl) * nb;
   const int cnt = min(k, b + 1);
   block_topk<kSelThreads>(x, b + 1, k, row, sm);
   for (int i = cnt + threadIdx.x; i < k; i += kSelThreads) row[i] = -1;
@@ -280,7 +282,7 @@ hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs
   return hipGetLastError();
 }
 
-hipError_t launch_bs_select(const float* scores, int nb, int n_bs, const int32_t* k_of_slot,
+hipError_t launch_bs_select(const float* scores, int nb, int nbq, int qb0, int n_bs, const int32_t* k_of_slot,
                             const int64_t* dst_off_of_slot, int32_t* blocks, hipStream_t s) {
   if (n_bs <= 0) return hipSuccess;
   BsSelArgs sa;
@@ -288,7 +290,8 @@ hipError_t launch_bs_select(const float* scores, int nb, int n_bs, const int32_t
     sa.k[i] = k_of_slot[i];
     sa.dst_off[i] = dst_off_of_slot[i];
   }
-  hipLaunchKernelGGL(bs_select, dim3((unsigned)nb, (unsigned)n_bs), dim3(kSelThreads), 0, s, scores, nb, sa, blocks);
+  hipLaunchKernelGGL(bs_select, dim3((unsigned)nbq, (unsigned)n_bs), dim3(kSelThreads), 0, s, scores, nb, nbq, qb0,
+                     sa, blocks);
   return hipGetLastError();
 }
 

@@ -25,9 +25,10 @@ constexpr int kPS = kT + 1;      // LDS row stride of the probability tile (floa
 constexpr int kDiagStride = 320; // stored diagonals per tile (319 used)
 
 struct VsArgs {
-  const uint16_t* q;
+  const uint16_t* q;  // [H_q][qm][128]: the call's query rows, which end at row n - 1
   const uint16_t* k;
   int64_t n;
+  int64_t qm;
   int32_t ntiles;
   float sl2;          // scale * log2(e): logits are kept in log2 units
   float* part_mz;     // [n_vs][ntiles][64][2]
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void vs_pass1(VsArgs a) {
   for (int qi = a.groups.q_begin[gi]; qi < a.groups.q_begin[gi + 1]; ++qi) {
     const int h = a.groups.q_head[qi], slot = a.groups.q_slot[qi];
     f32x16 x[2][2];
-    logits(kf, a.q + ((int64_t)h * n + n - kLastQ) * kD, n, j0w, lane, a.sl2, x);
+    logits(kf, a.q + ((int64_t)h * a.qm + a.qm - kLastQ) * kD, n, j0w, lane, a.sl2, x);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       float m = -INFINITY;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(256) void vs_pass2(VsArgs a) {
   for (int qi = a.groups.q_begin[gi]; qi < a.groups.q_begin[gi + 1]; ++qi) {
     const int h = a.groups.q_head[qi], slot = a.groups.q_slot[qi];
     f32x16 x[2][2];
-    logits(kf, a.q + ((int64_t)h * n + n - kLastQ) * kD, n, j0w, lane, a.sl2, x);
+    logits(kf, a.q + ((int64_t)h * a.qm + a.qm - kLastQ) * kD, n, j0w, lane, a.sl2, x);
     const float* st = a.stats + (int64_t)slot * kLastQ * 2;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
@@ -234,14 +235,14 @@ __global__ __launch_bounds__(256) void vs_diag(const float* diag_part, float* s_
 
 }  // namespace
 
-hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int hq, float scale_log2,
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int64_t qm, float scale_log2,
                               const VsGroups& groups, int n_vs, float* part_mz, float* stats, float* diag_part,
                               float* v_scores, float* s_scores, hipStream_t s) {
-  (void)hq;
   VsArgs a;
   a.q = q;
   a.k = k;
   a.n = n;
+  a.qm = qm;
   a.ntiles = (int)((n + kT - 1) / kT);
   a.sl2 = scale_log2;
   a.part_mz = part_mz;

@@ -17,10 +17,14 @@
  *     line up, so the index must say which keys each query tile covers.
  *
  * Conventions for every call:
- *   Layout.   Q is [H_q][n][128], K and V are [H_kv][n][128], out is
- *             [H_q][n][128]; bfloat16, row-major, 16-byte aligned base
- *             pointers.  Batch is 1; attention is causal (pre-filling).  Q head
- *             h reads KV head h / (H_q / H_kv).
+ *   Layout.   K and V are [H_kv][n][128]; Q and out are [H_q][m][128] with
+ *             m = n - 64*q_block0 rows: the queries of sequence positions
+ *             64*q_block0 .. n-1 (m = n unless a chunk of a longer prefill is
+ *             computed, see ms_problem); bfloat16, row-major, 16-byte aligned
+ *             base pointers.  Attention is causal (pre-filling).  Q head h reads
+ *             KV head h / (H_q / H_kv).  A batch of sequences of one length is
+ *             served by stacking them along the head axis (B*H_q Q heads,
+ *             B*H_kv KV heads, sequence-major), within the head limit.
  *   Memory.   Every tensor pointer is a device pointer owned by the caller.
  *             The library allocates nothing and keeps no global state besides a
  *             thread-local error string.  Workspaces and the index arena are
@@ -59,7 +63,11 @@ typedef enum { MS_A_SHAPE = 0, MS_VERTICAL_SLASH = 1, MS_BLOCK_SPARSE = 2, MS_DE
 typedef enum { MS_OUT_BF16 = 0, MS_OUT_F32 = 1 } ms_out_dtype;
 
 /* One attention layer.  Limits of this build: head_dim == 128, n % 64 == 0,
- * 64 <= n <= 8388608, 1 <= n_q_heads <= 128, n_kv_heads divides n_q_heads. */
+ * 64 <= n <= 8388608, 1 <= n_q_heads <= 128, n_kv_heads divides n_q_heads,
+ * 0 <= q_block0 < n/64.  Below, NBq = n/64 - q_block0 is the number of query
+ * blocks of the call; "query block b" is a block of the sequence
+ * (q_block0 <= b < n/64) and arrays over query blocks are indexed by
+ * b - q_block0. */
 typedef struct {
   int64_t n;          /* sequence length: rows of Q and of K/V */
   int32_t n_q_heads;  /* H_q */
@@ -67,7 +75,12 @@ typedef struct {
   int32_t head_dim;   /* must be 128 */
   float scale;        /* softmax scale on q.k; 0 selects 1/sqrt(head_dim) */
   int32_t out_dtype;  /* ms_out_dtype */
-  int32_t reserved;   /* must be 0 */
+  int32_t q_block0;   /* chunked prefill: the call computes query blocks
+                         q_block0 .. n/64-1 only (rows 64*q_block0 .. n-1),
+                         attending to all n keys; 0 for the whole sequence.
+                         Every result equals the corresponding rows of the
+                         whole-sequence call: estimation only reads the last
+                         64 query rows and the query blocks' own pools. */
 } ms_problem;
 
 /* Pattern and budgets of one Q head (the offline search's output; MInference
@@ -97,7 +110,7 @@ ms_status ms_validate(const ms_problem* prob, const ms_head_params* params);
 /* Sizes (in int32 elements) of the packed selection arrays:
  *   vert  : for each VS head in head order, n_vertical ascending key indices j;
  *   slash : for each VS head in head order, n_slash ascending offsets o = i - j;
- *   blocks: for each BS head in head order, [n/64][top_k_blocks] ascending key
+ *   blocks: for each BS head in head order, [NBq][top_k_blocks] ascending key
  *           block indices per query block, padded with -1 (early query blocks
  *           have fewer than top_k candidates).
  * Heads of other patterns take no space. */
@@ -108,9 +121,9 @@ ms_status ms_selection_sizes(const ms_problem* prob, const ms_head_params* param
 ms_status ms_estimate_workspace_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes);
 
 /* Index arena of ms_build_index: worst-case size, fixed by the parameters (no
- * device round trip).  Per head it holds a CSR over the n/64 query blocks:
- *   rng_ptr[n/64+1] int32, rng[2*R] int32 pairs [lo, hi) of key ranges,
- *   col_ptr[n/64+1] int32, col[C] int32 single key columns.
+ * device round trip).  Per head it holds a CSR over the NBq query blocks:
+ *   rng_ptr[NBq+1] int32, rng[2*R] int32 pairs [lo, hi) of key ranges,
+ *   col_ptr[NBq+1] int32, col[C] int32 single key columns.
  * ms_index_layout() returns, for each Q head h, the byte offsets
  *   offsets[4h+0] rng_ptr, [4h+1] rng, [4h+2] col_ptr, [4h+3] col
  * from the arena base, and the capacities caps[2h+0] = R_max, caps[2h+1] = C_max
@@ -138,6 +151,7 @@ ms_status ms_workspace_bytes(const ms_problem* prob, const ms_head_params* param
  * n_vertical of v and top n_slash of s are written ascending to vert/slash
  * (packed, see ms_selection_sizes); equal scores go to the lower index.
  * dbg_v / dbg_s (nullable, fp32 [H_q][n]) receive the scores of VS heads.
+ * The last 64 rows of q are rows n-64 .. n-1 of the sequence, so m >= 64. 
  * q, k: device bf16.  ws: device, >= ms_estimate_workspace_bytes. */
 ms_status ms_estimate_vs(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
                          int32_t* vert, int32_t* slash, float* dbg_v, float* dbg_s,
@@ -147,7 +161,7 @@ ms_status ms_estimate_vs(const ms_problem* prob, const ms_head_params* params, c
  * "Key points": 64-token mean pooling).  S_bc = mean(q over block b) .
  * mean(k over block c) for c <= b, in fp32; the top min(top_k, b+1) key
  * blocks per query block go to `blocks` ascending, -1 padded.  dbg_scores
- * (nullable, fp32 [H_q][n/64][n/64]) receives S of BS heads, -inf above the
+ * (nullable, fp32 [H_q][NBq][n/64]) receives S of BS heads, -inf above the
  * diagonal. */
 ms_status ms_estimate_block(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
                             int32_t* blocks, float* dbg_scores, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -170,7 +184,7 @@ ms_status ms_build_index(const ms_problem* prob, const ms_head_params* params, c
  * third stage).  Row i of head h attends key j iff j <= i, j lies in a range
  * or column of block i/64, and, for A-shape heads, j < sink or i - j < window.
  * out_i = sum_j softmax_j(scale * q_i.k_j) v_j; a row with no key gives 0.
- * out: bf16 or fp32 per prob->out_dtype.  lse (nullable, fp32 [H_q][n]):
+ * out: bf16 or fp32 per prob->out_dtype.  lse (nullable, fp32 [H_q][m]):
  * natural-log log-sum-exp of the scaled logits, -inf for empty rows.
  * ws: >= ms_attn_workspace_bytes.  Precondition: |v| < 65504 (V is staged as
  * fp16 for the P.V product). */
@@ -191,10 +205,10 @@ ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, co
 /* Index-quality instrument (MInference 1.0 summary, "Key points": the share
  * of the attention mass that the kept entries capture).  With lse_sparse from
  * ms_sparse_attn / ms_sparse_attn_indexed and lse_dense from ms_dense_attn on
- * the same q, k and scale (device fp32 [H_q][n] each), the full causal
+ * the same q, k and scale (device fp32 [H_q][m] each), the full causal
  * attention of row i puts mass exp(lse_sparse_i - lse_dense_i) on the kept
  * keys of that row; recall[h] (device fp32 [H_q]) receives the mean of that
- * mass over the n rows of head h (an empty sparse row counts 0).  The sum is
+ * mass over the m rows of head h (an empty sparse row counts 0).  The sum is
  * taken in float64 in a fixed order (deterministic). */
 ms_status ms_attention_recall(const ms_problem* prob, const float* lse_sparse, const float* lse_dense,
                               float* recall, hipStream_t stream);

@@ -85,17 +85,21 @@ def bs_pool(x: np.ndarray) -> np.ndarray:
     return x.reshape(n // BM, BM, d).mean(axis=1)
 
 
-def bs_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
-    """S[b, c] = mean(q over block b) . mean(k over block c) for c <= b; -inf above."""
+def bs_scores(q: np.ndarray, k: np.ndarray, q_block0: int = 0) -> np.ndarray:
+    """S[b, c] = mean(q over block b) . mean(k over block c) for c <= b; -inf above.
+
+    q holds the query rows from block q_block0 on (chunked prefill, reading
+    R15); row r of the result is query block q_block0 + r."""
     qh, kh = bs_pool(q), bs_pool(k)
     s = qh @ kh.T
-    nb = s.shape[0]
-    return np.where(np.tril(np.ones((nb, nb), dtype=bool)), s, -np.inf)
+    b = q_block0 + np.arange(s.shape[0])[:, None]
+    c = np.arange(s.shape[1])[None, :]
+    return np.where(c <= b, s, -np.inf)
 
 
-def bs_select(scores: np.ndarray, top_k: int) -> List[np.ndarray]:
-    """B_b = top-min(k, b+1) of S[b, 0..b], ascending (R5)."""
-    return [topk(scores[b, : b + 1], top_k) for b in range(scores.shape[0])]
+def bs_select(scores: np.ndarray, top_k: int, q_block0: int = 0) -> List[np.ndarray]:
+    """B_b = top-min(k, b+1) of S[b, 0..b], ascending (R5); row r is block q_block0 + r."""
+    return [topk(scores[r, : q_block0 + r + 1], top_k) for r in range(scores.shape[0])]
 
 
 # --------------------------------------------------------------------------
@@ -294,23 +298,29 @@ def topk_mass(q: np.ndarray, k: np.ndarray, rows: Sequence[int], budget: Sequenc
     return out
 
 
-def estimate_head(params, q: np.ndarray, k: np.ndarray, scale: Optional[float] = None):
-    """Selections of one Q head: ('vs', vert, slash), ('bs', list of B_b) or (pattern,)."""
-    n = q.shape[0]
+def estimate_head(params, q: np.ndarray, k: np.ndarray, scale: Optional[float] = None, q_block0: int = 0):
+    """Selections of one Q head: ('vs', vert, slash), ('bs', list of B_b) or (pattern,).
+
+    q holds the query rows from block q_block0 on, the last of them the last
+    row of the sequence (chunked prefill, reading R15): Vertical-Slash scores
+    its last L rows against every key, Block-Sparse selects for its blocks."""
+    m = q.shape[0]
     if params.pattern == VERTICAL_SLASH:
-        L = min(params.last_q, n)
-        v_sc, s_sc = vs_scores(q[n - L:], k, scale)
+        L = min(params.last_q, m)
+        v_sc, s_sc = vs_scores(q[m - L:], k, scale)
         return "vs", topk(v_sc, params.n_vertical), topk(s_sc, params.n_slash)
     if params.pattern == BLOCK_SPARSE:
-        return "bs", bs_select(bs_scores(q, k), params.top_k_blocks)
+        return "bs", bs_select(bs_scores(q, k, q_block0), params.top_k_blocks, q_block0)
     return ("static",)
 
 
-def head_index(params, sel, n: int) -> List[BlockIndex]:
+def head_index(params, sel, n: int, q_block0: int = 0) -> List[BlockIndex]:
+    """Index of query blocks q_block0 .. n/64 - 1 (entry r is block q_block0 + r)."""
+    blocks = range(q_block0, n // BM)
     if params.pattern == VERTICAL_SLASH:
-        return vs_index(sel[1], sel[2], n)
+        return [vs_block_index(sel[1], sel[2], b) for b in blocks]
     if params.pattern == BLOCK_SPARSE:
         return bs_index(sel[1])
     if params.pattern == A_SHAPE:
-        return ashape_index(params.sink, params.window, n)
-    return dense_index(n)
+        return [ashape_block_index(params.sink, params.window, b) for b in blocks]
+    return [dense_block_index(b) for b in blocks]

@@ -68,9 +68,9 @@ def test_problem_validation():
     _expect(1, ms.ms_validate, ms.problem(1024, 3, 2), ms.head_params([W.dense()] * 3))
     _expect(1, ms.ms_validate, ms.problem(1024, 1, 1, scale=-1.0), hp)
     _expect(1, ms.ms_validate, ms.problem(1024, 1, 1, out_dtype=7), hp)
-    p = ms.problem(1024, 1, 1)
-    p.reserved = 1
-    _expect(1, ms.ms_validate, p, hp)
+    _expect(1, ms.ms_validate, ms.problem(1024, 1, 1, q_block0=-1), hp)
+    _expect(1, ms.ms_validate, ms.problem(1024, 1, 1, q_block0=16), hp)   # no query block left
+    ms.ms_validate(ms.problem(1024, 1, 1, q_block0=15), hp)                 # the last block alone
     _expect(1, ms.ms_validate, ms.problem(1024, 129, 1), ms.head_params([W.dense()] * 129))
 
 
@@ -179,3 +179,17 @@ def test_calls_reject_bad_arguments_before_launch():
                                    ctypes.c_void_p(1 << 20), None) == 1
     assert lib.ms_topk_f32(ctypes.c_void_p(1 << 20), 10, -1, ctypes.c_void_p(1 << 20), None) == 1
     assert b"negative" in lib.ms_last_error()
+
+
+def test_chunk_sizes_follow_the_query_blocks():
+    """With q_block0 = 15 of 20 blocks, Block-Sparse selections, index and
+    estimation workspace cover 5 query blocks; Vertical-Slash sizes do not
+    depend on the chunk."""
+    hp = ms.head_params([W.bs(4), W.vs(3, 5)])
+    full, part = ms.problem(64 * 20, 2, 1), ms.problem(64 * 20, 2, 1, q_block0=15)
+    assert ms.ms_selection_sizes(full, hp) == (3, 5, 20 * 4)
+    assert ms.ms_selection_sizes(part, hp) == (3, 5, 5 * 4)
+    assert ms.ms_index_bytes(part, hp) < ms.ms_index_bytes(full, hp)
+    assert ms.ms_estimate_workspace_bytes(part, hp) < ms.ms_estimate_workspace_bytes(full, hp)
+    offs, caps = ms.ms_index_layout(part, hp)
+    assert caps[0][0] == sum(min(4, b + 1, b // 2 + 1) for b in range(15, 20))

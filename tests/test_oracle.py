@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+import workloads as W
 from oracle.core import BM
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -401,3 +402,51 @@ def test_topk_mass_exhaustive_and_bounds_any_index():
     rows = list(range(0, n, 5))
     best = oracle.topk_mass(q, k, rows, budget[rows])
     assert np.all(m[rows] <= best + 1e-12)
+
+
+# ------------------------------------------------------------ chunked prefill
+@pytest.mark.parametrize("q_block0", [1, 7, 11])
+def test_chunk_estimation_and_index_restrict_the_whole_sequence(q_block0):
+    """A chunk of query blocks q_block0.. (with every key present) estimates
+    and indexes exactly as the whole sequence does for those blocks: the
+    Vertical-Slash selections are equal (same last 64 rows), the Block-Sparse
+    selections and every block's index are the whole sequence's from block
+    q_block0 on, and so is attention."""
+    rng = np.random.default_rng(40 + q_block0)
+    n, d = 64 * 12, 128
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    k[200] += 2.0 * q[-64:].mean(axis=0)  # one strong vertical
+    qc = q[q_block0 * BM:]
+    for params in (W.vs(8, 12), W.bs(3), W.ashape(20, 70), W.dense()):
+        full = oracle.estimate_head(params, q, k)
+        chunk = oracle.estimate_head(params, qc, k, q_block0=q_block0)
+        if params.pattern == W.VERTICAL_SLASH:
+            np.testing.assert_array_equal(chunk[1], full[1])
+            np.testing.assert_array_equal(chunk[2], full[2])
+        elif params.pattern == W.BLOCK_SPARSE:
+            assert len(chunk[1]) == n // BM - q_block0
+            for r, sel in enumerate(chunk[1]):
+                np.testing.assert_array_equal(sel, full[1][q_block0 + r])
+        idx_full = oracle.head_index(params, full, n)
+        idx_chunk = oracle.head_index(params, chunk, n, q_block0=q_block0)
+        assert len(idx_chunk) == n // BM - q_block0
+        ashape = (params.sink, params.window) if params.pattern == W.A_SHAPE else None
+        for r, bidx in enumerate(idx_chunk):
+            b = q_block0 + r
+            np.testing.assert_array_equal(bidx[0], idx_full[b][0])
+            np.testing.assert_array_equal(bidx[1], idx_full[b][1])
+            o1, l1 = oracle.attention_block(qc[r * BM:(r + 1) * BM], k, v, bidx, b, ashape=ashape)
+            o2, l2 = oracle.attention_block(q[b * BM:(b + 1) * BM], k, v, idx_full[b], b, ashape=ashape)
+            np.testing.assert_array_equal(o1, o2)
+            np.testing.assert_array_equal(l1, l2)
+
+
+def test_chunk_block_scores_are_rows_of_the_full_matrix():
+    rng = np.random.default_rng(3)
+    n, d = 64 * 9, 128
+    q, k = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    full = oracle.bs_scores(q, k)
+    part = oracle.bs_scores(q[4 * BM:], k, q_block0=4)
+    assert part.shape == (5, 9)
+    np.testing.assert_array_equal(part, full[4:])
+    assert np.isneginf(part[0, 5:]).all() and np.isfinite(part[0, :5]).all()
