@@ -24,10 +24,10 @@ __all__ = [
     "ms_index_layout", "ms_attn_workspace_bytes", "ms_workspace_bytes", "ms_estimate_vs",
     "ms_estimate_block", "ms_build_index", "ms_sparse_attn_indexed", "ms_sparse_attn",
     "ms_dense_attn", "ms_topk_f32", "ms_version", "read_index", "empty_workspace",
-    "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "DENSE", "OUT_BF16", "OUT_F32",
+    "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "DENSE", "GRID", "OUT_BF16", "OUT_F32",
 ]
 
-A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, DENSE = 0, 1, 2, 3
+A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, DENSE, GRID = 0, 1, 2, 3, 4
 OUT_BF16, OUT_F32 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "insufficient capacity", 4: "device error"}
 
@@ -48,7 +48,8 @@ class Problem(ctypes.Structure):
 class HeadParams(ctypes.Structure):
     _fields_ = [("pattern", ctypes.c_int32), ("last_q", ctypes.c_int32), ("n_vertical", ctypes.c_int32),
                 ("n_slash", ctypes.c_int32), ("block", ctypes.c_int32), ("top_k_blocks", ctypes.c_int32),
-                ("sink", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("sink", ctypes.c_int32), ("window", ctypes.c_int32), ("grid_stride", ctypes.c_int32),
+                ("grid_frames", ctypes.c_int32), ("grid_width", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -117,7 +118,8 @@ def head_params(heads: Sequence) -> ctypes.Array:
         arr[i] = HeadParams(int(h.pattern), int(getattr(h, "last_q", 64)), int(getattr(h, "n_vertical", 0)),
                             int(getattr(h, "n_slash", 0)), int(getattr(h, "block", 64)),
                             int(getattr(h, "top_k_blocks", 0)), int(getattr(h, "sink", 0)),
-                            int(getattr(h, "window", 0)))
+                            int(getattr(h, "window", 0)), int(getattr(h, "grid_stride", 0)),
+                            int(getattr(h, "grid_frames", 0)), int(getattr(h, "grid_width", 0)))
     return arr
 
 

@@ -129,6 +129,15 @@ ms_status validate(const ms_problem* prob, const ms_head_params* params, bool ne
         if (q.sink < 0 || q.sink > n) return fail(MS_ERR_INVALID_ARG, "head %d: sink = %d out of 0..n", h, q.sink);
         if (q.window < 1 || q.window > n) return fail(MS_ERR_INVALID_ARG, "head %d: window = %d out of 1..n", h, q.window);
         break;
+      case MS_GRID:
+        if (q.grid_stride < 1 || q.grid_stride > n)
+          return fail(MS_ERR_INVALID_ARG, "head %d: grid_stride = %d out of 1..n", h, q.grid_stride);
+        if (q.grid_frames < 0 || q.grid_frames > n)
+          return fail(MS_ERR_INVALID_ARG, "head %d: grid_frames = %d out of 0..n", h, q.grid_frames);
+        if (q.grid_width < 0 || q.grid_width > n)
+          return fail(MS_ERR_INVALID_ARG, "head %d: grid_width = %d out of 0..n", h, q.grid_width);
+        if (q.window < 1 || q.window > n) return fail(MS_ERR_INVALID_ARG, "head %d: window = %d out of 1..n", h, q.window);
+        break;
       case MS_DENSE:
         break;
       default:
@@ -155,6 +164,9 @@ std::pair<int64_t, int64_t> head_caps(const ms_head_params& q, int64_t qb0, int6
       case MS_A_SHAPE:
         r += 2;
         break;
+      case MS_GRID:  // at most one range per frame group that reaches the block, plus the local one
+        r += std::min<int64_t>(q.grid_frames, (last + q.grid_width) / q.grid_stride) + 1;
+        break;
       default:
         r += 1;
     }
@@ -179,6 +191,9 @@ double expected_density(const ms_head_params& q, int64_t n) {
     }
     case MS_A_SHAPE:
       return std::min(1.0, ((double)q.sink + (double)q.window) / (0.5 * nd));
+    case MS_GRID:  // a 64-row block keeps window + 63 local keys and 2w + 64 per frame
+      return std::min(1.0, ((double)q.window + 63.0 + (double)q.grid_frames * (2.0 * q.grid_width + 64.0)) /
+                               (0.5 * nd));
     default:
       return 1.0;
   }
@@ -252,12 +267,14 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.cap_r.assign(P.hq, 0);
   P.cap_c.assign(P.hq, 0);
   P.desc.assign(P.hq, HeadDesc{});
-  std::map<std::tuple<int, int, int>, std::pair<int64_t, int64_t>> memo;
+  std::map<std::tuple<int, int, int, int, int, int>, std::pair<int64_t, int64_t>> memo;
   for (int h = 0; h < P.hq; ++h) {
     const ms_head_params& q = P.p[h];
     const int a = q.pattern == MS_VERTICAL_SLASH ? q.n_vertical : q.pattern == MS_BLOCK_SPARSE ? q.top_k_blocks : 0;
     const int b = q.pattern == MS_VERTICAL_SLASH ? q.n_slash : 0;
-    const auto key = std::make_tuple(q.pattern, a, b);
+    const bool gr = q.pattern == MS_GRID;
+    const auto key = std::make_tuple(q.pattern, a, b, gr ? q.grid_stride : 0, gr ? q.grid_frames : 0,
+                                     gr ? q.grid_width : 0);
     auto it = memo.find(key);
     if (it == memo.end()) it = memo.emplace(key, head_caps(q, P.qb0, P.nb)).first;
     P.cap_r[h] = it->second.first;
@@ -276,6 +293,11 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     } else if (q.pattern == MS_A_SHAPE) {
       d.p0 = q.sink;
       d.p1 = q.window;
+    } else if (q.pattern == MS_GRID) {
+      d.p0 = q.grid_stride;
+      d.p1 = q.window;
+      d.p2 = q.grid_frames;
+      d.p3 = q.grid_width;
     }
     d.vert_off = P.vert_off[h];
     d.slash_off = P.slash_off[h];

@@ -64,6 +64,7 @@ __device__ __forceinline__ int cap_ranges(const HeadDesc& d, int b) {
     case MS_VERTICAL_SLASH: return min(d.p1, last / 65 + 1);
     case MS_BLOCK_SPARSE: return min(min(d.p0, b + 1), b / 2 + 1);
     case MS_A_SHAPE: return 2;
+    case MS_GRID: return min(d.p2, (last + d.p3) / d.p0) + 1;
     default: return 1;
   }
 }
@@ -199,6 +200,40 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
     } else {
       nr = 1;
       if (kFill && tid == 0 && rlim >= 1) rng[rbase] = make_int2(sink > 0 ? 0 : wlo, end);
+    }
+  } else if (d.pattern == MS_GRID) {
+    // Offsets (o = i - j) kept: 0 .. window-1 and tP-w .. tP+w for t = 1..T,
+    // only those <= last reaching this block.  The intervals are merged in
+    // ascending order of their first offset: two offsets at most 64 apart
+    // give key spans that touch, so intervals closer than that form one run,
+    // and a run [ra, rb] of offsets keeps keys [max(0, row0 - rb), row0 + 64
+    // - ra).  Larger offsets give lower keys, so run r goes to slot nr-1-r.
+    // One thread.
+    const int P = d.p0, W = d.p1, T = d.p2, wd = d.p3;
+    if (tid == 0) {
+      int cnt = 0, ra = -1, rb = -1;
+      auto emit = [&]() {
+        const int pos = rlim - 1 - cnt;
+        if (kFill && pos >= 0) rng[rbase + pos] = make_int2(max(0, row0 - rb), end - ra);
+        ++cnt;
+      };
+      auto add = [&](int oa, int ob) {  // called in ascending oa
+        oa = max(oa, 0);
+        ob = min(ob, last);
+        if (oa > ob) return;
+        if (ra >= 0 && oa - rb <= kBM) {
+          rb = max(rb, ob);
+        } else {
+          if (ra >= 0) emit();
+          ra = oa;
+          rb = ob;
+        }
+      };
+      add(0, W - 1);
+      const int tmax = min(T, (last + wd) / P);
+      for (int t = 1; t <= tmax; ++t) add(t * P - wd, t * P + wd);
+      if (ra >= 0) emit();
+      nr = min(cnt, rcap);
     }
   } else {  // dense
     nr = 1;

@@ -28,10 +28,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // kernel from kernel arguments, read by the index builders and attention).
 struct HeadDesc {
   int32_t pattern;
-  int32_t p0, p1;    // VS: n_vertical, n_slash.  BS: top_k, -.  A: sink, window
+  int32_t p0, p1;    // VS: n_vertical, n_slash.  BS: top_k, -.  A: sink, window.  GRID: stride, window
   int32_t vs_slot;   // rank among VS heads (-1 if not VS)
   int32_t bs_slot;   // rank among BS heads (-1 if not BS)
-  int32_t pad0, pad1, pad2;
+  int32_t p2, p3;    // GRID: frames, width
+  int32_t pad0;
   int64_t vert_off;  // int32 elements into the packed vert array (VS)
   int64_t slash_off; // into the packed slash array (VS)
   int64_t blk_off;   // into the packed blocks array (BS)

@@ -57,8 +57,9 @@ typedef enum {
 } ms_status;
 
 /* Per-head sparse pattern (MInference abstract: the three shapes; DENSE is the
- * full causal baseline). */
-typedef enum { MS_A_SHAPE = 0, MS_VERTICAL_SLASH = 1, MS_BLOCK_SPARSE = 2, MS_DENSE = 3 } ms_pattern;
+ * full causal baseline; GRID is the video pattern the MMInference abstract
+ * names: keys at the same spatial position in earlier frames). */
+typedef enum { MS_A_SHAPE = 0, MS_VERTICAL_SLASH = 1, MS_BLOCK_SPARSE = 2, MS_DENSE = 3, MS_GRID = 4 } ms_pattern;
 
 typedef enum { MS_OUT_BF16 = 0, MS_OUT_F32 = 1 } ms_out_dtype;
 
@@ -94,7 +95,10 @@ typedef struct {
   int32_t block;        /* BS: pooling block; must be 64 */
   int32_t top_k_blocks; /* BS: key blocks kept per query block, 1..n/64 */
   int32_t sink;         /* A-shape: initial keys kept, 0..n */
-  int32_t window;       /* A-shape: local causal window in keys, 1..n */
+  int32_t window;       /* A-shape: local causal window in keys, 1..n; GRID: local offsets 0..window-1, 1..n */
+  int32_t grid_stride;  /* GRID: tokens per frame P, 1..n */
+  int32_t grid_frames;  /* GRID: earlier frames T kept at the same position, 0..n */
+  int32_t grid_width;   /* GRID: half-width w of the kept neighbourhood, 0..n */
 } ms_head_params;
 
 /* `params` below always points to n_q_heads entries. */
@@ -173,6 +177,10 @@ ms_status ms_estimate_block(const ms_problem* prob, const ms_head_params* params
  *       range become columns.
  *   BS: selected key blocks c give [64c, 64c+64), consecutive ones merged.
  *   A-shape: [0, min(sink, 64b+64)) and [max(0, 64b-window+1), 64b+64), merged.
+ *   GRID: as VS with no verticals and the fixed offsets 0 .. window-1 and
+ *       tP-w .. tP+w for t = 1..T (those >= 0): the same keys of the same
+ *       spatial neighbourhood in each of the T previous frames, plus the
+ *       local window.
  *   DENSE: [0, 64b+64).
  * vert/slash/blocks: device arrays as written by the estimators (may be null
  * when no head needs them).  index: device arena of >= ms_index_bytes. */

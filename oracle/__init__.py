@@ -34,6 +34,11 @@ function (readings R1..R13 of the design notes):
       spans that overlap or touch are merged; columns outside every span are
       listed separately.  The mask is that union intersected with causality.
   R8  A row with no key gives out = 0 and lse = -inf.
+  R15 Chunked prefill: the results of query blocks q_block0.. are the
+      whole-sequence results of those blocks.
+  R16 Grid heads keep fixed offsets: 0 .. window-1 and tP-w .. tP+w for the
+      T previous frames of P tokens; their index is the Vertical-Slash
+      conversion of that slash set.
 
 Every array is numpy float64 (scores, attention) or int64/int32 (indices).
 Inputs arrive as bfloat16 values widened exactly to float64 by the caller.
@@ -57,6 +62,8 @@ from .core import (  # noqa: F401
     bs_index,
     ashape_block_index,
     ashape_index,
+    grid_offsets,
+    grid_block_index,
     dense_block_index,
     dense_index,
     index_to_csr,

@@ -21,7 +21,7 @@ import numpy as np
 BM = 64  # query rows per block, and the pooling block of Block-Sparse heads ([P2] "Key points")
 
 # Pattern codes of the per-head parameters (the offline search's output, [P2] "Summary").
-A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, DENSE = 0, 1, 2, 3
+A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, DENSE, GRID = 0, 1, 2, 3, 4
 
 BlockIndex = Tuple[np.ndarray, np.ndarray]
 
@@ -161,6 +161,30 @@ def ashape_block_index(sink: int, window: int, b: int) -> BlockIndex:
 
 def ashape_index(sink: int, window: int, n: int) -> List[BlockIndex]:
     return [ashape_block_index(sink, window, b) for b in range(n // BM)]
+
+
+# --------------------------------------------------------------------------
+# Grid pattern (the MMInference abstract: video tokens attend along a grid,
+# from the temporal and spatial locality of frames).  Reading R16: with P
+# tokens per frame, a query keeps the keys of its own spatial neighbourhood
+# (half-width w) in each of the T previous frames, offsets o = i - j in
+# tP - w .. tP + w, plus the local offsets 0 .. window - 1; the index of a
+# 64-row query block is the Vertical-Slash conversion (R7) of that fixed
+# slash set with no verticals.
+# --------------------------------------------------------------------------
+def grid_offsets(stride: int, frames: int, width: int, window: int, n: int) -> np.ndarray:
+    """The kept offsets, ascending and distinct, within [0, n)."""
+    o = set(range(min(window, n)))
+    for t in range(1, frames + 1):
+        for delta in range(-width, width + 1):
+            x = t * stride + delta
+            if 0 <= x < n:
+                o.add(x)
+    return np.asarray(sorted(o), dtype=np.int64)
+
+
+def grid_block_index(stride: int, frames: int, width: int, window: int, b: int, n: int) -> BlockIndex:
+    return vs_block_index(np.zeros(0, dtype=np.int64), grid_offsets(stride, frames, width, window, n), b)
 
 
 def dense_block_index(b: int) -> BlockIndex:
@@ -323,4 +347,7 @@ def head_index(params, sel, n: int, q_block0: int = 0) -> List[BlockIndex]:
         return bs_index(sel[1])
     if params.pattern == A_SHAPE:
         return [ashape_block_index(params.sink, params.window, b) for b in blocks]
+    if params.pattern == GRID:
+        offs = grid_offsets(params.grid_stride, params.grid_frames, params.grid_width, params.window, n)
+        return [vs_block_index(np.zeros(0, dtype=np.int64), offs, b) for b in blocks]
     return [dense_block_index(b) for b in blocks]

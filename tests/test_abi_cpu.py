@@ -8,6 +8,7 @@ import re
 import pytest
 
 import dynamic_sparse_attention_est_amd as ms
+import oracle
 import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -84,6 +85,11 @@ def test_problem_validation():
     (W.bs(17), 1),
     (W.ashape(-1, 10), 1),
     (W.ashape(4, 0), 1),
+    (W.grid(0, 2, 1, 8), 1),
+    (W.grid(100, -1, 1, 8), 1),
+    (W.grid(100, 2, -1, 8), 1),
+    (W.grid(100, 2, 1, 0), 1),
+    (W.grid(2000, 2, 1, 8), 1),
 ])
 def test_head_validation(head, status):
     _expect(status, ms.ms_validate, ms.problem(1024, 1, 1), ms.head_params([head]))
@@ -103,9 +109,23 @@ def _cap_bound(h, nb):
             r += min(cnt, b // 2 + 1)  # runs of blocks are separated by >= 1 gap
         elif h.pattern == W.A_SHAPE:
             r += 2
+        elif h.pattern == W.GRID:
+            # one run per frame group reaching the block, plus the local one
+            r += min(h.grid_frames, (last + h.grid_width) // h.grid_stride) + 1
         else:
             r += 1
     return r, c
+
+
+def test_grid_capacity_bounds_the_oracle_runs():
+    """The per-block range capacity of Grid heads is never below the runs the
+    oracle's index holds (strides below, at and above 64 + 2w)."""
+    n = 64 * 40
+    for P, T, w, W_ in [(10, 50, 2, 5), (70, 30, 3, 1), (66, 40, 1, 3), (500, 4, 30, 700), (1, 3, 0, 1)]:
+        hp = W.grid(P, T, w, W_)
+        _, caps = ms.ms_index_layout(ms.problem(n, 1, 1), ms.head_params([hp]))
+        runs = sum(oracle.grid_block_index(P, T, w, W_, b, n)[0].shape[0] for b in range(n // 64))
+        assert caps[0][0] == _cap_bound(hp, n // 64)[0] >= runs
 
 
 def test_index_layout_capacities_and_alignment():

@@ -171,3 +171,21 @@ def test_chunk_of_a_long_sequence_by_key_segments():
     part = _run(ms.problem(n, 8, 2, q_block0=q_block0), hp, heads, qc, k, v)
     assert torch.equal(part["out"].view(torch.int16), full_out.view(torch.int16))
     assert torch.equal(part["lse"], full_lse)
+
+
+def test_batch_by_stacking_heads():
+    """Two sequences of one length stacked along the head axis (their Q heads,
+    then their KV heads) give, head for head, the results of two separate
+    calls."""
+    n = 64 * 21
+    heads = [W.vs(30, 50), W.bs(5), W.ashape(30, 100), W.dense()]
+    seqs = [W.generate(W.custom(f"batch{i}", n, 4, 2, heads, recipe="vs_planted", seed=70 + i), device="cuda")
+            for i in range(2)]
+    sep = [_run(ms.problem(n, 4, 2), ms.head_params(heads), heads, *s) for s in seqs]
+    q = torch.cat([s[0] for s in seqs]).contiguous()
+    k = torch.cat([s[1] for s in seqs]).contiguous()
+    v = torch.cat([s[2] for s in seqs]).contiguous()
+    both = _run(ms.problem(n, 8, 4), ms.head_params(heads * 2), heads * 2, q, k, v)
+    for i in range(2):
+        assert torch.equal(both["out"][4 * i:4 * i + 4].view(torch.int16), sep[i]["out"].view(torch.int16))
+        assert torch.equal(both["lse"][4 * i:4 * i + 4], sep[i]["lse"])

@@ -394,3 +394,38 @@ def test_attention_recall_instrument():
         # is within about 2 LSE_ATOL relative
         assert abs(got[h] - ref) <= 2.5 * LSE_ATOL, f"head {h}: recall {got[h]:.6f} vs {ref:.6f}"
     assert abs(got[3] - 1.0) <= 2.5 * LSE_ATOL  # the dense head keeps all of its mass
+
+
+# ------------------------------------------------------------ Grid pattern
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_grid_heads_index_and_attention(hkv):
+    """Grid heads (reading R16) with strides below, at and above 64 + 2w,
+    frame groups reaching before key 0 and a local window wider than early
+    prefixes, beside a Vertical-Slash head: every block's CSR equals the
+    oracle's and attention meets the bar on every block.  With one KV head
+    the dense-enough Grid heads are served together over their union."""
+    n = 64 * 37
+    heads = [W.grid(7, 30, 1, 4), W.grid(100, 5, 3, 50), W.grid(64, 3, 0, 1), W.grid(300, 6, 20, 600),
+             W.grid(1, 2, 0, 1), W.vs(20, 40), W.grid(130, 20, 40, 90), W.grid(2000, 1, 10, 64)]
+    w = W.custom("grid_mix", n, len(heads), hkv, heads, recipe="grid_video", n_planted=100, seed=81)
+    _attention_check(run_staged(make(w), debug=False))
+
+
+def test_grid_keeps_more_attention_mass_on_video_like_inputs():
+    """On frame-major inputs whose tokens lean toward their own spatial
+    position in every frame (recipe grid_video, 1000 tokens per frame), a Grid
+    head keeps more of the attention mass than an A-shape head with at least
+    as many keys per row."""
+    n, P = 64 * 256, 1000
+    heads = [W.grid(P, 16, 8, 128), W.ashape(128, 16 * 17 + 128 + 64)]
+    w = W.custom("video", n, 2, 1, heads, recipe="grid_video", n_planted=P, seed=82)
+    st = run_staged(make(w), debug=False)
+    prob = st.prob
+    lse_d = torch.empty_like(st.lse)
+    ms.ms_dense_attn(prob, st.q, st.k, st.v, torch.empty_like(st.out),
+                     ms.empty_workspace(ms.ms_attn_workspace_bytes(prob)), lse_d)
+    rec = torch.empty(2, dtype=torch.float32, device="cuda")
+    ms.ms_attention_recall(prob, st.lse, lse_d, rec)
+    r = rec.cpu().numpy()
+    print(f"  recall grid {r[0]:.4f}  a-shape {r[1]:.4f}", flush=True)
+    assert r[0] > r[1] + 0.05

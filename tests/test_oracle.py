@@ -450,3 +450,42 @@ def test_chunk_block_scores_are_rows_of_the_full_matrix():
     assert part.shape == (5, 9)
     np.testing.assert_array_equal(part, full[4:])
     assert np.isneginf(part[0, 5:]).all() and np.isfinite(part[0, :5]).all()
+
+
+# ------------------------------------------------------------ Grid pattern
+def test_grid_index_hand_worked():
+    """Reading R16 worked by hand.  P = 100, T = 2, w = 2, window = 10:
+    offsets {0..9} u {98..102} u {198..202}.  Block 3 (rows 192..255): the
+    local run gives keys [192-9, 256) = [183, 256); 98..102 (gap 89 > 64 from
+    9) gives [192-102, 256-98) = [90, 158); 198..202 (gap 96) gives
+    [max(0, -10), 58) = [0, 58).  Block 1 (rows 64..127): [0, 30) and
+    [55, 128); 198 > 127 reaches nothing.  P = 50, w = 10, window = 20,
+    T = 2: offsets 0..19, 40..60, 90..110 lie within 64 of each other, one run
+    0..110: block 2 (rows 128..191) keeps [128-110, 192) = [18, 192)."""
+    n = 64 * 8
+    r, c = oracle.grid_block_index(100, 2, 2, 10, 3, n)
+    np.testing.assert_array_equal(r, [[0, 58], [90, 158], [183, 256]])
+    assert c.size == 0
+    r, _ = oracle.grid_block_index(100, 2, 2, 10, 1, n)
+    np.testing.assert_array_equal(r, [[0, 30], [55, 128]])
+    r, _ = oracle.grid_block_index(50, 2, 10, 20, 2, n)
+    np.testing.assert_array_equal(r, [[18, 192]])
+    np.testing.assert_array_equal(oracle.grid_offsets(100, 2, 2, 10, n),
+                                  list(range(10)) + list(range(98, 103)) + list(range(198, 203)))
+
+
+@pytest.mark.parametrize("params", [(7, 3, 1, 4), (100, 5, 3, 50), (64, 2, 0, 1), (30, 9, 20, 200), (1, 1, 0, 1)])
+def test_grid_mask_elementwise(params):
+    """Brute force on a small sequence: row i of block b keeps key j iff j <= i
+    and some kept offset o has j in the block's span [64b - o, 64b + 63 - o]."""
+    P, T, w, W = params
+    n = 64 * 6
+    offs = set(range(min(W, n))) | {t * P + d for t in range(1, T + 1) for d in range(-w, w + 1) if 0 <= t * P + d < n}
+    for b in range(n // 64):
+        got = oracle.block_mask(oracle.grid_block_index(P, T, w, W, b, n), b, n)
+        ref = np.zeros((64, n), dtype=bool)
+        for r in range(64):
+            i = 64 * b + r
+            for j in range(i + 1):
+                ref[r, j] = any(64 * b - o <= j <= 64 * b + 63 - o for o in offs)
+        np.testing.assert_array_equal(got, ref)

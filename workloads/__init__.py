@@ -34,9 +34,10 @@ A_SHAPE = 0
 VERTICAL_SLASH = 1
 BLOCK_SPARSE = 2
 DENSE = 3
+GRID = 4
 
 PATTERN_NAMES = {A_SHAPE: "a_shape", VERTICAL_SLASH: "vertical_slash",
-                 BLOCK_SPARSE: "block_sparse", DENSE: "dense"}
+                 BLOCK_SPARSE: "block_sparse", DENSE: "dense", GRID: "grid"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -50,6 +51,9 @@ class HeadParams:
     top_k_blocks: int = 0
     sink: int = 0
     window: int = 0
+    grid_stride: int = 0
+    grid_frames: int = 0
+    grid_width: int = 0
 
 
 def vs(n_vertical: int, n_slash: int, last_q: int = 64) -> HeadParams:
@@ -66,6 +70,10 @@ def ashape(sink: int, window: int) -> HeadParams:
 
 def dense() -> HeadParams:
     return HeadParams(DENSE)
+
+
+def grid(stride: int, frames: int, width: int, window: int) -> HeadParams:
+    return HeadParams(GRID, window=window, grid_stride=stride, grid_frames=frames, grid_width=width)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,7 +160,7 @@ def _gen(w: Workload, tensor_id: int, head: int, device) -> torch.Generator:
     return g
 
 
-_Q, _K, _V, _PLANT, _LOWRANK_U, _LOWRANK_W, _LOWRANK_BLK = range(7)
+_Q, _K, _V, _PLANT, _LOWRANK_U, _LOWRANK_W, _LOWRANK_BLK, _GRID_U = range(8)
 
 
 def _randn(w: Workload, tensor_id: int, head: int, shape, device) -> torch.Tensor:
@@ -175,6 +183,12 @@ def generate(w: Workload, device="cpu"):
                   += 2 * U w.
       ashape_sink q, k, v ~ N(0, 1).  u = mean(q) / |mean(q)| per head; the
                   first 128 keys get k_j += 2 (k_j . u) u, i.e. x3 along u.
+      grid_video  video-like tokens, frames of P = n_planted tokens: q, k, v ~
+                  N(0, s^2); per KV head a table U [P, 128] ~ N(0, 1) (one
+                  vector per spatial position); the group's queries and the
+                  keys at position i get += 0.7 U[i mod P], so a query leans
+                  toward the keys at its own spatial position in every frame
+                  (about +5.5 on the scaled logit).
     """
     n, d = w.n, HEAD_DIM
     hq, hkv, grp = w.n_q_heads, w.n_kv_heads, w.group
@@ -229,6 +243,16 @@ def generate(w: Workload, device="cpu"):
             kf[:ns] += 2.0 * proj[:, None] * u[None, :]
             q[h] = qf.to(torch.bfloat16)
             k[h] = kf.to(torch.bfloat16)
+    elif w.recipe == "grid_video":
+        P = w.n_planted
+        assert P >= 1, "grid_video needs the frame size in n_planted"
+        pos = torch.arange(n, device=device) % P
+        for kv in range(hkv):
+            u = _randn(w, _GRID_U, kv, (P, d), device)[pos] * 0.7
+            for h in range(kv * grp, (kv + 1) * grp):
+                q[h] = (_randn(w, _Q, h, (n, d), device) * s + u).to(torch.bfloat16)
+            k[kv] = (_randn(w, _K, kv, (n, d), device) * s + u).to(torch.bfloat16)
+            del u
     else:
         raise ValueError(w.recipe)
     return q, k, v
