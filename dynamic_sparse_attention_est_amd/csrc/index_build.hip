@@ -202,39 +202,48 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
       if (kFill && tid == 0 && rlim >= 1) rng[rbase] = make_int2(sink > 0 ? 0 : wlo, end);
     }
   } else if (d.pattern == MS_GRID) {
-    // Offsets (o = i - j) kept: 0 .. window-1 and tP-w .. tP+w for t = 1..T,
-    // only those <= last reaching this block.  The intervals are merged in
-    // ascending order of their first offset: two offsets at most 64 apart
-    // give key spans that touch, so intervals closer than that form one run,
-    // and a run [ra, rb] of offsets keeps keys [max(0, row0 - rb), row0 + 64
-    // - ra).  Larger offsets give lower keys, so run r goes to slot nr-1-r.
-    // One thread.
+    // Offsets (o = i - j) kept: the local interval 0 .. window-1 and frame
+    // group t = tP-w .. tP+w for t = 1..T, cut to <= last (groups with tP-w >
+    // last do not reach the block: t <= tmax).  Offsets at most 64 apart give
+    // key spans that touch, so intervals that close form one run, and a run
+    // [ra, rb] of offsets keeps keys [max(0, row0 - rb), row0 + 64 - ra).
+    //   P - 2w <= 64: consecutive groups touch; groups 1..tmax are one run,
+    //     merged with the local one when it starts within 64 of it.
+    //   P - 2w > 64: groups never touch each other; group t joins the local
+    //     run iff tP - w <= window + 63 (t <= t1), the others are runs alone.
+    // Ranges ascending in key order = runs in descending offset order.
     const int P = d.p0, W = d.p1, T = d.p2, wd = d.p3;
-    if (tid == 0) {
-      int cnt = 0, ra = -1, rb = -1;
-      auto emit = [&]() {
-        const int pos = rlim - 1 - cnt;
-        if (kFill && pos >= 0) rng[rbase + pos] = make_int2(max(0, row0 - rb), end - ra);
-        ++cnt;
-      };
-      auto add = [&](int oa, int ob) {  // called in ascending oa
-        oa = max(oa, 0);
-        ob = min(ob, last);
-        if (oa > ob) return;
-        if (ra >= 0 && oa - rb <= kBM) {
-          rb = max(rb, ob);
-        } else {
-          if (ra >= 0) emit();
-          ra = oa;
-          rb = ob;
+    const int tmax = min(T, (last + wd) / P);
+    const int lob = min(W - 1, last);  // local interval [0, lob]
+    if (P - 2 * wd <= kBM) {
+      const bool grp = tmax >= 1;
+      const int goa = max(0, P - wd), gob = min(last, tmax * P + wd);
+      const bool merged = grp && goa - lob <= kBM;
+      nr = grp && !merged ? 2 : 1;
+      if (kFill && tid == 0) {
+        if (!grp || merged) {
+          if (rlim >= 1) rng[rbase] = make_int2(max(0, row0 - (grp ? max(lob, gob) : lob)), end);
+        } else if (rlim >= 2) {
+          rng[rbase] = make_int2(max(0, row0 - gob), end - goa);
+          rng[rbase + 1] = make_int2(max(0, row0 - lob), end);
         }
-      };
-      add(0, W - 1);
-      const int tmax = min(T, (last + wd) / P);
-      for (int t = 1; t <= tmax; ++t) add(t * P - wd, t * P + wd);
-      if (ra >= 0) emit();
-      nr = min(cnt, rcap);
+      }
+    } else {
+      const int t1 = min(tmax, (W + 63 + wd) / P);
+      const int alone = tmax - t1;  // groups t1+1 .. tmax, one run each
+      nr = alone + 1;
+      if (kFill) {
+        for (int u = tid; u < alone && u < rlim; u += kT) {
+          const int t = tmax - u;
+          rng[rbase + u] = make_int2(max(0, row0 - min(last, t * P + wd)), end - (t * P - wd));
+        }
+        if (tid == 0 && alone < rlim) {
+          const int rb = t1 >= 1 ? max(lob, min(last, t1 * P + wd)) : lob;
+          rng[rbase + alone] = make_int2(max(0, row0 - rb), end);
+        }
+      }
     }
+    nr = min(nr, rcap);
   } else {  // dense
     nr = 1;
     if (kFill && tid == 0 && rlim >= 1) rng[rbase] = make_int2(0, end);
