@@ -14,8 +14,12 @@
 // (equal starts or keys ordered by list); a prefix maximum of the range ends
 // then marks where a new union range starts, and equal keys sit next to each
 // other.  Count pass, per-chunk scan, fill pass; counts never exceed the sums
-// of the heads' per-block counts, which bound the arrays.  A block whose lists
-// do not fit in LDS is merged by one thread, list by list.
+// of the heads' per-block counts, which bound the arrays.  Lists longer than
+// LDS holds are merged in windows of the merged order: a window takes, from
+// every list, the entries below the smallest of the lists' (cap / heads)-th
+// next keys, so it never exceeds the cap and always advances; prefix maxima
+// and counts carry from window to window, and a union range's end is written
+// when the next one starts (or after the last window).
 #include "block_scan.h"
 #include "internal.h"
 
@@ -58,68 +62,6 @@ __device__ __forceinline__ void open_lists(const UnionArgs& a, const GroupDesc& 
   }
 }
 
-// One thread's merge of a block's lists (blocks too large for LDS).
-template <bool kFill>
-__device__ int merge_ranges_seq(Lists L, int2* out, int lim) {
-  int nr = 0;
-  int lo = 0, hi = -1;  // current union range (none while hi < 0)
-  for (;;) {
-    int best = -1, blo = 0, bhi = 0;
-    for (int j = 0; j < L.nh; ++j) {
-      if (L.r[j] < L.r_end[j]) {
-        const int2 x = L.rng[j][L.r[j]];
-        if (best < 0 || x.x < blo) {
-          best = j;
-          blo = x.x;
-          bhi = x.y;
-        }
-      }
-    }
-    if (best < 0) break;
-    ++L.r[best];
-    if (bhi <= blo) continue;  // empty range
-    if (hi >= 0 && blo <= hi) {
-      hi = max(hi, bhi);
-    } else {
-      if (hi >= 0) {
-        if (kFill && nr < lim) out[nr] = make_int2(lo, hi);
-        ++nr;
-      }
-      lo = blo;
-      hi = bhi;
-    }
-  }
-  if (hi >= 0) {
-    if (kFill && nr < lim) out[nr] = make_int2(lo, hi);
-    ++nr;
-  }
-  return nr;
-}
-
-template <bool kFill>
-__device__ int merge_cols_seq(Lists L, int32_t* out, uint8_t* mask, int lim) {
-  int nc = 0;
-  for (;;) {
-    int key = 0x7fffffff;
-    for (int j = 0; j < L.nh; ++j)
-      if (L.c[j] < L.c_end[j]) key = min(key, L.col[j][L.c[j]]);
-    if (key == 0x7fffffff) break;
-    int m = 0;
-    for (int j = 0; j < L.nh; ++j) {
-      if (L.c[j] < L.c_end[j] && L.col[j][L.c[j]] == key) {
-        m |= 1 << j;
-        ++L.c[j];
-      }
-    }
-    if (kFill && nc < lim) {
-      out[nc] = key;
-      mask[nc] = (uint8_t)m;
-    }
-    ++nc;
-  }
-  return nc;
-}
-
 constexpr int kUT = 256;
 constexpr int kCapR = 4096;  // ranges of one (chunk, block) merged in LDS
 constexpr int kCapC = 8192;  // columns of one (chunk, block) merged in LDS
@@ -156,7 +98,9 @@ __global__ __launch_bounds__(kUT) void union_block(UnionArgs a) {
   __shared__ int s_key[kCapC];   // list entries (range starts / columns), lists one after another
   __shared__ int s_aux[kCapC];   // range ends (ranges), merged keys (columns)
   __shared__ int s_end[kCapR];   // merged range ends
-  __shared__ int s_off[5], s_coff[5];
+  __shared__ int s_off[5];       // window: entries of list j at [s_off[j], s_off[j+1])
+  __shared__ int s_pos[4], s_wend[4];
+  __shared__ int s_bound;
   __shared__ int s_wbuf[kUT / 64];
   const int b = blockIdx.x, u = blockIdx.y, t = threadIdx.x;
   const GroupDesc gd = a.groups[u];
@@ -168,15 +112,6 @@ __global__ __launch_bounds__(kUT) void union_block(UnionArgs a) {
   Lists L;
   open_lists(a, gd, b, L);
   const int nh = L.nh;
-  if (t == 0) {
-    s_off[0] = s_coff[0] = 0;
-    for (int j = 0; j < nh; ++j) {
-      s_off[j + 1] = s_off[j] + (L.r_end[j] - L.r[j]);
-      s_coff[j + 1] = s_coff[j] + (L.c_end[j] - L.c[j]);
-    }
-  }
-  __syncthreads();
-  const int R = s_off[nh], C = s_coff[nh];
   int rbase = 0, rlim = 0, cbase = 0, clim = 0;
   if (kFill) {
     rbase = urp[b];
@@ -184,16 +119,47 @@ __global__ __launch_bounds__(kUT) void union_block(UnionArgs a) {
     cbase = ucp[b];
     clim = ucp[b + 1] - cbase;
   }
-  int nr = 0, nc = 0;
+
+  // Next window of the merged order: list j contributes its entries from
+  // s_pos[j] whose key is below s_bound, the smallest of the lists'
+  // (cap/nh)-th next keys (0x7fffffff: every list has fewer left, the last
+  // window).  key(j, i) is entry i's key in list j.  Returns the window size.
+  auto next_window = [&](int cap, const int* end, auto key) -> int {
+    if (t == 0) {
+      const int q = cap / nh;
+      int x = 0x7fffffff;
+      for (int j = 0; j < nh; ++j)
+        if (s_pos[j] + q < end[j]) x = min(x, key(j, s_pos[j] + q));
+      s_bound = x;
+    }
+    __syncthreads();
+    if (t < nh) {
+      int lo = s_pos[t], hi = end[t];
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (key(t, mid) < s_bound) lo = mid + 1; else hi = mid;
+      }
+      s_wend[t] = lo;
+    }
+    __syncthreads();
+    if (t == 0) {
+      s_off[0] = 0;
+      for (int j = 0; j < nh; ++j) s_off[j + 1] = s_off[j] + (s_wend[j] - s_pos[j]);
+    }
+    __syncthreads();
+    return s_off[nh];
+  };
 
   // ---- ranges
-  if (R > kCapR) {
-    if (t == 0) nr = merge_ranges_seq<kFill>(L, urng + rbase, rlim);
-  } else if (R > 0) {
+  if (t < nh) s_pos[t] = L.r[t];
+  __syncthreads();
+  int carry_max = -1, carry_n = 0;
+  for (;;) {
+    const int R = next_window(kCapR, L.r_end, [&](int j, int i) { return L.rng[j][i].x; });
     for (int e = t; e < R; e += kUT) {
       int j = 0;
       while (e >= s_off[j + 1]) ++j;
-      const int2 x = L.rng[j][L.r[j] + e - s_off[j]];
+      const int2 x = L.rng[j][s_pos[j] + e - s_off[j]];
       s_key[e] = x.x;
       s_aux[e] = x.y;
     }
@@ -207,7 +173,6 @@ __global__ __launch_bounds__(kUT) void union_block(UnionArgs a) {
       s_aux[kCapR + rank] = x;  // merged starts in the upper half of s_aux
     }
     __syncthreads();
-    int carry_max = -1, carry_n = 0;
     for (int c0 = 0; c0 < R; c0 += kUT) {
       const int e = c0 + t;
       const bool valid = e < R;
@@ -216,64 +181,72 @@ __global__ __launch_bounds__(kUT) void union_block(UnionArgs a) {
       const bool empty = valid && hi <= lo;
       int incl, excl, tot;
       block_scan_max<kUT>(valid && !empty ? hi : -1, -1, s_wbuf, &incl, &excl, &tot);
-      incl = max(incl, carry_max);
       excl = max(excl, carry_max);
-      // a range starts a union range when it begins after every end before it
+      // a range starts a union range when it begins after every end before it,
+      // which is then where the previous union range ends
       const bool is_new = valid && !empty && (lo > excl || excl < 0);
       int ntot;
       const int gid = carry_n + block_excl_scan<kUT>(is_new ? 1 : 0, s_wbuf, &ntot);
-      if (kFill && is_new && gid < rlim) urng[rbase + gid].x = lo;
-      // ... and ends one when the next non-empty range begins after incl
-      if (kFill && valid && !empty) {
-        int nx = e + 1;
-        while (nx < R && s_end[nx] <= s_aux[kCapR + nx]) ++nx;  // skip empty ranges
-        const bool is_last = nx >= R || s_aux[kCapR + nx] > incl;
-        const int g = gid + (is_new ? 1 : 0) - 1;
-        if (is_last && g >= 0 && g < rlim) urng[rbase + g].y = incl;
+      if (kFill && is_new) {
+        if (gid < rlim) urng[rbase + gid].x = lo;
+        if (gid >= 1 && gid - 1 < rlim) urng[rbase + gid - 1].y = excl;
       }
       carry_max = max(carry_max, tot);
       carry_n += ntot;
     }
-    nr = carry_n;
+    const bool last = s_bound == 0x7fffffff;
+    __syncthreads();
+    if (t < nh) s_pos[t] = s_wend[t];
+    __syncthreads();
+    if (last) break;
   }
+  if (kFill && t == 0 && carry_n >= 1 && carry_n - 1 < rlim) urng[rbase + carry_n - 1].y = carry_max;
+  const int nr = carry_n;
   __syncthreads();
 
   // ---- columns
-  if (C > kCapC) {
-    if (t == 0) nc = merge_cols_seq<kFill>(L, ucol + cbase, umask + cbase, clim);
-  } else if (C > 0) {
+  if (t < nh) s_pos[t] = L.c[t];
+  __syncthreads();
+  int ccarry_n = 0, carry_last = -1;
+  for (;;) {
+    const int C = next_window(kCapC, L.c_end, [&](int j, int i) { return L.col[j][i]; });
     for (int e = t; e < C; e += kUT) {
       int j = 0;
-      while (e >= s_coff[j + 1]) ++j;
-      s_key[e] = L.col[j][L.c[j] + e - s_coff[j]];
+      while (e >= s_off[j + 1]) ++j;
+      s_key[e] = L.col[j][s_pos[j] + e - s_off[j]];
     }
     __syncthreads();
     for (int e = t; e < C; e += kUT) {
       int j = 0;
-      while (e >= s_coff[j + 1]) ++j;
+      while (e >= s_off[j + 1]) ++j;
       const int x = s_key[e];
-      s_aux[(e - s_coff[j]) + preceding(s_key, s_coff, nh, j, x)] = x;
+      s_aux[(e - s_off[j]) + preceding(s_key, s_off, nh, j, x)] = x;
     }
     __syncthreads();
-    int carry_n = 0;
     for (int c0 = 0; c0 < C; c0 += kUT) {
       const int e = c0 + t;
       const bool valid = e < C;
       const int x = valid ? s_aux[e] : 0;
-      const bool first = valid && (e == 0 || s_aux[e - 1] != x);
+      const bool first = valid && (e == 0 ? x != carry_last : s_aux[e - 1] != x);
       int ntot;
-      const int pos = carry_n + block_excl_scan<kUT>(first ? 1 : 0, s_wbuf, &ntot);
+      const int pos = ccarry_n + block_excl_scan<kUT>(first ? 1 : 0, s_wbuf, &ntot);
       if (kFill && first && pos < clim) {
         int m = 0;
         for (int j = 0; j < nh; ++j)
-          if (contains(s_key, s_coff[j], s_coff[j + 1], x)) m |= 1 << j;
+          if (contains(s_key, s_off[j], s_off[j + 1], x)) m |= 1 << j;
         ucol[cbase + pos] = x;
         umask[cbase + pos] = (uint8_t)m;
       }
-      carry_n += ntot;
+      ccarry_n += ntot;
     }
-    nc = carry_n;
+    if (C > 0) carry_last = s_aux[C - 1];
+    const bool last = s_bound == 0x7fffffff;
+    __syncthreads();
+    if (t < nh) s_pos[t] = s_wend[t];
+    __syncthreads();
+    if (last) break;
   }
+  const int nc = ccarry_n;
 
   if (!kFill && t == 0) {
     urp[b + 1] = nr;

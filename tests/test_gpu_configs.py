@@ -191,3 +191,28 @@ def test_key_segments_and_chunks(out_dtype):
     ms.ms_sparse_attn(st.prob, st.hp, st.q, st.k, st.v, out2, ws)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), st.out.view(torch.int16))
+
+
+def test_union_of_many_columns_per_block():
+    """Four Vertical-Slash heads of one KV head, dense enough to be grouped
+    through their many verticals (16000 of 32768 keys, few slashes): late
+    query blocks hold more union columns than LDS takes at once, so the union
+    builder merges them in several windows.  Sampled blocks against the
+    oracle."""
+    n = 32768
+    heads = [W.vs(16000, 20)] * 4
+    w = W.custom("union_cols", n, 4, 1, heads, recipe="vs_planted", seed=32)
+    st = run_staged(make(w), debug=False)
+    sel = selections(st)
+    nb = n // 64
+    blocks = [0, 7, nb // 2, nb - 2, nb - 1]
+    per_head = [read_index_blocks(st.prob, st.hp, st.index, h, blocks) for h in range(4)]
+    assert sum(len(per_head[h][nb - 1][1]) for h in range(4)) > 8192, "late blocks should exceed one window"
+    q, k, v = f64(st.q), f64(st.k[0]), f64(st.v[0])
+    for h in range(4):
+        for b in blocks:
+            ref_b = oracle.vs_block_index(sel[h][1], sel[h][2], b)
+            np.testing.assert_array_equal(per_head[h][b][0], ref_b[0])
+            np.testing.assert_array_equal(per_head[h][b][1], ref_b[1])
+            ro, rl = oracle.attention_block(q[h, 64 * b:64 * b + 64], k, v, ref_b, b)
+            check_attention(f64(st.out[h, 64 * b:64 * b + 64]), ro, f"head {h} block {b}")

@@ -429,3 +429,57 @@ def test_grid_keeps_more_attention_mass_on_video_like_inputs():
     r = rec.cpu().numpy()
     print(f"  recall grid {r[0]:.4f}  a-shape {r[1]:.4f}", flush=True)
     assert r[0] > r[1] + 0.05
+
+
+@pytest.mark.parametrize("n,q_block0", [(64, 0), (128, 1), (192, 0)])
+def test_smallest_sequences_every_pattern(n, q_block0):
+    """One to three query blocks, every pattern (Grid with frames that reach
+    before the first key), whole sequences and a one-block chunk."""
+    heads = [W.vs(3, 5), W.bs(1), W.ashape(8, 16), W.dense(), W.grid(20, 3, 2, 8), W.vs(n, n)]
+    w = W.custom("tiny", n, len(heads), 2, heads, recipe="vs_planted", seed=90)
+    q, k, v = W.generate(w, device="cuda")
+    qc = q[:, 64 * q_block0:].contiguous()
+    st = make(w, qkv=(qc, k, v))
+    st.prob = ms.problem(n, len(heads), 2, q_block0=q_block0)
+    nv, ns, nbk = ms.ms_selection_sizes(st.prob, st.hp)
+    vert = torch.empty(max(nv, 1), dtype=torch.int32, device="cuda")
+    slash = torch.empty(max(ns, 1), dtype=torch.int32, device="cuda")
+    blocks = torch.empty(max(nbk, 1), dtype=torch.int32, device="cuda")
+    ws = ms.empty_workspace(ms.ms_estimate_workspace_bytes(st.prob, st.hp))
+    ms.ms_estimate_vs(st.prob, st.hp, qc, k, vert, slash, ws)
+    ms.ms_estimate_block(st.prob, st.hp, qc, k, blocks, ws)
+    index = ms.empty_workspace(ms.ms_index_bytes(st.prob, st.hp))
+    ms.ms_build_index(st.prob, st.hp, vert, slash, blocks, index)
+    out = torch.empty_like(qc)
+    lse = torch.empty((len(heads), qc.shape[1]), dtype=torch.float32, device="cuda")
+    ms.ms_sparse_attn_indexed(st.prob, st.hp, qc, k, v, index, out, ms.empty_workspace(ms.ms_attn_workspace_bytes(st.prob)),
+                              lse)
+    torch.cuda.synchronize()
+    qh, kh, vh = f64(qc), f64(k), f64(v)
+    got_idx = ms.read_index(st.prob, st.hp, index)
+    vv, sv, bv = vert.cpu().numpy(), slash.cpu().numpy(), blocks.cpu().numpy()
+    ov = os_ = ob = 0
+    for h, p in enumerate(heads):
+        kv = h // (len(heads) // 2)
+        if p.pattern == W.VERTICAL_SLASH:
+            sel = ("vs", vv[ov:ov + p.n_vertical].astype(np.int64), sv[os_:os_ + p.n_slash].astype(np.int64))
+            ov += p.n_vertical
+            os_ += p.n_slash
+        elif p.pattern == W.BLOCK_SPARSE:
+            nbq = n // 64 - q_block0
+            rows = bv[ob:ob + nbq * p.top_k_blocks].reshape(nbq, p.top_k_blocks)
+            sel = ("bs", [r[r >= 0].astype(np.int64) for r in rows])
+            ob += nbq * p.top_k_blocks
+        else:
+            sel = ("static",)
+        ref_idx = oracle.head_index(p, sel, n, q_block0=q_block0)
+        for g_arr, r_arr in zip(got_idx[h], oracle.index_to_csr(ref_idx)):
+            np.testing.assert_array_equal(g_arr, r_arr, err_msg=f"head {h}")
+        for r, bidx in enumerate(ref_idx):
+            b = q_block0 + r
+            ro, rl = oracle.attention_block(qh[h, 64 * r:64 * r + 64], kh[kv], vh[kv], bidx, b, ashape=ashape_of(p))
+            check_attention(f64(out[h, 64 * r:64 * r + 64]), ro, f"head {h} block {b}")
+            gl = f64(lse[h, 64 * r:64 * r + 64])
+            fin = np.isfinite(rl)
+            assert np.all(np.isneginf(gl[~fin]))
+            np.testing.assert_allclose(gl[fin], rl[fin], rtol=0, atol=LSE_ATOL)
