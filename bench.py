@@ -5,8 +5,9 @@ own dense causal kernel on the same GPU.
 One step = one ms_sparse_attn call on one layer of synthetic inputs already
 resident in HBM.  The headline workload is the 1M-token Vertical-Slash layer
 (32 Q / 8 KV heads, d = 128, 1000 verticals + 6096 slashes per head); the
-128K mixed-pattern layer (24 VS / 6 BS / 2 A-shape heads) is reported beside
-it.  Prints ONE JSON line.
+other four workloads (128K mixed 24 VS / 6 BS / 2 A-shape heads, 32K
+Block-Sparse, 128K A-shape, 4K Vertical-Slash) are reported beside it under
+"side".  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload vs_1m|mixed_128k|...]
 """
@@ -38,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="vs_1m", choices=sorted(WORKLOADS))
-    ap.add_argument("--side", default="mixed_128k", help="second workload reported beside the headline ('' = none)")
+    ap.add_argument("--side", default="mixed_128k,bs_32k,ashape_128k,vs_4k",
+                    help="comma-separated workloads reported beside the headline ('' = none)")
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -376,13 +378,14 @@ def main():
     torch.cuda.empty_cache()
 
     side = {}
-    if a.side and a.side != a.workload:
-        print(f"[bench] side workload {a.side}", file=sys.stderr, flush=True)
-        r2 = run_layer(ms, torch, W, WORKLOADS[a.side], a.steps, a.warmup, a.dense_steps, not a.no_dense)
+    for name in [x for x in a.side.split(",") if x and x != a.workload]:
+        print(f"[bench] side workload {name}", file=sys.stderr, flush=True)
+        r2 = run_layer(ms, torch, W, WORKLOADS[name], a.steps, a.warmup, a.dense_steps, not a.no_dense)
         for key in ("q", "k", "v"):
             r2.pop(key)
-        side[a.side] = summary(r2)
-        print(f"[bench] {a.side}: {json.dumps(side[a.side])}", file=sys.stderr, flush=True)
+        side[name] = summary(r2)
+        print(f"[bench] {name}: {json.dumps(side[name])}", file=sys.stderr, flush=True)
+        del r2
         torch.cuda.empty_cache()
 
     if a.copy_calibration:
