@@ -26,8 +26,9 @@
 // edges, and of its columns, found by a wave-wide search of the CSR) and
 // writes O / l and the log-sum-exp of that share; the combine kernel merges a
 // block's segment records in segment order.  Workgroups are numbered segment
-// first, so the ones in flight read the same segment of K/V and L2 serves
-// most of their rows; per (query block, key) the work is unchanged.
+// first, so the ones in flight read the same segment of K/V and L2 serves the
+// rows that several of them read; per (query block, key) the work is
+// unchanged.
 //
 // LDS tiles are row-major (one 256-byte row per key) with the 16-byte chunks
 // of row r XOR-swizzled: chunk c sits at chunk slot c ^ swz(r).  One
