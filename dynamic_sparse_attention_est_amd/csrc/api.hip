@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <string>
 #include <tuple>
@@ -82,6 +83,7 @@ struct Plan {
   std::vector<HeadDesc> desc;
   int hpw = 1;
   std::vector<GroupDesc> gdesc;  // chunks served by the grouped sparse kernel
+  int n_wide = 0;                // the first n_wide chunks run with hpw heads per workgroup, the rest with 2
   std::vector<int16_t> solo;     // heads served one by one
   size_t index_bytes = 0;
   // attention workspace: fp16 V copy, then the key-segment records (without
@@ -336,6 +338,14 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       P.gdesc.push_back(g);
     }
   }
+  // With four heads per workgroup, chunks of two go to the two-head kernel
+  // instead (a four-head workgroup costs about the same per piece however many
+  // of its heads are present): the wider chunks first, then those.
+  P.n_wide = (int)P.gdesc.size();
+  if (P.hpw == 4) {
+    std::stable_partition(P.gdesc.begin(), P.gdesc.end(), [](const GroupDesc& g) { return g.nheads > 2; });
+    P.n_wide = (int)std::count_if(P.gdesc.begin(), P.gdesc.end(), [](const GroupDesc& g) { return g.nheads > 2; });
+  }
   for (GroupDesc& g : P.gdesc) {
     int64_t ur = 0, uc = 0;
     for (int j = 0; j < g.nheads; ++j) {
@@ -536,8 +546,15 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
   if (!P.gdesc.empty()) {
-    a.n_list = (int)P.gdesc.size();
-    HIP_TRY(launch_group_sparse(a, reinterpret_cast<const GroupDesc*>(index + kTableBytes), s), "attention launch");
+    const GroupDesc* chunks = reinterpret_cast<const GroupDesc*>(index + kTableBytes);
+    if (P.n_wide > 0) {
+      a.n_list = P.n_wide;
+      HIP_TRY(launch_group_sparse(a, chunks, P.hpw, s), "attention launch");
+    }
+    if ((int)P.gdesc.size() > P.n_wide) {
+      a.n_list = (int)P.gdesc.size() - P.n_wide;
+      HIP_TRY(launch_group_sparse(a, chunks + P.n_wide, 2, s), "attention launch");
+    }
   }
   if (!P.solo.empty()) {
     a.n_list = (int)P.solo.size();

@@ -673,10 +673,9 @@ __global__ __launch_bounds__(256) void group_sparse_h2(AttnArgs a, const GroupDe
   group_sparse_body<2, 4>(a, groups, arena);
 }
 
-hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, hipStream_t s) {
-  const int hpw = hpw_of(a.grp);
+hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, int hpw, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)a.nb * a.n_list));
-  // chunks exist only for group sizes with two or four heads per workgroup
+  // chunks of two to four heads, two or four heads per workgroup
   if (hpw == 4)
     hipLaunchKernelGGL(group_sparse_h4, grid, dim3(512), 0, s, a, groups, a.arena);
   else if (hpw == 2)

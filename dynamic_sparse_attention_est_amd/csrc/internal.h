@@ -156,8 +156,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s);
 // Full causal attention, query heads that share a KV head served together.
 hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s);
-// Sparse attention over the union index (groups: device table of the chunks).
-hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, hipStream_t s);
+// Sparse attention over the union index (groups: device table of the
+// a.n_list chunks, hpw = 2 or 4 heads per workgroup, chunks of at most hpw).
+hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, int hpw, hipStream_t s);
 // Union index of every chunk (after the per-head index is complete).
 hipError_t launch_union_build(const HeadDesc* table, GroupDesc* groups, const GroupDesc* host_groups, char* arena,
                               int n_groups, int nb, hipStream_t s);

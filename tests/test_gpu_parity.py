@@ -339,6 +339,17 @@ def test_attention_grouped_union(hq, hkv, seed):
     _attention_check(run_staged(make(w)))
 
 
+def test_attention_chunks_of_two_three_and_four_heads():
+    """Four Q heads per KV head: KV heads with two, three and four dense heads
+    form chunks of two (served two heads per workgroup), three (one idle
+    slot) and four, beside sparse heads served one by one."""
+    n = 64 * 24
+    d, sp = W.vs(200, 90), W.bs(2)
+    heads = [d, d, sp, sp,  d, d, d, sp,  d, d, d, d,  sp, d, sp, d]
+    w = W.custom("chunks", n, 16, 4, heads, recipe="vs_planted", seed=24)
+    _attention_check(run_staged(make(w)))
+
+
 def test_one_shot_equals_staged_and_is_deterministic():
     n = 1024
     heads = [W.vs(48, 80), W.bs(6), W.ashape(40, 150), W.vs(100, 30)]
