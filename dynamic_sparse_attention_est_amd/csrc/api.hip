@@ -325,10 +325,14 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       else
         P.solo.push_back((int16_t)h);
     }
-    for (size_t c = 0; c < dense_heads.size(); c += P.hpw) {
-      const size_t m = std::min<size_t>(P.hpw, dense_heads.size() - c);
+    for (size_t c = 0; c < dense_heads.size();) {
+      size_t m = std::min<size_t>(P.hpw, dense_heads.size() - c);
+      // A four-head workgroup costs about the same per piece however many of
+      // its heads are present, so three heads run as a chunk of two and a
+      // head alone.
+      if (m == 3) m = 2;
       if (m < 2) {
-        P.solo.push_back((int16_t)dense_heads[c]);
+        P.solo.push_back((int16_t)dense_heads[c++]);
         continue;
       }
       GroupDesc g{};
@@ -336,11 +340,11 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       g.nheads = (int)m;
       for (size_t j = 0; j < m; ++j) g.head[j] = (int16_t)dense_heads[c + j];
       P.gdesc.push_back(g);
+      c += m;
     }
   }
   // With four heads per workgroup, chunks of two go to the two-head kernel
-  // instead (a four-head workgroup costs about the same per piece however many
-  // of its heads are present): the wider chunks first, then those.
+  // instead: the four-head chunks first, then those.
   P.n_wide = (int)P.gdesc.size();
   if (P.hpw == 4) {
     std::stable_partition(P.gdesc.begin(), P.gdesc.end(), [](const GroupDesc& g) { return g.nheads > 2; });

@@ -71,6 +71,11 @@ struct RangeWindow {
     } else {
       lo = hi = 0x7fffffff;
     }
+    // The window is settled here (the compiler waits for the load before this
+    // use) and from then on counts as defined by this statement, so the
+    // readlanes of later pieces wait for nothing, in particular not for the
+    // ring's loads in flight.
+    asm volatile("" : "+v"(lo), "+v"(hi));
   }
   __device__ __forceinline__ void init(const int2* l, int first, int end_) {
     list = l;
