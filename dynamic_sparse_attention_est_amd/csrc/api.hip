@@ -74,7 +74,9 @@ struct Plan {
   std::vector<int16_t> bs_kv_slot;               // per BS slot: index into bs_kv_heads
   std::vector<int64_t> vert_off, slash_off, blk_off;
   int64_t n_vert = 0, n_slash = 0, n_blocks = 0;
-  int ntiles = 0;
+  VsGroups vsg{};     // VS heads by KV head, at most four a group
+  int vs_chunk = 0;   // 64-key tiles per estimation workgroup
+  int vs_nchunks = 0;
   // estimation workspace (byte offsets)
   size_t e_part = 0, e_stats = 0, e_diag = 0, e_v = 0, e_s = 0, e_qpool = 0, e_kpool = 0, e_scores = 0, e_topk = 0;
   size_t est_bytes = 0;
@@ -248,14 +250,37 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       P.bs_kv_slot.push_back((int16_t)kv_slot_of[kv]);
     }
   }
+  // Vertical-Slash estimation groups: the VS heads of one KV head, four at a
+  // time (one estimation workgroup reads a K tile once for its group).
+  P.vsg = VsGroups{};
+  for (int kv = 0; kv < P.hkv; ++kv) {
+    int cnt = 0;
+    for (int h = kv * P.grp; h < (kv + 1) * P.grp; ++h) {
+      if (P.vs_slot[h] < 0) continue;
+      if (cnt == 4) {
+        ++P.vsg.n_groups;
+        cnt = 0;
+      }
+      const int i = P.vsg.q_begin[P.vsg.n_groups] + cnt;
+      P.vsg.q_head[i] = (int16_t)h;
+      P.vsg.q_slot[i] = (int16_t)P.vs_slot[h];
+      P.vsg.kv_head[P.vsg.n_groups] = (int16_t)kv;
+      P.vsg.q_begin[P.vsg.n_groups + 1] = (int16_t)(i + 1);
+      ++cnt;
+    }
+    if (cnt) ++P.vsg.n_groups;
+  }
   // Estimation workspace.
-  P.ntiles = (int)((P.n + kVsTile - 1) / kVsTile);
+  if (P.n_vs) {
+    P.vs_chunk = vs_chunk_tiles(P.n, P.vsg.n_groups);
+    P.vs_nchunks = (int)((P.n / 64 + P.vs_chunk - 1) / P.vs_chunk);
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   const size_t f = sizeof(float);
-  P.e_part = take((size_t)P.n_vs * P.ntiles * kLastQ * 2 * f);
+  P.e_part = take((size_t)P.n_vs * P.vs_nchunks * kLastQ * 2 * f);
   P.e_stats = take((size_t)P.n_vs * kLastQ * 2 * f);
-  P.e_diag = take((size_t)P.n_vs * P.ntiles * 320 * f);
+  P.e_diag = take((size_t)P.n_vs * P.vs_nchunks * 128 * f);
   P.e_v = take((size_t)P.n_vs * P.n * f);
   P.e_s = take((size_t)P.n_vs * P.n * f);
   P.e_qpool = take((size_t)P.n_bs * P.nbq * kD * f);
@@ -437,25 +462,10 @@ ms_status check_ws(const void* ws, size_t have, size_t need, const char* name) {
 ms_status run_estimate_vs(const Plan& P, const uint16_t* q, const uint16_t* k, int32_t* vert, int32_t* slash,
                           float* dbg_v, float* dbg_s, char* ws, hipStream_t s) {
   if (P.n_vs == 0) return MS_OK;
-  VsGroups g{};
-  for (int kv = 0; kv < P.hkv; ++kv) {
-    const int begin = g.q_begin[g.n_groups];
-    int cnt = 0;
-    for (int h = kv * P.grp; h < (kv + 1) * P.grp; ++h)
-      if (P.vs_slot[h] >= 0) {
-        g.q_head[begin + cnt] = (int16_t)h;
-        g.q_slot[begin + cnt] = (int16_t)P.vs_slot[h];
-        ++cnt;
-      }
-    if (cnt) {
-      g.kv_head[g.n_groups] = (int16_t)kv;
-      g.q_begin[g.n_groups + 1] = (int16_t)(begin + cnt);
-      ++g.n_groups;
-    }
-  }
   float* v_sc = reinterpret_cast<float*>(ws + P.e_v);
   float* s_sc = reinterpret_cast<float*>(ws + P.e_s);
-  HIP_TRY(launch_vs_estimate(q, k, P.n, P.qm, P.scale_log2, g, P.n_vs, reinterpret_cast<float*>(ws + P.e_part),
+  HIP_TRY(launch_vs_estimate(q, k, P.n, P.qm, P.scale_log2, P.vsg, P.n_vs, P.vs_chunk,
+                             reinterpret_cast<float*>(ws + P.e_part),
                              reinterpret_cast<float*>(ws + P.e_stats), reinterpret_cast<float*>(ws + P.e_diag), v_sc,
                              s_sc, s),
           "vertical-slash estimation launch");

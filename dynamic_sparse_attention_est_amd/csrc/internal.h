@@ -12,8 +12,6 @@ constexpr int kD = 128;        // head dimension
 constexpr int kBM = 64;        // query rows per query block; Block-Sparse pooling block
 constexpr int kLastQ = 64;     // rows scored by the Vertical-Slash estimator
 constexpr int kMaxHeads = 128; // Q heads per call
-constexpr int kVsTile = 256;   // keys per workgroup in the Vertical-Slash estimator
-constexpr int kVsDiag = kVsTile + kLastQ - 1;  // diagonals touched by one estimator tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -69,16 +67,21 @@ hipError_t launch_write_table(HeadDesc* table, const HeadDesc* host_descs, int f
 
 // Vertical-Slash estimation.
 struct VsGroups {
-  int32_t n_groups;                 // KV heads that serve at least one VS head
+  int32_t n_groups;                 // KV heads that serve VS heads, at most four VS heads a group
   int16_t kv_head[kMaxHeads];       // per group
   int16_t q_begin[kMaxHeads + 1];   // per group: range into q_head[]
   int16_t q_head[kMaxHeads];        // VS Q heads, grouped by KV head
   int16_t q_slot[kMaxHeads];        // their VS slot
 };
-// q: the call's query rows [H_q][qm][128], the last of them row n - 1.
+// Tiles of 64 keys per estimation workgroup for a sequence of n keys and
+// n_groups groups (the workspace holds per-chunk partials).
+int vs_chunk_tiles(int64_t n, int n_groups);
+// q: the call's query rows [H_q][qm][128], the last of them row n - 1.  Every
+// group holds at most four VS heads.  part_mz: [n_vs][chunks][64][2] floats,
+// stats: [n_vs][64][2], diag_part: [n_vs][chunks][128], v/s_scores: [n_vs][n].
 hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int64_t qm, float scale_log2,
-                              const VsGroups& groups, int n_vs, float* part_mz, float* stats, float* diag_part,
-                              float* v_scores, float* s_scores, hipStream_t s);
+                              const VsGroups& groups, int n_vs, int chunk_tiles, float* part_mz, float* stats,
+                              float* diag_part, float* v_scores, float* s_scores, hipStream_t s);
 
 // Block-Sparse estimation.
 hipError_t launch_bs_pool(const uint16_t* src, int64_t n, const int16_t* heads, int nheads, float* pooled,

@@ -6,183 +6,380 @@
 // z_ij = scale q_i.k_j (j <= i) and p_ij = softmax_j z_ij:
 //   vertical score v_j = sum_r p_ij,   slash score s_o = sum_r p_{i,i-o}.
 // Column sums need the final row normalisers, so K is streamed twice:
-//   pass 1: per 256-key tile, partial row max and sum of exp  -> part_mz
-//   stats : fixed-order merge of the tile partials             -> (M_i, Z_i)
-//   pass 2: p = exp2(x - M)/Z into LDS; column sums (complete per tile) and
-//           per-tile partial diagonal sums (256 + 63 diagonals) -> v, diag_part
-//   diag  : each diagonal adds its (at most two) tile partials in tile order.
-// One workgroup covers one 256-key tile of one KV head for every Vertical-
-// Slash Q head that reads it, so each K tile is read once per pass.  Logits
-// come from v_mfma_f32_32x32x16_bf16 (S^T = K Q^T, keys x rows); every
-// reduction has a fixed order, so results are bitwise reproducible.
+//   vs_rows  : per chunk of keys, each row's running max and sum of exp -> part_mz
+//   vs_stats : fixed-order merge of the chunk partials               -> (M_i, Z_i)
+//   vs_scores: p = 2^(x - M) / Z; column sums (complete per 64-key tile) and
+//              diagonal sums (complete except at chunk edges)          -> v, s
+//   vs_diag  : the 64 diagonals at each chunk edge add their two halves.
+//
+// Both passes have one shape.  A workgroup takes one KV head and up to four of
+// its Vertical-Slash Q heads, one per wavefront, over a chunk of consecutive
+// 64-key tiles.  Each wave keeps its head's 64 query rows in registers for the
+// whole chunk (MFMA fragments); the K tiles stream through a ring of four LDS
+// stages, filled by buffer loads that go straight to LDS three tiles ahead of
+// the one being scored, and every K tile is read from memory once for all the
+// heads of the workgroup.  Logits come from v_mfma_f32_32x32x16_bf16.
+//
+// Row statistics take the logits transposed (keys x rows, one row per lane):
+// each lane keeps a running max and sum for its row over its half of the keys.
+// The scores pass takes them rows x keys (one key per lane), so a column sum
+// is a sum within the lane plus one exchange between the two half-waves.  A
+// diagonal runs across lanes: for register r, lane D of each half-wave fetches
+// (ds_bpermute) the element of its own diagonal class D = (row - key) mod 32,
+// and adds it to one of four accumulators by the sign and 32-block of
+// row - key; a tile's negative diagonals are completed by the next tile.
+// Every sum runs in a fixed order, so results are bitwise reproducible.
+#include <algorithm>
+#include <utility>
+
 #include "internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kT = kVsTile;      // 256 keys per workgroup, 64 per wave
-constexpr int kPS = kT + 1;      // LDS row stride of the probability tile (floats)
-constexpr int kDiagStride = 320; // stored diagonals per tile (319 used)
+constexpr int kET = 64;                   // keys per tile
+constexpr int kRowB = kD * 2;             // one K row (bytes)
+constexpr int kTileB = kET * kRowB;       // one K tile (16 KiB)
+constexpr int kES = 4;                    // ring stages
+constexpr int kLoads = kTileB / 1024 / 4; // load-to-LDS instructions per wave per tile
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__shared__ __attribute__((aligned(1024))) char e_stage0[kTileB];
+__shared__ __attribute__((aligned(1024))) char e_stage1[kTileB];
+__shared__ __attribute__((aligned(1024))) char e_stage2[kTileB];
+__shared__ __attribute__((aligned(1024))) char e_stage3[kTileB];
+__shared__ __attribute__((aligned(16))) float e_rows[4][2][kLastQ];
+
+template <int I>
+__device__ __forceinline__ char* est_stage() {
+  static_assert(I >= 0 && I < kES, "stage");
+  if constexpr (I == 0) return e_stage0;
+  if constexpr (I == 1) return e_stage1;
+  if constexpr (I == 2) return e_stage2;
+  if constexpr (I == 3) return e_stage3;
+}
+
+// Chunk slot of 16-byte chunk c of tile row r is c ^ swz(r) (16 distinct
+// values over 16 consecutive rows), so the K fragment reads are free of bank
+// conflicts.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for the ring's loads in flight); the empty asm statements keep memory
+// accesses on their side.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int I, int N, class F>
+__device__ __forceinline__ bool run_steps(F& f) {
+  if constexpr (I == N) {
+    return true;
+  } else {
+    if (!f(std::integral_constant<int, I>{})) return false;
+    return run_steps<I + 1, N>(f);
+  }
+}
 
 struct VsArgs {
   const uint16_t* q;  // [H_q][qm][128]: the call's query rows, which end at row n - 1
   const uint16_t* k;
   int64_t n;
   int64_t qm;
-  int32_t ntiles;
-  float sl2;          // scale * log2(e): logits are kept in log2 units
-  float* part_mz;     // [n_vs][ntiles][64][2]
-  float* stats;       // [n_vs][64][2]  (M, Z)
-  float* diag_part;   // [n_vs][ntiles][320]
-  float* v_scores;    // [n_vs][n]
-  float* s_scores;    // [n_vs][n]
+  int32_t ntiles;      // n / 64
+  int32_t chunk_tiles; // tiles per workgroup
+  int32_t nchunks;
+  float sl2;           // scale * log2(e): logits are kept in log2 units
+  float* part_mz;      // [n_vs][nchunks][64][2]
+  float* stats;        // [n_vs][64][2]  (M, Z)
+  float* diag_part;    // [n_vs][nchunks][128]: first tile's diagonals 0..63, last tile's carry
+  float* v_scores;     // [n_vs][n]
+  float* s_scores;     // [n_vs][n]
   VsGroups groups;
 };
 
-// Logit tile of one wave: keys j0 + 64w + 32kt + 8(r/4) + 4g + r%4 (kt = 0, 1)
-// against rows 32rt + lane%32 (rt = 0, 1) of the last 64 rows, in log2 units,
-// -inf where the key lies after the row.
-__device__ __forceinline__ void logits(const bf16x8 (&kf)[2][8], const uint16_t* qlast, int64_t n, int j0w,
-                                       int lane, float sl2, f32x16 (&x)[2][2]) {
+// Element r of a 32x32 product tile sits in lane half g at position
+// 8(r/4) + 4g + r%4 along the tile's first axis.
+__device__ __forceinline__ constexpr int pos5(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+template <bool kScores>
+__device__ __forceinline__ void est_body(const VsArgs& a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
+  const int chunk = blockIdx.x, gi = blockIdx.y;
+  const int q0 = a.groups.q_begin[gi];
+  const bool active = w < a.groups.q_begin[gi + 1] - q0;
+  const int h = active ? a.groups.q_head[q0 + w] : a.groups.q_head[q0];
+  const int slot = active ? a.groups.q_slot[q0 + w] : 0;
+  const int64_t n = a.n;
+  const int t0 = chunk * a.chunk_tiles;
+  const int t1 = min(a.ntiles, t0 + a.chunk_tiles);
+  const int last_tile = a.ntiles - 1;  // the only tile with keys after some of the 64 rows
+
+  const int nbytes = (int)((uint32_t)n * (uint32_t)kRowB);
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.k + (int64_t)a.groups.kv_head[gi] * n * kD), 0, nbytes, 0x00020000);
+  // Load d of this wave fills tile rows 16w + 4d + lane/16; the lane writes
+  // slot lane%16 and fetches chunk (lane%16) ^ swz(row).
+  uint32_t lofs[kLoads];
+#pragma unroll
+  for (int d = 0; d < kLoads; ++d) {
+    const int row = 16 * w + 4 * d + (lane >> 4);
+    lofs[d] = (uint32_t)row * kRowB + 16u * (uint32_t)((lane & 15) ^ swz(row));
+  }
+  // Tiles past the chunk read out of range (zeros, no memory traffic).
+  auto issue = [&](char* st, int tile) {
+    const uint32_t base = tile < t1 ? (uint32_t)tile * kTileB : (uint32_t)nbytes;
+#pragma unroll
+    for (int d = 0; d < kLoads; ++d)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(st + 1024 * (kLoads * w + d)), 16, base + lofs[d], 0,
+                                               0, 0);
+  };
+  // K fragment t of key half kt: key 32kt + l32, d = 16t + 8g .. +8.
+  auto kfrag = [&](const char* st, int kt, int t) {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(st + kt * (32 * kRowB) + l32 * kRowB + 16 * ((2 * t + g) ^ swz(l32))));
+  };
+
+  // Query fragments of rows 32rt + l32 of the last 64, d = 16t + 8g .. +8.
   bf16x8 qf[2][8];
+  if (active) {
+    const uint16_t* qh = a.q + ((int64_t)h * a.qm + a.qm - kLastQ) * kD;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        qf[rt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + (32 * rt + l32) * kD + 16 * t + 8 * g));
+  }
+
+  // Scores pass: the head's row maxima and 1 / row sums, row = lane, kept in
+  // LDS (e_rows[w][0][row], e_rows[w][1][row]) and read four rows at a time.
+  float stat_m = 0.f, stat_z = 1.f;
+  if constexpr (kScores) {
+    if (active) {
+      const float* st = a.stats + ((int64_t)slot * kLastQ + lane) * 2;
+      stat_m = st[0];
+      stat_z = st[1];
+    }
+  }
+
+  auto prologue = [&](auto st_c) -> bool {
+    constexpr int ST = decltype(st_c)::value;
+    issue(est_stage<ST>(), t0 + ST);
+    return true;
+  };
+  run_steps<0, kES - 1>(prologue);
+  // The query fragments and statistics, loaded before the ring, have landed
+  // once only the ring's loads are in flight; from here on they count as
+  // defined by these statements, so no later use waits for memory.
+  wait_vm<(kES - 1) * kLoads>();
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      qf[rt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qlast + (32 * rt + l32) * kD + 16 * t + 8 * g));
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kt][t], qf[rt][t], acc, 0, 0, 0);
-      const int64_t row = n - kLastQ + 32 * rt + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t key = j0w + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-        x[kt][rt][r] = key <= row ? acc[r] * sl2 : -INFINITY;
-      }
-    }
-}
-
-// K fragments (A operand) of one wave: key j0w + 32kt + lane%32 (clamped
-// inside the sequence; keys past n are masked as lying after every row),
-// d = 16t + 8g .. +8.
-__device__ __forceinline__ void load_k(const uint16_t* kb, int64_t n, int j0w, int lane, bf16x8 (&kf)[2][8]) {
-  const int l32 = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int64_t key = min((int64_t)(j0w + 32 * kt + l32), n - 1);
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      kf[kt][t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + key * kD + 16 * t + 8 * g));
+    for (int t = 0; t < 8; ++t) asm volatile("" : "+v"(qf[rt][t]));
+  if constexpr (kScores) {
+    asm volatile("" : "+v"(stat_m), "+v"(stat_z));
+    e_rows[w][0][lane] = stat_m;
+    e_rows[w][1][lane] = 1.f / stat_z;
   }
-}
 
-__global__ __launch_bounds__(256) void vs_pass1(VsArgs a) {
-  __shared__ float red[4][kLastQ][2];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int tile = blockIdx.x, gi = blockIdx.y;
-  const int64_t n = a.n;
-  const int j0w = tile * kT + 64 * w;
-  bf16x8 kf[2][8];
-  load_k(a.k + (int64_t)a.groups.kv_head[gi] * n * kD, n, j0w, lane, kf);
+  // Row statistics state: lane's row 32rt + l32, over its half of the keys.
+  float m_run[2] = {-INFINITY, -INFINITY}, z_run[2] = {0.f, 0.f};
+  // Scores state: diagonal carry into the next tile (diagonals D and D + 32).
+  float carry0 = 0.f, carry1 = 0.f;
+  // bpermute source of register r: lane (pos5(r, g) - D) mod 32 of this half.
+  const int D = l32;
 
-  for (int qi = a.groups.q_begin[gi]; qi < a.groups.q_begin[gi + 1]; ++qi) {
-    const int h = a.groups.q_head[qi], slot = a.groups.q_slot[qi];
-    f32x16 x[2][2];
-    logits(kf, a.q + ((int64_t)h * a.qm + a.qm - kLastQ) * kD, n, j0w, lane, a.sl2, x);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, x[kt][rt][r]);
-      m = fmaxf(m, __shfl_xor(m, 32));
-      float z = 0.f;
-      if (m != -INFINITY) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) z += exp2f(x[kt][rt][r] - m);
-      }
-      z += __shfl_xor(z, 32);
-      if (g == 0) {
-        red[w][32 * rt + l32][0] = m;
-        red[w][32 * rt + l32][1] = z;
-      }
+  int tau = t0;
+  auto step = [&](auto st_c) -> bool {
+    constexpr int ST = decltype(st_c)::value;
+    if (tau >= t1) return false;
+    // Tile tau has landed once at most the later ops of this wave are in
+    // flight: the loads of the kES-2 tiles after it and, in the scores pass,
+    // two stores per tile scored since tile tau's loads were issued.
+    if (!(kScores && active)) {
+      wait_vm<(kES - 2) * kLoads>();
+    } else {
+      const int k = tau - t0;
+      if (k == 0)
+        wait_vm<(kES - 2) * kLoads>();
+      else if (k == 1)
+        wait_vm<(kES - 2) * kLoads + 2>();
+      else if (k == 2)
+        wait_vm<(kES - 2) * kLoads + 4>();
+      else
+        wait_vm<(kES - 2) * kLoads + 6>();
     }
-    __syncthreads();
-    if (tid < kLastQ) {
-      float m = -INFINITY;
+    barrier_only();
+    issue(est_stage<(ST + kES - 1) % kES>(), tau + kES - 1);
+    const char* st = est_stage<ST>();
+    const bool last = tau == last_tile;
+    if (active) {
+      if constexpr (!kScores) {
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww) m = fmaxf(m, red[ww][tid][0]);
-      float z = 0.f;
+        for (int kt = 0; kt < 2; ++kt) {
+          bf16x8 kf[8];
 #pragma unroll
-      for (int ww = 0; ww < 4; ++ww)
-        if (red[ww][tid][0] != -INFINITY) z += red[ww][tid][1] * exp2f(red[ww][tid][0] - m);
-      float* dst = a.part_mz + (((int64_t)slot * a.ntiles + tile) * kLastQ + tid) * 2;
-      dst[0] = m;
-      dst[1] = z;
-    }
-    __syncthreads();
-  }
-}
-
-__global__ __launch_bounds__(256) void vs_pass2(VsArgs a) {
-  __shared__ float P[kLastQ * kPS];  // probabilities of the tile, [row][key]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int tile = blockIdx.x, gi = blockIdx.y;
-  const int64_t n = a.n;
-  const int j0 = tile * kT, j0w = j0 + 64 * w;
-  bf16x8 kf[2][8];
-  load_k(a.k + (int64_t)a.groups.kv_head[gi] * n * kD, n, j0w, lane, kf);
-
-  for (int qi = a.groups.q_begin[gi]; qi < a.groups.q_begin[gi + 1]; ++qi) {
-    const int h = a.groups.q_head[qi], slot = a.groups.q_slot[qi];
-    f32x16 x[2][2];
-    logits(kf, a.q + ((int64_t)h * a.qm + a.qm - kLastQ) * kD, n, j0w, lane, a.sl2, x);
-    const float* st = a.stats + (int64_t)slot * kLastQ * 2;
+          for (int t = 0; t < 8; ++t) kf[t] = kfrag(st, kt, t);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int rr = 32 * rt + l32;
-      const float M = st[rr * 2], invZ = 1.f / st[rr * 2 + 1];
+          for (int rt = 0; rt < 2; ++rt) {
+            f32x16 acc = f32x16{};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+            for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[rt][t], acc, 0, 0, 0);
+            // acc[r]: key 32kt + pos5(r, g) of the tile, row 32rt + l32.
+            if (last) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = 64 * w + 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-          P[rr * kPS + kl] = exp2f(x[kt][rt][r] - M) * invZ;
+              for (int r = 0; r < 16; ++r)
+                if (32 * kt + pos5(r, g) > 32 * rt + l32) acc[r] = -INFINITY;
+            }
+            float mx = acc[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+            const float mn = fmaxf(m_run[rt], mx * a.sl2);
+            if (mn != -INFINITY) {
+              const float alpha = m_run[rt] == -INFINITY ? 0.f : exp2f(m_run[rt] - mn);
+              float s = 0.f;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) s += exp2f(fmaf(acc[r], a.sl2, -mn));
+              z_run[rt] = fmaf(z_run[rt], alpha, s);
+              m_run[rt] = mn;
+            }
+          }
         }
+      } else {
+        // Diagonal accumulators by 32-block of row - key: -2, -1, 0, 1.
+        float bm2 = 0.f, bm1 = 0.f, b0 = 0.f, b1 = 0.f;
+        float cs[2] = {0.f, 0.f};
+        float pa[16];
+        // One stream of 16 registers whose row - key lies in 32-block base
+        // (lanes whose class D exceeds the register's row position) or in
+        // base + 1 (the rest): move each element to the lane of its class and
+        // add it to its accumulator.
+        auto bin = [&](const float (&x)[16], float& lo, float& hi) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int src = (((pos5(r, g) - D) & 31) | (g << 5)) << 2;
+            const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x[r])));
+            const bool below = D > pos5(r, g);
+            lo += below ? v : 0.f;
+            hi += below ? 0.f : v;
+          }
+        };
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          bf16x8 kf[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) kf[t] = kfrag(st, kt, t);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rt][t], kf[t], acc, 0, 0, 0);
+            // acc[r]: row 32rt + pos5(r, g), key 32kt + l32 of the tile.
+            float p[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4 mq = *reinterpret_cast<const f32x4*>(&e_rows[w][0][32 * rt + pos5(4 * q4, g)]);
+              const f32x4 zq = *reinterpret_cast<const f32x4*>(&e_rows[w][1][32 * rt + pos5(4 * q4, g)]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 4 * q4 + e;
+                p[r] = exp2f(fmaf(acc[r], a.sl2, -mq[e])) * zq[e];
+                if (last && 32 * kt + l32 > 32 * rt + pos5(r, g)) p[r] = 0.f;
+              }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cs[kt] += p[r];
+            // row - key = 32(rt - kt) + pos5 - l32: the streams (rt, kt) =
+            // (0,0) + (1,1), (1,0) and (0,1) lie in 32-blocks {0,-1}, {1,0},
+            // {-1,-2} of row - key.
+            if (rt == 0 && kt == 0) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) pa[r] = p[r];
+            } else if (rt == 1 && kt == 0) {
+              bin(p, b0, b1);
+            } else if (rt == 0 && kt == 1) {
+              bin(p, bm2, bm1);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) pa[r] += p[r];
+              bin(pa, bm1, b0);
+            }
+            // keep the four products apart (registers)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // Half-waves hold the same diagonals for different rows: add them.
+        const float t0s = b0 + __shfl_xor(b0, 32), t1s = b1 + __shfl_xor(b1, 32);
+        const float tm2 = bm2 + __shfl_xor(bm2, 32), tm1 = bm1 + __shfl_xor(bm1, 32);
+        // Diagonals dl = D (half 0) and D + 32 (half 1), dl = row - key,
+        // offset o = n - 64 - 64 tau + dl; the previous tile's carry completes
+        // them unless this is the chunk's first tile.
+        const float out = g ? t1s + carry1 : t0s + carry0;
+        const int64_t o = n - kLastQ - (int64_t)kET * tau + 32 * g + D;
+        if (tau == t0)
+          a.diag_part[((int64_t)slot * a.nchunks + chunk) * 128 + 32 * g + D] = out;
+        else
+          a.s_scores[(int64_t)slot * n + o] = out;
+        carry0 = tm2;
+        carry1 = tm1;
+        // Column sums: half g writes keys 32g + l32 of the tile.
+        const float c0 = cs[0] + __shfl_xor(cs[0], 32), c1 = cs[1] + __shfl_xor(cs[1], 32);
+        a.v_scores[(int64_t)slot * n + (int64_t)kET * tau + 32 * g + l32] = g ? c1 : c0;
+      }
     }
-    __syncthreads();
-    // Column sums: thread t owns key j0 + t (complete within the tile).
-    if (j0 + tid < n) {
-      float v = 0.f;
-      for (int rr = 0; rr < kLastQ; ++rr) v += P[rr * kPS + tid];
-      a.v_scores[(int64_t)slot * n + j0 + tid] = v;
+    ++tau;
+    return true;
+  };
+  while (run_steps<0, kES>(step)) {
+  }
+  wait_vm<0>();
+
+  if (!active) return;
+  if constexpr (!kScores) {
+    // Merge the two half-waves' statistics of each row; half g writes row
+    // 32g + l32.
+    float mo[2], zo[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const float m2 = __shfl_xor(m_run[rt], 32), z2 = __shfl_xor(z_run[rt], 32);
+      const float mn = fmaxf(m_run[rt], m2);
+      float z = 0.f;
+      if (mn != -INFINITY) {
+        const float za = m_run[rt] == -INFINITY ? 0.f : z_run[rt] * exp2f(m_run[rt] - mn);
+        const float zb = m2 == -INFINITY ? 0.f : z2 * exp2f(m2 - mn);
+        z = g ? zb + za : za + zb;  // the same order in both halves
+      }
+      mo[rt] = mn;
+      zo[rt] = z;
     }
-    // Partial diagonal sums: local diagonal od = rr - kl + 255 is the global
-    // offset o = n - 319 - j0 + od.
-    float* dp = a.diag_part + ((int64_t)slot * a.ntiles + tile) * kDiagStride;
-    for (int od = tid; od < kT + kLastQ - 1; od += 256) {
-      float s = 0.f;
-      const int r_lo = max(0, od - (kT - 1)), r_hi = min(kLastQ - 1, od);
-      for (int rr = r_lo; rr <= r_hi; ++rr) s += P[rr * kPS + rr + kT - 1 - od];
-      dp[od] = s;
-    }
-    __syncthreads();
+    float* dst = a.part_mz + (((int64_t)slot * a.nchunks + chunk) * kLastQ + 32 * g + l32) * 2;
+    dst[0] = g ? mo[1] : mo[0];
+    dst[1] = g ? zo[1] : zo[0];
+  } else {
+    // The last tile's negative diagonals: the next chunk's first tile
+    // completes them (nothing follows the sequence's last tile).
+    a.diag_part[((int64_t)slot * a.nchunks + chunk) * 128 + 64 + 32 * g + D] = g ? carry1 : carry0;
   }
 }
 
-// Row statistics of the last 64 rows: merge the per-tile partials (m_t, z_t),
-// m in log2 units, into M = max m_t and Z = sum z_t 2^(m_t - M).  One
-// workgroup per (row, head); thread t merges tiles t, t+256, ... online, then
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void vs_rows(VsArgs a) { est_body<false>(a); }
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void vs_scores(VsArgs a) { est_body<true>(a); }
+
+// Row statistics of the last 64 rows: merge the per-chunk partials (m_c, z_c),
+// m in log2 units, into M = max m_c and Z = sum z_c 2^(m_c - M).  One
+// workgroup per (row, head); thread t merges chunks t, t+256, ... online, then
 // the 256 partials are merged pairwise in a fixed tree order.
 __device__ __forceinline__ void merge_mz(float& m, float& z, float m2, float z2) {
   const float mn = fmaxf(m, m2);
@@ -191,12 +388,12 @@ __device__ __forceinline__ void merge_mz(float& m, float& z, float m2, float z2)
   m = mn;
 }
 
-__global__ __launch_bounds__(256) void vs_stats(const float* part_mz, float* stats, int ntiles) {
+__global__ __launch_bounds__(256) void vs_stats(const float* part_mz, float* stats, int nchunks) {
   __shared__ float sm[256], sz[256];
   const int rr = blockIdx.x, slot = blockIdx.y, tid = threadIdx.x;
-  const float* p = part_mz + (int64_t)slot * ntiles * kLastQ * 2 + rr * 2;
+  const float* p = part_mz + (int64_t)slot * nchunks * kLastQ * 2 + rr * 2;
   float m = -INFINITY, z = 0.f;
-  for (int t = tid; t < ntiles; t += 256) merge_mz(m, z, p[(int64_t)t * kLastQ * 2], p[(int64_t)t * kLastQ * 2 + 1]);
+  for (int t = tid; t < nchunks; t += 256) merge_mz(m, z, p[(int64_t)t * kLastQ * 2], p[(int64_t)t * kLastQ * 2 + 1]);
   sm[tid] = m;
   sz[tid] = z;
   __syncthreads();
@@ -215,35 +412,37 @@ __global__ __launch_bounds__(256) void vs_stats(const float* part_mz, float* sta
   }
 }
 
-__global__ __launch_bounds__(256) void vs_diag(const float* diag_part, float* s_scores, int64_t n, int ntiles) {
-  const int slot = blockIdx.y;
-  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (o >= n) return;
-  // Tile t holds offsets [n - 319 - 256t, n - 1 - 256t].
-  const int64_t span = kT + kLastQ - 1;
-  int64_t t_hi = (n - 1 - o) / kT;
-  if (t_hi > ntiles - 1) t_hi = ntiles - 1;
-  const int64_t num = n - span - o;  // t >= num / 256, rounded up
-  int64_t t_lo = num <= 0 ? 0 : (num + kT - 1) / kT;
-  float s = 0.f;
-  for (int64_t t = t_lo; t <= t_hi; ++t) {
-    const int64_t od = o - (n - span - (int64_t)kT * t);
-    s += diag_part[((int64_t)slot * ntiles + t) * kDiagStride + od];
-  }
-  s_scores[(int64_t)slot * n + o] = s;
+// The 64 diagonals at the start of each chunk: the chunk's first tile holds
+// one part, the previous chunk's last tile the other.
+__global__ __launch_bounds__(64) void vs_diag(const float* diag_part, float* s_scores, int64_t n, int chunk_tiles,
+                                              int nchunks) {
+  const int c = blockIdx.x, slot = blockIdx.y, dl = threadIdx.x;
+  const float* dp = diag_part + (int64_t)slot * nchunks * 128;
+  const float head = dp[(int64_t)c * 128 + dl];
+  const float s = c > 0 ? head + dp[(int64_t)(c - 1) * 128 + 64 + dl] : head;
+  s_scores[(int64_t)slot * n + n - kLastQ - (int64_t)kET * c * chunk_tiles + dl] = s;
 }
 
 }  // namespace
 
+int vs_chunk_tiles(int64_t n, int n_groups) {
+  const int64_t ntiles = n / kET;
+  // About 1024 workgroups (two per CU twice over), at least four tiles each.
+  const int64_t want = (ntiles * n_groups + 1023) / 1024;
+  return (int)std::max<int64_t>(4, std::min<int64_t>(want, ntiles));
+}
+
 hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int64_t qm, float scale_log2,
-                              const VsGroups& groups, int n_vs, float* part_mz, float* stats, float* diag_part,
-                              float* v_scores, float* s_scores, hipStream_t s) {
+                              const VsGroups& groups, int n_vs, int chunk_tiles, float* part_mz, float* stats,
+                              float* diag_part, float* v_scores, float* s_scores, hipStream_t s) {
   VsArgs a;
   a.q = q;
   a.k = k;
   a.n = n;
   a.qm = qm;
-  a.ntiles = (int)((n + kT - 1) / kT);
+  a.ntiles = (int)(n / kET);
+  a.chunk_tiles = chunk_tiles;
+  a.nchunks = (a.ntiles + chunk_tiles - 1) / chunk_tiles;
   a.sl2 = scale_log2;
   a.part_mz = part_mz;
   a.stats = stats;
@@ -251,16 +450,16 @@ hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, i
   a.v_scores = v_scores;
   a.s_scores = s_scores;
   a.groups = groups;
-  const dim3 grid((unsigned)a.ntiles, (unsigned)groups.n_groups);
-  hipLaunchKernelGGL(vs_pass1, grid, dim3(256), 0, s, a);
+  const dim3 grid((unsigned)a.nchunks, (unsigned)groups.n_groups);
+  hipLaunchKernelGGL(vs_rows, grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_stats, dim3((unsigned)kLastQ, (unsigned)n_vs), dim3(256), 0, s, part_mz, stats, a.ntiles);
+  hipLaunchKernelGGL(vs_stats, dim3((unsigned)kLastQ, (unsigned)n_vs), dim3(256), 0, s, part_mz, stats, a.nchunks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_pass2, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(vs_scores, grid, dim3(256), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_diag, dim3((unsigned)((n + 255) / 256), (unsigned)n_vs), dim3(256), 0, s, diag_part,
-                     s_scores, n, a.ntiles);
+  hipLaunchKernelGGL(vs_diag, dim3((unsigned)a.nchunks, (unsigned)n_vs), dim3(64), 0, s, diag_part, s_scores, n,
+                     chunk_tiles, a.nchunks);
   return hipGetLastError();
 }
 
