@@ -224,8 +224,11 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
     barrier_only();
     issue(est_stage<(ST + kES - 1) % kES>(), tau + kES - 1);
     const char* st = est_stage<ST>();
-    const bool last = tau == last_tile;
-    if (active) {
+    // The sequence's last tile is the only one with keys after some of the
+    // rows; the statistics pass takes a copy of its code for it.
+    const bool last_tile_now = tau == last_tile;
+    auto score_tile = [&](auto last_c) {
+      constexpr bool last = decltype(last_c)::value;
       if constexpr (!kScores) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
@@ -238,7 +241,7 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
 #pragma unroll
             for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[rt][t], acc, 0, 0, 0);
             // acc[r]: key 32kt + pos5(r, g) of the tile, row 32rt + l32.
-            if (last) {
+            if constexpr (last) {
 #pragma unroll
               for (int r = 0; r < 16; ++r)
                 if (32 * kt + pos5(r, g) > 32 * rt + l32) acc[r] = -INFINITY;
@@ -248,10 +251,10 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
             const float mn = fmaxf(m_run[rt], mx * a.sl2);
             if (mn != -INFINITY) {
-              const float alpha = m_run[rt] == -INFINITY ? 0.f : exp2f(m_run[rt] - mn);
+              const float alpha = m_run[rt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rt] - mn);
               float s = 0.f;
 #pragma unroll
-              for (int r = 0; r < 16; ++r) s += exp2f(fmaf(acc[r], a.sl2, -mn));
+              for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[r], a.sl2, -mn));
               z_run[rt] = fmaf(z_run[rt], alpha, s);
               m_run[rt] = mn;
             }
@@ -295,9 +298,13 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int r = 4 * q4 + e;
-                p[r] = exp2f(fmaf(acc[r], a.sl2, -mq[e])) * zq[e];
-                if (last && 32 * kt + l32 > 32 * rt + pos5(r, g)) p[r] = 0.f;
+                p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], a.sl2, -mq[e])) * zq[e];
               }
+            }
+            if (last_tile_now) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (32 * kt + l32 > 32 * rt + pos5(r, g)) p[r] = 0.f;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) cs[kt] += p[r];
@@ -337,6 +344,16 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
         // Column sums: half g writes keys 32g + l32 of the tile.
         const float c0 = cs[0] + __shfl_xor(cs[0], 32), c1 = cs[1] + __shfl_xor(cs[1], 32);
         a.v_scores[(int64_t)slot * n + (int64_t)kET * tau + 32 * g + l32] = g ? c1 : c0;
+      }
+    };
+    if (active) {
+      if constexpr (kScores) {
+        score_tile(std::false_type{});
+      } else {
+        if (last_tile_now)
+          score_tile(std::true_type{});
+        else
+          score_tile(std::false_type{});
       }
     }
     ++tau;
