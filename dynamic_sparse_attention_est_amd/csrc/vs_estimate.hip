@@ -264,21 +264,10 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
         // Diagonal accumulators by 32-block of row - key: -2, -1, 0, 1.
         float bm2 = 0.f, bm1 = 0.f, b0 = 0.f, b1 = 0.f;
         float cs[2] = {0.f, 0.f};
-        float pa[16];
-        // One stream of 16 registers whose row - key lies in 32-block base
-        // (lanes whose class D exceeds the register's row position) or in
-        // base + 1 (the rest): move each element to the lane of its class and
-        // add it to its accumulator.
-        auto bin = [&](const float (&x)[16], float& lo, float& hi) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int src = (((pos5(r, g) - D) & 31) | (g << 5)) << 2;
-            const float v = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, x[r])));
-            const bool below = D > pos5(r, g);
-            lo += below ? v : 0.f;
-            hi += below ? 0.f : v;
-          }
-        };
+        // Probabilities by (rt, kt): row - key = 32(rt - kt) + pos5 - l32, so
+        // the streams A = (0,0) + (1,1), B = (1,0) and C = (0,1) lie in
+        // 32-blocks {0,-1}, {1,0} and {-1,-2} of row - key.
+        float pa[16], pb[16], pc[16];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           bf16x8 kf[8];
@@ -307,25 +296,31 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
                 if (32 * kt + l32 > 32 * rt + pos5(r, g)) p[r] = 0.f;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) cs[kt] += p[r];
-            // row - key = 32(rt - kt) + pos5 - l32: the streams (rt, kt) =
-            // (0,0) + (1,1), (1,0) and (0,1) lie in 32-blocks {0,-1}, {1,0},
-            // {-1,-2} of row - key.
-            if (rt == 0 && kt == 0) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) pa[r] = p[r];
-            } else if (rt == 1 && kt == 0) {
-              bin(p, b0, b1);
-            } else if (rt == 0 && kt == 1) {
-              bin(p, bm2, bm1);
-            } else {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) pa[r] += p[r];
-              bin(pa, bm1, b0);
+            for (int r = 0; r < 16; ++r) {
+              cs[kt] += p[r];
+              if (rt == 0 && kt == 0) pa[r] = p[r];
+              if (rt == 1 && kt == 0) pb[r] = p[r];
+              if (rt == 0 && kt == 1) pc[r] = p[r];
+              if (rt == 1 && kt == 1) pa[r] += p[r];
             }
             // keep the four products apart (registers)
             __builtin_amdgcn_sched_barrier(0);
           }
+        }
+        // Register r: lane D of each half fetches the elements of diagonal
+        // class D; where D exceeds the register's row position they lie one
+        // 32-block lower.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int src = (((pos5(r, g) - D) & 31) | (g << 5)) << 2;
+          const float va = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, pa[r])));
+          const float vb = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, pb[r])));
+          const float vc = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, pc[r])));
+          const bool below = D > pos5(r, g);
+          b0 += below ? vb : va;
+          bm1 += below ? va : vc;
+          b1 += below ? 0.f : vb;
+          bm2 += below ? vc : 0.f;
         }
         // Half-waves hold the same diagonals for different rows: add them.
         const float t0s = b0 + __shfl_xor(b0, 32), t1s = b1 + __shfl_xor(b1, 32);
