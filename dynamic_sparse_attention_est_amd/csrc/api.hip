@@ -335,37 +335,57 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     d.col_off = (int64_t)take((size_t)P.cap_c[h] * 4);
     d.run_off = (int64_t)take(q.pattern == MS_VERTICAL_SLASH ? (size_t)(q.n_slash + 1) * 4 : 4);
   }
-  // Heads of one KV head whose key sets are dense enough to overlap heavily
-  // (expected density >= 1/2) are served together, up to hpw per chunk, by the
-  // grouped kernel over the union of their index; the rest one by one.
+  // Heads of one KV head whose key sets overlap heavily are served together,
+  // up to hpw per chunk, by the grouped kernel over the union of their index;
+  // the rest one by one.  Heavy overlap: every head dense enough (expected
+  // density >= 1/2), or heads whose index the parameters alone fix (A-shape,
+  // Grid) with equal parameters, whose union is each one's index.
   P.hpw = hpw_of(P.grp);
   P.gdesc.clear();
   P.solo.clear();
-  for (int kv = 0; kv < P.hkv; ++kv) {
-    std::vector<int> dense_heads;
-    for (int j = 0; j < P.grp; ++j) {
-      const int h = kv * P.grp + j;
-      if (P.hpw > 1 && expected_density(P.p[h], P.n) >= 0.5)
-        dense_heads.push_back(h);
-      else
-        P.solo.push_back((int16_t)h);
-    }
-    for (size_t c = 0; c < dense_heads.size();) {
-      size_t m = std::min<size_t>(P.hpw, dense_heads.size() - c);
+  auto emit_chunks = [&](int kv, const std::vector<int>& heads) {
+    for (size_t c = 0; c < heads.size();) {
+      size_t m = std::min<size_t>(P.hpw, heads.size() - c);
       // A four-head workgroup costs about the same per piece however many of
       // its heads are present, so three heads run as a chunk of two and a
       // head alone.
       if (m == 3) m = 2;
       if (m < 2) {
-        P.solo.push_back((int16_t)dense_heads[c++]);
+        P.solo.push_back((int16_t)heads[c++]);
         continue;
       }
       GroupDesc g{};
       g.kvh = kv;
       g.nheads = (int)m;
-      for (size_t j = 0; j < m; ++j) g.head[j] = (int16_t)dense_heads[c + j];
+      for (size_t j = 0; j < m; ++j) g.head[j] = (int16_t)heads[c + j];
       P.gdesc.push_back(g);
       c += m;
+    }
+  };
+  auto static_key = [&](const ms_head_params& q) {
+    return std::make_tuple(q.pattern, q.sink, q.window, q.grid_stride, q.grid_frames, q.grid_width);
+  };
+  for (int kv = 0; kv < P.hkv; ++kv) {
+    std::vector<int> dense_heads, fixed_heads;
+    for (int j = 0; j < P.grp; ++j) {
+      const int h = kv * P.grp + j;
+      const int pat = P.p[h].pattern;
+      if (P.hpw > 1 && expected_density(P.p[h], P.n) >= 0.5)
+        dense_heads.push_back(h);
+      else if (P.hpw > 1 && (pat == MS_A_SHAPE || pat == MS_GRID))
+        fixed_heads.push_back(h);
+      else
+        P.solo.push_back((int16_t)h);
+    }
+    emit_chunks(kv, dense_heads);
+    // fixed-index heads with equal parameters, in head order within a set
+    std::stable_sort(fixed_heads.begin(), fixed_heads.end(),
+                     [&](int x, int y) { return static_key(P.p[x]) < static_key(P.p[y]); });
+    for (size_t i = 0; i < fixed_heads.size();) {
+      size_t e = i + 1;
+      while (e < fixed_heads.size() && static_key(P.p[fixed_heads[e]]) == static_key(P.p[fixed_heads[i]])) ++e;
+      emit_chunks(kv, std::vector<int>(fixed_heads.begin() + i, fixed_heads.begin() + e));
+      i = e;
     }
   }
   // With four heads per workgroup, chunks of two go to the two-head kernel

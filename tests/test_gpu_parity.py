@@ -350,6 +350,18 @@ def test_attention_chunks_of_two_three_and_four_heads():
     _attention_check(run_staged(make(w)))
 
 
+def test_attention_fixed_index_heads_with_equal_parameters_grouped():
+    """A-shape and Grid heads of one KV head with equal parameters share one
+    index and are served together (a chunk of four, a chunk of two); those
+    with parameters of their own are served one by one."""
+    n = 64 * 40
+    a, a2 = W.ashape(32, 300), W.ashape(16, 200)
+    gr, gr2 = W.grid(300, 3, 8, 64), W.grid(250, 2, 4, 96)
+    heads = [a, a, a, a,  a, a2, gr, gr,  gr2, a2, gr, a]
+    w = W.custom("fixed", n, 12, 3, heads, recipe="vs_planted", seed=31)
+    _attention_check(run_staged(make(w)))
+
+
 def test_one_shot_equals_staged_and_is_deterministic():
     n = 1024
     heads = [W.vs(48, 80), W.bs(6), W.ashape(40, 150), W.vs(100, 30)]
