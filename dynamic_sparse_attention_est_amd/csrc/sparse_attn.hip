@@ -579,47 +579,70 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // Combination of a (head, block)'s segment records (O_s / l_s and lse_s per
 // row): with M the largest lse_s of a row and c_s = e^(lse_s - M), out =
 // sum_s c_s (O_s / l_s) / sum_s c_s and lse = M + ln(sum_s c_s), summed in
-// segment order.  Thread t takes half a row: row t / 2, columns 64 (t % 2)
-// onward.
-__global__ __launch_bounds__(kThreads) void seg_combine(AttnArgs a) {
+// segment order.  Threads 0..63 turn each row's lse_s into the weights c_s
+// (LDS, [segment][row], up to 64 segments at a time); every thread then
+// accumulates 16-byte pieces q = 256 j + t of the records (row q / 32), so
+// each load instruction of a wave reads 1 KiB of contiguous memory.
+constexpr int kCombThreads = 256;
+constexpr int kCombSegs = 64;  // segments whose weights LDS holds at once
+__global__ __launch_bounds__(kCombThreads) void seg_combine(AttnArgs a) {
+  __shared__ float cw[kCombSegs][kBM];
+  __shared__ float inv[kBM];
   const int t = threadIdx.x;
-  const int rr = t >> 1, c0 = 64 * (t & 1);
   const int bl = blockIdx.x / a.n_list, hi = blockIdx.x - bl * a.n_list;
   const int b = a.seg_b0 + a.seg_nb - 1 - bl;  // the call's query block
   const int h = a.list[hi];
   const int row0 = (a.qb0 + b) * kBM;           // its first query row in the sequence
   const int ns = ((row0 + kBM - 1) >> a.seg_shift) + 1;
   const float* rec0 = a.part + (int64_t)(bl * a.n_list + hi) * a.seg_n * kSegRecFloats;
-  float mx = -INFINITY;
-  for (int sg = 0; sg < ns; ++sg) mx = fmaxf(mx, rec0[(int64_t)sg * kSegRecFloats + kSegRowFloats + rr]);
-  f32x4 acc[16];
+  const int64_t orow0 = (int64_t)h * a.qm + (int64_t)b * kBM;  // first row of out and lse
+  float mx = -INFINITY, den = 0.f;
+  if (t < kBM)
+    for (int sg = 0; sg < ns; ++sg) mx = fmaxf(mx, rec0[(int64_t)sg * kSegRecFloats + kSegRowFloats + t]);
+  constexpr int kPer = kSegRowFloats / 4 / kCombThreads;  // 16-byte pieces per thread
+  f32x4 acc[kPer];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = f32x4{};
-  float den = 0.f;
-  for (int sg = 0; sg < ns; ++sg) {
-    const float* rec = rec0 + (int64_t)sg * kSegRecFloats;
-    const float ls = rec[kSegRowFloats + rr];
-    const float c = ls == -INFINITY ? 0.f : expf(ls - mx);
-    den += c;
-    const f32x4* src = reinterpret_cast<const f32x4*>(rec + rr * kD + c0);
+  for (int j = 0; j < kPer; ++j) acc[j] = f32x4{};
+  for (int s0 = 0; s0 < ns; s0 += kCombSegs) {
+    const int s1 = min(ns, s0 + kCombSegs);
+    if (t < kBM) {
+      for (int sg = s0; sg < s1; ++sg) {
+        const float ls = rec0[(int64_t)sg * kSegRecFloats + kSegRowFloats + t];
+        const float c = ls == -INFINITY ? 0.f : expf(ls - mx);
+        cw[sg - s0][t] = c;
+        den += c;
+      }
+    }
+    __syncthreads();
+    for (int sg = s0; sg < s1; ++sg) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(rec0 + (int64_t)sg * kSegRecFloats);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] += c * src[j];
+      for (int j = 0; j < kPer; ++j) {
+        const int q = kCombThreads * j + t;
+        acc[j] += cw[sg - s0][q >> 5] * src[q];
+      }
+    }
+    __syncthreads();
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const int64_t orow = (int64_t)h * a.qm + (int64_t)b * kBM + rr;  // row of out and lse
-  const int64_t obase = orow * kD + c0;
+  if (t < kBM) {
+    inv[t] = den > 0.f ? 1.f / den : 0.f;
+    if (a.lse) a.lse[orow0 + t] = den > 0.f ? mx + logf(den) : -INFINITY;
+  }
+  __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const f32x4 x = acc[j] * inv;
+  for (int j = 0; j < kPer; ++j) {
+    const int q = kCombThreads * j + t;
+    const int rr = q >> 5;
+    const f32x4 x = acc[j] * inv[rr];
+    const int64_t o = (orow0 + rr) * kD + 4 * (q & 31);
     if (a.out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + 4 * j) = x;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = x;
     } else {
       typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       const bf16x4 y = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(a.out) + obase + 4 * j) = y;
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(a.out) + o) = y;
     }
   }
-  if (a.lse && (t & 1) == 0) a.lse[orow] = den > 0.f ? mx + logf(den) : -INFINITY;
 }
 
 __global__ __launch_bounds__(256) void v_to_f16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -661,7 +684,7 @@ hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(sparse_attn_seg, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seg_combine, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(seg_combine, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 
