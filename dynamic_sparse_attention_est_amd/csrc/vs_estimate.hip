@@ -439,9 +439,10 @@ __global__ __launch_bounds__(64) void vs_diag(const float* diag_part, float* s_s
 
 int vs_chunk_tiles(int64_t n, int n_groups) {
   const int64_t ntiles = n / kET;
-  // About 1024 workgroups (two per CU twice over), at least four tiles each.
+  // About 1024 workgroups (two per CU twice over); short sequences get one
+  // tile per workgroup.
   const int64_t want = (ntiles * n_groups + 1023) / 1024;
-  return (int)std::max<int64_t>(4, std::min<int64_t>(want, ntiles));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, ntiles));
 }
 
 hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int64_t n, int64_t qm, float scale_log2,
