@@ -79,7 +79,9 @@ def test_topk_hook_continuous_scores():
 
 
 # ---------------------------------------------------------------- Vertical-Slash estimation
-@pytest.mark.parametrize("n,hq,hkv", [(1024, 4, 2), (832, 2, 1), (2048, 1, 1)])
+# (8, 1) and (6, 1): more than four VS heads share a KV head, so the estimator
+# splits them into groups of at most four
+@pytest.mark.parametrize("n,hq,hkv", [(1024, 4, 2), (832, 2, 1), (2048, 1, 1), (1280, 8, 1), (1536, 6, 1)])
 def test_vs_estimation(n, hq, hkv):
     w = W.custom("vs_small", n, hq, hkv, [W.vs(64, 96)] * hq, recipe="vs_planted", n_planted=6, seed=n)
     st = run_staged(make(w))
@@ -347,6 +349,17 @@ def test_attention_chunks_of_two_three_and_four_heads():
     d, sp = W.vs(200, 90), W.bs(2)
     heads = [d, d, sp, sp,  d, d, d, sp,  d, d, d, d,  sp, d, sp, d]
     w = W.custom("chunks", n, 16, 4, heads, recipe="vs_planted", seed=24)
+    _attention_check(run_staged(make(w)))
+
+
+def test_attention_eight_heads_per_kv_head():
+    """Eight Q heads on one KV head: six dense heads form a chunk of four and a
+    chunk of two, two sparse heads run alone; estimation splits the VS heads
+    into groups of at most four."""
+    n = 64 * 24
+    d, sp = W.vs(200, 90), W.bs(2)
+    heads = [d, sp, d, d, d, sp, d, d]
+    w = W.custom("eight", n, 8, 1, heads, recipe="vs_planted", seed=8)
     _attention_check(run_staged(make(w)))
 
 
