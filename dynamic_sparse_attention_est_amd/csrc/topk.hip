@@ -264,6 +264,9 @@ size_t topk_scratch_bytes(int64_t n, int problems) {
 hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, void* scratch,
                                hipStream_t s) {
   if (jobs.count <= 0) return hipSuccess;
+  // Short vectors: one workgroup per vector runs every pass in one launch
+  // (the same selection; launch latency dominates at these sizes).
+  if (n <= 2 * kChunk) return launch_topk_rows(src, n, jobs, dst, s);
   const int nchunks = (int)((n + kChunk - 1) / kChunk);
   char* w = static_cast<char*>(scratch);
   TopkState* st = reinterpret_cast<TopkState*>(w);
