@@ -103,17 +103,50 @@ struct BsSelArgs {
   int64_t dst_off[kMaxHeads];
 };
 
+// Rows of up to kRankMax candidates rank every candidate directly: with
+// key_j = (order key of score j, ~j) as one 64-bit value, candidate i is kept
+// iff fewer than min(k, b+1) keys exceed key_i (larger score, or equal score
+// and lower index); the kept ones are compacted in index order.
+constexpr int kRankMax = 512;  // (b+1)^2 comparisons per row: short rows only
+
 __global__ __launch_bounds__(kSelThreads) void bs_select(const float* scores, int nb, int nbq, int qb0,
                                                          BsSelArgs sa, int32_t* blocks) {
   __shared__ TopkSmem<kSelThreads> sm;
+  __shared__ uint64_t kv[kRankMax];
+  const int t = threadIdx.x;
   const int bl = blockIdx.x, slot = blockIdx.y;
   const int b = qb0 + bl;
   const int k = sa.k[slot];
   int32_t* row = blocks + sa.dst_off[slot] + (int64_t)bl * k;
   const float* x = scores + ((int64_t)slot * nbq + bl) * nb;
-  const int cnt = min(k, b + 1);
-  block_topk<kSelThreads>(x, b + 1, k, row, sm);
-  for (int i = cnt + threadIdx.x; i < k; i += kSelThreads) row[i] = -1;
+  const int m = b + 1;  // candidate key blocks 0..b
+  const int cnt = min(k, m);
+  if (cnt == m) {
+    for (int i = t; i < m; i += kSelThreads) row[i] = i;
+  } else if (m <= kRankMax) {
+    for (int i = t; i < m; i += kSelThreads)
+      kv[i] = ((uint64_t)order_key(x[i]) << 32) | (uint64_t)(~(uint32_t)i);
+    __syncthreads();
+    int base = 0;
+    for (int r0 = 0; r0 < m; r0 += kSelThreads) {
+      const int i = r0 + t;
+      int sel = 0;
+      if (i < m) {
+        const uint64_t me = kv[i];
+        int above = 0;
+#pragma unroll 8
+        for (int j = 0; j < m; ++j) above += kv[j] > me;
+        sel = above < cnt;
+      }
+      int total;
+      const int pos = base + block_excl_scan<kSelThreads>(sel, sm.warp_sum, &total);
+      if (sel) row[pos] = i;
+      base += total;
+    }
+  } else {
+    block_topk<kSelThreads>(x, m, k, row, sm);
+  }
+  for (int i = cnt + t; i < k; i += kSelThreads) row[i] = -1;
 }
 
 // ---------------------------------------------------------------------------
