@@ -588,6 +588,8 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
     if (count == 0 || !active) return 0u;
     const int e = start + count;
     while (hhi <= start) head_advance();
+    // the usual case for heads that keep most keys: one range covers the piece
+    if (hlo <= start && hhi >= e) return count >= 32 ? 0xffffffffu : (1u << count) - 1u;
     uint32_t bits = 0u;
     while (hlo < e) {
       const int lo = max(hlo, start) - start, w = min(hhi, e) - start - lo;
