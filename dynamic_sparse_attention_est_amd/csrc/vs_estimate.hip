@@ -207,7 +207,9 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
     if (tau >= t1) return false;
     // Tile tau has landed once at most the later ops of this wave are in
     // flight: the loads of the kES-2 tiles after it and, in the scores pass,
-    // two stores per tile scored since tile tau's loads were issued.
+    // two stores per tile scored since tile tau's loads were issued (gfx9
+    // counts a wave's vector loads and stores in one counter that drains in
+    // issue order).
     if (!(kScores && active)) {
       wait_vm<(kES - 2) * kLoads>();
     } else {
