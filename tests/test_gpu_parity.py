@@ -343,8 +343,8 @@ def test_attention_grouped_union(hq, hkv, seed):
 
 def test_attention_chunks_of_two_three_and_four_heads():
     """Four Q heads per KV head: KV heads with two, three and four dense heads
-    form chunks of two (served two heads per workgroup), three (one idle
-    slot) and four, beside sparse heads served one by one."""
+    form a chunk of two (served two heads per workgroup), a chunk of two plus
+    a head alone, and a chunk of four, beside sparse heads served one by one."""
     n = 64 * 24
     d, sp = W.vs(200, 90), W.bs(2)
     heads = [d, d, sp, sp,  d, d, d, sp,  d, d, d, d,  sp, d, sp, d]
