@@ -247,6 +247,23 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
     t_wall = time.perf_counter() - t_wall
     ms_step = e0.elapsed_time(e1) / steps
 
+    # Short sequences are bound by launch latency (about 20 kernels per
+    # call): the same call captured once in a HIP graph and replayed.
+    graph_ms = None
+    if w.n <= 32768:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            ms.ms_sparse_attn(prob, hp, q, k, v, out, ws)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(max(steps, 10)):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / max(steps, 10)
+        del g
+
     # Stage split: the attention kernel alone (index already built by the
     # steps above) and estimation + index conversion.
     nv, ns, nbk = ms.ms_selection_sizes(prob, hp)
@@ -282,7 +299,7 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
     dense_pairs = w.n * (w.n + 1) // 2 * w.n_q_heads
     del index
     res = {"w": w, "q": q, "k": k, "v": v, "ms": ms_step, "wall_s": t_wall, "t_est": t_est, "t_idx": t_idx,
-           "t_att": t_att, "kept": kept, "block_keys": bkeys, "dense_pairs": dense_pairs}
+           "t_att": t_att, "kept": kept, "block_keys": bkeys, "dense_pairs": dense_pairs, "graph_ms": graph_ms}
     del ws
     if do_dense:
         dout = torch.empty_like(q)
@@ -322,6 +339,8 @@ def summary(r):
         "attention_mfma_frac": round(att_tflops / PEAK_BF16_TFLOPS, 4),
         "effective_tflops": round(kept_tf / (r["ms"] / 1e3), 1),
     }
+    if r.get("graph_ms") is not None:
+        s["graph_replay_ms_per_layer"] = round(r["graph_ms"], 3)
     # K/V bytes as the per-head kernel loads them (512 B per kept (query
     # block, key) pair).  Heads served together by the grouped kernel share
     # their loads, so for them this is an upper bound on what is read.
