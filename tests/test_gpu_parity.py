@@ -99,6 +99,25 @@ def test_vs_estimation(n, hq, hkv):
         _near_tie_ok(gs, oracle.topk(s_ref, 96), s_ref, ds[h], 96)
 
 
+@pytest.mark.parametrize("n,hq", [(64, 1), (128, 2), (192, 1)])
+def test_vs_estimation_one_to_three_tiles(n, hq):
+    """Sequences of one to three 64-key tiles: the last tile (the only one with
+    keys after some scored rows) is also the first of its chunk."""
+    w = W.custom("vs_tiny", n, hq, 1, [W.vs(16, 24)] * hq, recipe="vs_planted", n_planted=2, seed=n)
+    st = run_staged(make(w))
+    q, k, _ = _host(st)
+    sel = selections(st)
+    dv, ds = st.dbg_v.cpu().numpy().astype(np.float64), st.dbg_s.cpu().numpy().astype(np.float64)
+    for h in range(hq):
+        v_ref, s_ref = oracle.vs_scores(q[h, n - 64:], k[0])
+        _score_check(dv[h], v_ref, f"head {h} vertical scores")
+        _score_check(ds[h], s_ref, f"head {h} slash scores")
+        _, gv, gs = sel[h]
+        np.testing.assert_array_equal(gv, oracle.topk(dv[h], 16))
+        np.testing.assert_array_equal(gs, oracle.topk(ds[h], 24))
+    _attention_check(st)
+
+
 def test_vs_estimation_zero_query_closed_form():
     # q = 0: p_ij = 1/(i+1); the scores are harmonic partial sums.
     n = 512
