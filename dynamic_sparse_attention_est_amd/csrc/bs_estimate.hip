@@ -60,11 +60,14 @@ struct ScoreArgs {
 };
 
 constexpr int kST = 64;      // score tile
-constexpr int kSP = kD + 1;  // LDS row stride (floats)
+constexpr int kTP = kST + 4; // LDS stride of a transposed tile (floats; rows stay 16-byte aligned)
 
+// Tiles are held transposed in LDS ([d][block]), so a thread's four query
+// blocks (or four key blocks) at one d are one 16-byte read: two reads per 16
+// FMAs.  Each sum runs over d in order.
 __global__ __launch_bounds__(256) void bs_scores(ScoreArgs a) {
-  __shared__ float qs[kST * kSP];
-  __shared__ float ks[kST * kSP];
+  __shared__ __attribute__((aligned(16))) float qs[kD * kTP];
+  __shared__ __attribute__((aligned(16))) float ks[kD * kTP];
   const int ct = blockIdx.x, bt = blockIdx.y, slot = blockIdx.z, tid = threadIdx.x;
   const int nb = a.nb, nbq = a.nbq;
   const int tx = tid & 15, ty = tid >> 4;
@@ -81,18 +84,14 @@ __global__ __launch_bounds__(256) void bs_scores(ScoreArgs a) {
   const float* kp = a.kpool + (int64_t)a.kv_slot[slot] * nb * kD;
   for (int i = tid; i < kST * kD; i += 256) {
     const int r = i / kD, d = i % kD;
-    qs[r * kSP + d] = b0 + r < nbq ? qp[(int64_t)(b0 + r) * kD + d] : 0.f;
-    ks[r * kSP + d] = c0 + r < nb ? kp[(int64_t)(c0 + r) * kD + d] : 0.f;
+    qs[d * kTP + r] = b0 + r < nbq ? qp[(int64_t)(b0 + r) * kD + d] : 0.f;
+    ks[d * kTP + r] = c0 + r < nb ? kp[(int64_t)(c0 + r) * kD + d] : 0.f;
   }
   __syncthreads();
   float acc[4][4] = {};
   for (int d = 0; d < kD; ++d) {
-    float qv[4], kv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qv[i] = qs[(4 * ty + i) * kSP + d];
-      kv[i] = ks[(4 * tx + i) * kSP + d];
-    }
+    const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[d * kTP + 4 * ty]);
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(&ks[d * kTP + 4 * tx]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
