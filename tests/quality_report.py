@@ -1,4 +1,4 @@
-"""Index-quality report on the synthetic workloads (run on a GPU machine:
+"""Index-quality report on the synthetic workloads (needs a GPU:
 ``python tests/quality_report.py [workload ...]``).
 
 For each workload: the layer's estimated index is built on the GPU, the
