@@ -216,3 +216,42 @@ def test_union_of_many_columns_per_block():
             np.testing.assert_array_equal(per_head[h][b][1], ref_b[1])
             ro, rl = oracle.attention_block(q[h, 64 * b:64 * b + 64], k, v, ref_b, b)
             check_attention(f64(st.out[h, 64 * b:64 * b + 64]), ro, f"head {h} block {b}")
+
+
+def test_longest_sequence():
+    """The longest sequence a call accepts (2^23 keys): byte offsets of K/V rows
+    reach 2^31, the CSR spans 131072 query blocks.  Selections against the
+    GPU's own scores, and the index and attention of sampled query blocks
+    (the first, the last and random ones) against the oracle."""
+    n = 1 << 23
+    heads = [W.vs(16, 32), W.ashape(128, 1024)]
+    w = W.custom("longest", n, 2, 1, heads, recipe="vs_planted", n_planted=2, seed=23)
+    print(f"[longest] n={n}", flush=True)
+    st = run_staged(make(w), debug=True)
+    sel = selections(st)
+    dv = st.dbg_v[0].cpu().numpy().astype(np.float64)
+    ds = st.dbg_s[0].cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(sel[0][1], oracle.topk(dv, 16))
+    np.testing.assert_array_equal(sel[0][2], oracle.topk(ds, 32))
+    del dv, ds
+    # K and V rows as float32 (exact for bf16); the oracle upcasts per block
+    k32 = st.k[0].float().cpu().numpy()
+    v32 = st.v[0].float().cpu().numpy()
+    for h, p in enumerate(heads):
+        blocks = sample_blocks(w.nb, 6, 23 + h)
+        got_idx = read_index_blocks(st.prob, st.hp, st.index, h, blocks)
+        for b in blocks:
+            if p.pattern == W.VERTICAL_SLASH:
+                ref_b = oracle.vs_block_index(sel[h][1], sel[h][2], b)
+            else:
+                ref_b = oracle.ashape_block_index(p.sink, p.window, b)
+            np.testing.assert_array_equal(got_idx[b][0], ref_b[0], err_msg=f"head {h} block {b} ranges")
+            np.testing.assert_array_equal(got_idx[b][1], ref_b[1], err_msg=f"head {h} block {b} cols")
+            rows = slice(64 * b, 64 * b + 64)
+            ro, rl = oracle.attention_block(f64(st.q[h, rows]), k32, v32, ref_b, b, ashape=ashape_of(p))
+            check_attention(f64(st.out[h, rows]), ro, f"head {h} block {b}")
+            got_l = st.lse[h, rows].cpu().numpy().astype(np.float64)
+            fin = np.isfinite(rl)
+            assert np.all(np.isneginf(got_l[~fin]))
+            np.testing.assert_allclose(got_l[fin], rl[fin], rtol=0, atol=LSE_ATOL)
+        print(f"  head {h}: {len(blocks)} blocks ok", flush=True)
