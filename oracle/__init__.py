@@ -43,10 +43,11 @@ function (readings R1..R13 of the design notes):
 Every array is numpy float64 (scores, attention) or int64/int32 (indices).
 Inputs arrive as bfloat16 values widened exactly to float64 by the caller.
 
-Pins: every function here is checked in tests/test_oracle_*.py against
+Pins: every function here is checked in tests/test_oracle.py against
 closed forms, brute force on tiny inputs, library routines (numpy's trace,
 torch's scaled-dot-product attention) and hand-worked fixtures in
-tests/golden/.
+tests/golden/; the per-head dispatch (estimate_head, head_index) is checked
+by pushing those fixtures and constructions through it for every pattern.
 """
 from .core import (  # noqa: F401
     BM,

@@ -489,3 +489,136 @@ def test_grid_mask_elementwise(params):
             for j in range(i + 1):
                 ref[r, j] = any(64 * b - o <= j <= 64 * b + 63 - o for o in offs)
         np.testing.assert_array_equal(got, ref)
+
+
+# ------------------------------------------------------------ per-head dispatch
+# head_index and estimate_head route one head's pattern and parameters to the
+# per-pattern functions pinned above; these tests push the hand-worked fixtures
+# and constructions through the dispatch itself, so a swapped argument or a
+# wrong branch there fails here.
+def _assert_index(got, blocks, b0=0):
+    for blk in blocks:
+        b = blk["b"]
+        if b < b0:
+            continue
+        r, c = got[b - b0]
+        assert r.tolist() == blk["ranges"], blk
+        assert c.tolist() == blk.get("cols", []), blk
+
+
+@pytest.mark.parametrize("q_block0", [0, 3])
+def test_head_index_vertical_slash_golden(q_block0):
+    g = json.load(open(os.path.join(GOLDEN, "vs_index_n512.json")))
+    p = W.vs(len(g["vertical"]), len(g["slash"]))
+    sel = ("vs", np.array(g["vertical"]), np.array(g["slash"]))
+    got = oracle.head_index(p, sel, g["n"], q_block0=q_block0)
+    assert len(got) == g["n"] // BM - q_block0
+    _assert_index(got, g["blocks"], q_block0)
+
+
+@pytest.mark.parametrize("q_block0", [0, 2])
+def test_head_index_ashape_golden(q_block0):
+    g = json.load(open(os.path.join(GOLDEN, "ashape_index_n512.json")))
+    got = oracle.head_index(W.ashape(g["sink"], g["window"]), ("static",), g["n"], q_block0=q_block0)
+    assert len(got) == g["n"] // BM - q_block0
+    _assert_index(got, g["blocks"], q_block0)
+
+
+def test_head_index_grid_hand_worked():
+    # The cases worked by hand in test_grid_index_hand_worked, through the
+    # dispatch: P = 100, T = 2, w = 2, window = 10, and P = 50, T = 2, w = 10,
+    # window = 20.
+    n = 64 * 8
+    got = oracle.head_index(W.grid(100, 2, 2, 10), ("static",), n)
+    assert got[3][0].tolist() == [[0, 58], [90, 158], [183, 256]]
+    assert got[1][0].tolist() == [[0, 30], [55, 128]]
+    assert all(c.size == 0 for _, c in got)
+    got = oracle.head_index(W.grid(50, 2, 10, 20), ("static",), n)
+    assert got[2][0].tolist() == [[18, 192]]
+    got = oracle.head_index(W.grid(100, 2, 2, 10), ("static",), n, q_block0=3)
+    assert got[0][0].tolist() == [[0, 58], [90, 158], [183, 256]]
+
+
+def test_head_index_block_sparse_hand_worked():
+    # Selections of test_bs_integer_construction_hand_worked: block c keeps
+    # keys [64c, 64c + 64); consecutive blocks merge.
+    sel = [np.array(s) for s in ([0], [0, 1], [0, 2], [1, 3], [0, 1], [1, 5])]
+    got = oracle.head_index(W.bs(2), ("bs", sel), 6 * BM)
+    assert [r.tolist() for r, _ in got] == [[[0, 64]], [[0, 128]], [[0, 64], [128, 192]], [[64, 128], [192, 256]],
+                                            [[0, 128]], [[64, 128], [320, 384]]]
+    assert all(c.size == 0 for _, c in got)
+
+
+@pytest.mark.parametrize("q_block0", [0, 5])
+def test_head_index_dense(q_block0):
+    n = 64 * 7
+    got = oracle.head_index(W.dense(), ("static",), n, q_block0=q_block0)
+    assert [r.tolist() for r, _ in got] == [[[0, 64 * b + 64]] for b in range(q_block0, 7)]
+    assert all(c.size == 0 for _, c in got)
+
+
+def _one_hot_rows(n, plants, lam=30.0, d=128, seed=60):
+    """Zero queries except row i = lam * e_t for each plant (i, j, t); key j =
+    lam * e_t; every other key is random in the span of e_8 .. e_127, so it is
+    orthogonal to every planted query and its logits are exactly 0."""
+    r = rng(seed)
+    q = np.zeros((n, d))
+    k = np.zeros((n, d))
+    k[:, 8:] = r.standard_normal((n, d - 8))
+    for i, j, t in plants:
+        q[i, t] = lam
+        k[j] = 0.0
+        k[j, t] = lam
+    return q, k
+
+
+def test_estimate_head_scores_exactly_the_last_64_rows():
+    # Rows n-64 and n-1 each see one planted key strongly; row n-65 (outside
+    # the last 64) sees a third.  Every other logit is 0, so the remaining
+    # vertical scores tie and the lowest index fills the budget.  Scoring rows
+    # n-64..n-1 gives verticals {0, 100, 300} and slashes {(n-1) - 300,
+    # (n-64) - 100}; one row fewer at either end or one more changes them.
+    n = 512
+    q, k = _one_hot_rows(n, [(n - 64, 100, 0), (n - 1, 300, 1), (n - 65, 200, 2)])
+    sel = oracle.estimate_head(W.vs(3, 2), q, k)
+    assert sel[0] == "vs"
+    assert sel[1].tolist() == [0, 100, 300]
+    assert sel[2].tolist() == [(n - 1) - 300, (n - 64) - 100]
+    # the same through a chunk whose query rows start at block 5
+    sel_c = oracle.estimate_head(W.vs(3, 2), q[5 * BM:], k, q_block0=5)
+    assert sel_c[1].tolist() == [0, 100, 300]
+    assert sel_c[2].tolist() == [(n - 1) - 300, (n - 64) - 100]
+
+
+def test_estimate_head_zero_query_scores_closed_form():
+    # q = 0 on the last 64 rows: v_j = sum over rows i >= max(j, n-64) of
+    # 1/(i+1) ties for every j < n - 64, so the top k verticals are 0..k-1;
+    # a key planted for row n-64 only breaks that tie (row n-64 is scored).
+    n = 448
+    q, k = _one_hot_rows(n, [(n - 64, 250, 3)], lam=0.0)
+    sel = oracle.estimate_head(W.vs(4, 3), q, k)
+    assert sel[1].tolist() == [0, 1, 2, 3]
+    # s_o = sum over rows i >= max(o, n-64) of 1/(i+1) ties for o <= n - 64
+    assert sel[2].tolist() == [0, 1, 2]
+    q, k = _one_hot_rows(n, [(n - 64, 250, 3)])
+    sel = oracle.estimate_head(W.vs(4, 3), q, k)
+    assert sel[1].tolist() == [0, 1, 2, 250]
+    assert (n - 64) - 250 in sel[2].tolist()
+
+
+def test_estimate_head_block_sparse_integer_construction():
+    # The integer construction of test_bs_integer_construction_hand_worked,
+    # through the dispatch, whole and as a chunk from query block 3.
+    qa = [1, 2, -1, 2, 0, 3]
+    q, k = _integer_blocks(qa), _integer_blocks(qa)
+    sel = oracle.estimate_head(W.bs(2), q, k)
+    assert sel[0] == "bs"
+    assert [s.tolist() for s in sel[1]] == [[0], [0, 1], [0, 2], [1, 3], [0, 1], [1, 5]]
+    sel = oracle.estimate_head(W.bs(2), q[3 * BM:], k, q_block0=3)
+    assert [s.tolist() for s in sel[1]] == [[1, 3], [0, 1], [1, 5]]
+
+
+def test_estimate_head_static_patterns_select_nothing():
+    q = np.zeros((128, 128))
+    for p in (W.ashape(4, 8), W.dense(), W.grid(10, 1, 0, 4)):
+        assert oracle.estimate_head(p, q, q) == ("static",)
