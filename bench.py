@@ -100,7 +100,7 @@ def block_keys(ms, prob, hp, index, torch):
     offs, _ = ms.ms_index_layout(prob, hp)
     nb = prob.n // 64
     base = index.view(torch.int32)
-    total = 0
+    total = cols = 0
     for (o_rp, o_r, o_cp, o_c) in offs:
         nr = int(base[o_rp // 4 + nb])
         nc = int(base[o_cp // 4 + nb])
@@ -108,43 +108,36 @@ def block_keys(ms, prob, hp, index, torch):
             rng = base[o_r // 4:o_r // 4 + 2 * nr].long().view(-1, 2)
             total += int((rng[:, 1] - rng[:, 0]).clamp(min=0).sum())
         total += nc
-    return total
+        cols += nc
+    return total, cols
 
 
-def estimate_bytes(w):
-    """Algorithmic HBM bytes of the estimation stage: Vertical-Slash reads K of
-    each KV head it serves twice (softmax statistics, then scores) plus the last
-    64 query rows, and writes and re-reads two fp32 score vectors per head;
-    Block-Sparse pools Q of its heads and K of their KV heads once."""
-    vs = [h for h, p in enumerate(w.heads) if p.pattern == 1]
-    bs = [h for h, p in enumerate(w.heads) if p.pattern == 2]
-    row = 128 * 2
-    b = 0
-    if vs:
-        b += 2 * len({h // w.group for h in vs}) * w.n * row + len(vs) * 64 * row + 2 * 2 * len(vs) * w.n * 4
-    if bs:
-        b += (len(bs) + len({h // w.group for h in bs})) * w.n * row
-    return b
-
-
-def recorded_traffic(workload, srcs):
-    """HBM bytes of one attention call on `workload` from the committed
-    rocprofv3 counter summary (profiles/traffic_attention_<workload>.md), or
-    None when there is none or the sources that decide the attention kernels
-    and their launches changed since it was taken."""
-    import hashlib
-    import re
-    path = os.path.join(ROOT, "profiles", f"traffic_attention_{workload}.md")
-    if not os.path.exists(path):
-        return None, None
-    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
-    if not m:
-        return None, None
-    rec = json.loads(m.group(1))
-    digest = hashlib.sha256(b"".join(open(s, "rb").read() for s in srcs)).hexdigest()
-    if rec.get("source_sha256") != digest:
-        return None, rec
-    return rec["traffic_bytes_per_call"], rec
+def gather_stage(ms, torch, W, w, q, k, v, vert, aws, stream):
+    """HBM rate of the gathered column loads on a layer of Vertical-Slash
+    heads.  The heads are run with their verticals only (the selections the
+    estimator just made, no slashes): every key they attend is then a
+    gathered column, one bf16 K row and one fp16 V row (512 B) per (query
+    block, column), brought in by the column path of the attention kernel.
+    The timed call includes the fp16 copy of V the kernel reads."""
+    heads = [W.vs(p.n_vertical, 0) for p in w.heads]
+    prob, hp = ms.problem(w.n, w.n_q_heads, w.n_kv_heads), ms.head_params(heads)
+    index = ms.empty_workspace(ms.ms_index_bytes(prob, hp))
+    empty = torch.empty(1, dtype=torch.int32, device="cuda")
+    ms.ms_build_index(prob, hp, vert, empty, empty, index)
+    out = torch.empty_like(q)
+    ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    ms.ms_sparse_attn_indexed(prob, hp, q, k, v, index, out, aws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1)
+    offs, _ = ms.ms_index_layout(prob, hp)
+    base = index.view(torch.int32)
+    nb = w.n // 64
+    cols = sum(int(base[o[2] // 4 + nb]) for o in offs)
+    del index, out
+    return {"ms": t, "col_keys": cols}
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -295,11 +288,14 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
         t_att = ev[2].elapsed_time(ev[3]) / reps
     del ews
     kept = kept_entries(ms, prob, hp, w.heads, index, torch)
-    bkeys = block_keys(ms, prob, hp, index, torch)
+    bkeys, ckeys = block_keys(ms, prob, hp, index, torch)
     dense_pairs = w.n * (w.n + 1) // 2 * w.n_q_heads
     del index
     res = {"w": w, "q": q, "k": k, "v": v, "ms": ms_step, "wall_s": t_wall, "t_est": t_est, "t_idx": t_idx,
-           "t_att": t_att, "kept": kept, "block_keys": bkeys, "dense_pairs": dense_pairs, "graph_ms": graph_ms}
+           "t_att": t_att, "kept": kept, "block_keys": bkeys, "col_keys": ckeys, "dense_pairs": dense_pairs,
+           "graph_ms": graph_ms}
+    if all(p.pattern == W.VERTICAL_SLASH for p in w.heads) and any(p.n_vertical > 0 for p in w.heads):
+        res["gather"] = gather_stage(ms, torch, W, w, q, k, v, vert, aws, stream)
     del ws
     if do_dense:
         dout = torch.empty_like(q)
@@ -341,13 +337,19 @@ def summary(r):
     }
     if r.get("graph_ms") is not None:
         s["graph_replay_ms_per_layer"] = round(r["graph_ms"], 3)
-    # K/V bytes as the per-head kernel loads them (512 B per kept (query
-    # block, key) pair).  Heads served together by the grouped kernel share
-    # their loads, so for them this is an upper bound on what is read.
+    # K/V rows the kernels bring in when no row is reused across query blocks
+    # (512 B per kept (query block, key) pair: a bf16 K row and an fp16 V row);
+    # L2 reuse and heads served together make the HBM traffic smaller.
     att_bytes = 512.0 * r["block_keys"]
-    s["attention_kv_gbs"] = round(att_bytes / (r["t_att"] / 1e3) / 1e9, 1)
-    s["attention_kv_hbm_frac"] = round(s["attention_kv_gbs"] / PEAK_HBM_GBS, 4)
-    s["attention_flop_per_byte"] = round(4.0 * d * r["kept"] / att_bytes, 1)
+    s["attention_kv_rows_gbs"] = round(att_bytes / (r["t_att"] / 1e3) / 1e9, 1)
+    s["attention_flop_per_kv_row_byte"] = round(4.0 * d * r["kept"] / att_bytes, 1)
+    if "gather" in r:
+        g = r["gather"]
+        gb = 512.0 * g["col_keys"]
+        s["gather"] = {"ms": round(g["ms"], 3), "bytes": gb, "gbs": round(gb / (g["ms"] / 1e3) / 1e9, 1),
+                       "hbm_frac": round(gb / (g["ms"] / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "what": "the layer's heads with their verticals only: every kept key a gathered column, "
+                               "512 B per (query block, column)"}
     eb = estimate_bytes(r["w"])
     s["estimate_gbs"] = round(eb / (r["t_est"] / 1e3) / 1e9, 1)
     s["estimate_hbm_frac"] = round(s["estimate_gbs"] / PEAK_HBM_GBS, 4)
@@ -367,6 +369,9 @@ def summary(r):
         s["dense_tflops"] = round(dense_tf / (r["dense_ms"] / 1e3), 1)
         s["dense_mfma_frac"] = round(dense_tf / (r["dense_ms"] / 1e3) / PEAK_BF16_TFLOPS, 4)
         s["speedup_vs_dense"] = round(r["dense_ms"] / r["ms"], 3)
+        # an equally efficient dense kernel cannot be beaten by more than the
+        # FLOP ratio; a larger speedup flags a weak dense baseline
+        s["speedup_exceeds_flop_bound"] = s["speedup_vs_dense"] > s["flop_ratio_bound"]
     return s
 
 
@@ -415,35 +420,37 @@ def main():
         del src, dst
 
     w = main_r["w"]
-    # Roofline of the dominant kernel: the attention stage (per-head kernel on
-    # the headline layer).  Its intensity, 4 d FLOP per kept (row, key) pair
-    # over 512 bytes per kept (query block, key) pair, decides which ceiling
-    # binds (ridge = 2.5 PFLOP/s / 8 TB/s = 312.5 FLOP/byte).
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    att_bytes = 512.0 * main_r["block_keys"]
+    # Roofline of the dominant kernel, the sparse attention of the headline
+    # layer (on long sequences the per-head kernel by key segments, launched
+    # once per chunk of query blocks, plus the combination of its records and
+    # the fp16 V copy, < 2% together): MFMA-bound work of 4*128 flop per kept
+    # (row, key) pair, over the attention call's duration measured with HIP
+    # events on the library's stream.
+    kept_flop = 4.0 * 128 * main_r["kept"]
+    compulsory = (2 * w.n_q_heads + 2 * w.n_kv_heads) * w.n * 128 * 2  # Q, K, V read, out written (bf16)
     csrc = os.path.join(ROOT, "dynamic_sparse_attention_est_amd", "csrc")
     traffic, trec = recorded_traffic(a.workload, [os.path.join(csrc, f) for f in ATTN_SOURCES])
-    hbm_view = {"achieved": main_s["attention_kv_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": main_s["attention_kv_hbm_frac"],
-                "work": "512 B per kept (64-row query block, key) pair: one bf16 K row + one fp16 V row",
-                "bytes_per_launch": att_bytes}
-    mfma_view = {"achieved": main_s["attention_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                 "frac": main_s["attention_mfma_frac"], "work": "4*128 FLOP per kept (row, key) pair"}
-    bound = "hbm" if main_s["attention_flop_per_byte"] < ridge else "mfma"
-    view = hbm_view if bound == "hbm" else mfma_view
-    roof = {"bound": bound, "achieved": view["achieved"], "peak": view["peak"], "unit": view["unit"],
-            "frac": view["frac"], "traffic": traffic,
-            "kernel": "attention stage: the sparse attention kernels of one call (on long sequences the "
-                      "per-head kernel by key segments and the combination of its records), timed with the "
-                      "fp16 V copy they consume (< 0.1% of it)",
-            "work": view["work"], "flop_per_byte": main_s["attention_flop_per_byte"], "ridge": ridge,
-            "hbm_view": hbm_view, "mfma_view": mfma_view}
+    roof = {"bound": "mfma", "achieved": main_s["attention_tflops"], "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": main_s["attention_mfma_frac"], "traffic": traffic,
+            "kernel": "sparse attention stage of one call: the attention kernels (per-head kernel by key "
+                      "segments on long sequences, launched per chunk of query blocks, with the combination of "
+                      "its records) and the fp16 V copy they read",
+            "work": "4*128 flop per kept (row, key) pair, kept pairs counted exactly from the index",
+            "flop_per_launch": kept_flop, "launch_ms": round(main_r["t_att"], 3)}
     if traffic is not None:
-        roof["traffic_over_algorithmic"] = round(traffic / att_bytes, 3)
-        roof["measured_hbm_gbs"] = round(traffic / (main_r["t_att"] / 1e3) / 1e9, 1)
+        roof["hbm_gbs"] = round(traffic / (main_r["t_att"] / 1e3) / 1e9, 1)
+        roof["hbm_frac"] = round(roof["hbm_gbs"] / PEAK_HBM_GBS, 4)
+        roof["traffic_over_compulsory"] = round(traffic / compulsory, 1)
+        roof["flop_per_hbm_byte"] = round(kept_flop / traffic, 1)
         roof["traffic_source"] = f"profiles/traffic_attention_{a.workload}.md"
     elif trec is not None:
         roof["traffic_note"] = "recorded counters are for an older kernel source; not reported"
+    roof["compulsory_bytes"] = compulsory
+    roof["estimation"] = {"gbs": main_s["estimate_gbs"], "peak": PEAK_HBM_GBS, "frac": main_s["estimate_hbm_frac"],
+                          "ms": main_s["stages_ms"]["estimate"]}
+    if "gather" in main_s:
+        roof["gather"] = {"gbs": main_s["gather"]["gbs"], "peak": PEAK_HBM_GBS, "frac": main_s["gather"]["hbm_frac"],
+                          "ms": main_s["gather"]["ms"]}
     line = {
         "metric": "ms/layer sparse prefill attn (est+kernel) at 128K & 1M; speedup vs dense",
         "value": round(main_r["ms"], 3),

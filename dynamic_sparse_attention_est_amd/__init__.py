@@ -127,6 +127,55 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: Optional[torch.Tensor], name: str, dtype, numel: Optional[int] = None, at_least: bool = False,
+          optional: bool = False) -> None:
+    """Host-side checks of a tensor argument before the library sees its
+    pointer: the C ABI takes bare device pointers and cannot check extents,
+    so a wrong dtype, a strided view or a short buffer is refused here."""
+    if t is None:
+        if optional:
+            return
+        raise MsError(1, f"{name} is None")
+    if not isinstance(t, torch.Tensor):
+        raise MsError(1, f"{name} must be a torch.Tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise MsError(1, f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise MsError(1, f"{name} must be contiguous")
+    if numel is not None:
+        if at_least and t.numel() < numel:
+            raise MsError(1, f"{name} holds {t.numel()} elements, at least {numel} needed")
+        if not at_least and t.numel() != numel:
+            raise MsError(1, f"{name} holds {t.numel()} elements, {numel} expected")
+
+
+def _on_device(**tensors) -> None:
+    """Every tensor argument given must live on the GPU (checked after the
+    dtype and extent checks of all arguments)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise MsError(1, f"{name} must be a device tensor")
+
+
+def _rows(prob: Problem) -> int:
+    """Query rows per head of a call: n - 64 * q_block0."""
+    return int(prob.n) - 64 * int(prob.q_block0)
+
+
+def _need_qkv(prob: Problem, q, k, v=None) -> None:
+    d = int(prob.head_dim)
+    _need(q, "q", torch.bfloat16, int(prob.n_q_heads) * _rows(prob) * d)
+    _need(k, "k", torch.bfloat16, int(prob.n_kv_heads) * int(prob.n) * d)
+    if v is not None:
+        _need(v, "v", torch.bfloat16, int(prob.n_kv_heads) * int(prob.n) * d)
+
+
+def _need_out(prob: Problem, out, lse) -> None:
+    rows = int(prob.n_q_heads) * _rows(prob)
+    _need(out, "out", torch.float32 if prob.out_dtype == OUT_F32 else torch.bfloat16, rows * int(prob.head_dim))
+    _need(lse, "lse", torch.float32, rows, optional=True)
+
+
 def _nbytes(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
@@ -194,36 +243,74 @@ def empty_workspace(nbytes: int, device="cuda") -> torch.Tensor:
 
 # ---------------------------------------------------------------- calls
 def ms_estimate_vs(prob, heads, q, k, vert, slash, ws, dbg_v=None, dbg_s=None, stream=None) -> None:
+    nv, ns, _ = ms_selection_sizes(prob, heads)
+    _need_qkv(prob, q, k)
+    _need(vert, "vert", torch.int32, nv, at_least=True, optional=nv == 0)
+    _need(slash, "slash", torch.int32, ns, at_least=True, optional=ns == 0)
+    for name, t in (("dbg_v", dbg_v), ("dbg_s", dbg_s)):
+        _need(t, name, torch.float32, int(prob.n_q_heads) * int(prob.n), at_least=True, optional=True)
+    _need(ws, "ws", torch.uint8)
+    _on_device(q=q, k=k, vert=vert, slash=slash, dbg_v=dbg_v, dbg_s=dbg_s, ws=ws)
     _check(load().ms_estimate_vs(ctypes.byref(prob), heads, _ptr(q), _ptr(k), _ptr(vert), _ptr(slash), _ptr(dbg_v),
                                  _ptr(dbg_s), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def ms_estimate_block(prob, heads, q, k, blocks, ws, dbg_scores=None, stream=None) -> None:
+    _, _, nbk = ms_selection_sizes(prob, heads)
+    _need_qkv(prob, q, k)
+    _need(blocks, "blocks", torch.int32, nbk, at_least=True, optional=nbk == 0)
+    nb = int(prob.n) // 64
+    _need(dbg_scores, "dbg_scores", torch.float32, int(prob.n_q_heads) * (nb - int(prob.q_block0)) * nb,
+          at_least=True, optional=True)
+    _need(ws, "ws", torch.uint8)
+    _on_device(q=q, k=k, blocks=blocks, dbg_scores=dbg_scores, ws=ws)
     _check(load().ms_estimate_block(ctypes.byref(prob), heads, _ptr(q), _ptr(k), _ptr(blocks), _ptr(dbg_scores),
                                     _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def ms_build_index(prob, heads, vert, slash, blocks, index, stream=None) -> None:
+    nv, ns, nbk = ms_selection_sizes(prob, heads)
+    _need(vert, "vert", torch.int32, nv, at_least=True, optional=nv == 0)
+    _need(slash, "slash", torch.int32, ns, at_least=True, optional=ns == 0)
+    _need(blocks, "blocks", torch.int32, nbk, at_least=True, optional=nbk == 0)
+    _need(index, "index", torch.uint8)
+    _on_device(vert=vert, slash=slash, blocks=blocks, index=index)
     _check(load().ms_build_index(ctypes.byref(prob), heads, _ptr(vert), _ptr(slash), _ptr(blocks), _ptr(index),
                                  _nbytes(index), _stream(stream)))
 
 
 def ms_sparse_attn_indexed(prob, heads, q, k, v, index, out, ws, lse=None, stream=None) -> None:
+    _need_qkv(prob, q, k, v)
+    _need_out(prob, out, lse)
+    _need(index, "index", torch.uint8)
+    _need(ws, "ws", torch.uint8)
+    _on_device(q=q, k=k, v=v, index=index, out=out, ws=ws, lse=lse)
     _check(load().ms_sparse_attn_indexed(ctypes.byref(prob), heads, _ptr(q), _ptr(k), _ptr(v), _ptr(index),
                                          _nbytes(index), _ptr(out), _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def ms_sparse_attn(prob, heads, q, k, v, out, ws, lse=None, stream=None) -> None:
+    _need_qkv(prob, q, k, v)
+    _need_out(prob, out, lse)
+    _need(ws, "ws", torch.uint8)
+    _on_device(q=q, k=k, v=v, out=out, ws=ws, lse=lse)
     _check(load().ms_sparse_attn(ctypes.byref(prob), heads, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                  _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def ms_dense_attn(prob, q, k, v, out, ws, lse=None, stream=None) -> None:
+    _need_qkv(prob, q, k, v)
+    _need_out(prob, out, lse)
+    _need(ws, "ws", torch.uint8)
+    _on_device(q=q, k=k, v=v, out=out, ws=ws, lse=lse)
     _check(load().ms_dense_attn(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                                 _nbytes(ws), _stream(stream)))
 
 
 def ms_topk_f32(x: torch.Tensor, k: int, idx: torch.Tensor, stream=None) -> None:
+    _need(x, "x", torch.float32)
+    _need(idx, "idx", torch.int32, min(int(k), x.numel()), at_least=True)
+    _on_device(x=x, idx=idx)
     _check(load().ms_topk_f32(_ptr(x), x.numel(), int(k), _ptr(idx), _stream(stream)))
 
 
@@ -232,6 +319,11 @@ def ms_attention_recall(prob, lse_sparse: torch.Tensor, lse_dense: torch.Tensor,
     """recall[h] = mean over rows of exp(lse_sparse - lse_dense): the share of
     the full attention mass that the sparse index keeps (fp32 tensors on the
     device: [H_q, n], [H_q, n], [H_q])."""
+    rows = int(prob.n_q_heads) * _rows(prob)
+    _need(lse_sparse, "lse_sparse", torch.float32, rows)
+    _need(lse_dense, "lse_dense", torch.float32, rows)
+    _need(recall, "recall", torch.float32, int(prob.n_q_heads), at_least=True)
+    _on_device(lse_sparse=lse_sparse, lse_dense=lse_dense, recall=recall)
     _check(load().ms_attention_recall(ctypes.byref(prob), _ptr(lse_sparse), _ptr(lse_dense), _ptr(recall),
                                       _stream(stream)))
 

@@ -150,55 +150,96 @@ def test_workspace_sizes_cover_their_parts():
     assert ms.ms_workspace_bytes(prob, hp) >= est + idx + att
 
 
-class _Fake:
-    """Stands in for a tensor: an address the library never dereferences here."""
-
-    def __init__(self, addr, nbytes=1 << 20):
-        self.addr, self.nb = addr, nbytes
-
-    def data_ptr(self):
-        return self.addr
-
-    def numel(self):
-        return self.nb
-
-    def element_size(self):
-        return 1
+def _raw(status, name, *args):
+    """Calls the C ABI directly (ctypes), bypassing the binding's own checks."""
+    lib = ms.load()
+    got = getattr(lib, name)(*args)
+    assert got == status, (name, got, lib.ms_last_error())
 
 
-class _Stream:
-    cuda_stream = 0
+def _vp(addr):
+    return None if addr is None else ctypes.c_void_p(addr)
 
 
 def test_calls_reject_bad_arguments_before_launch():
+    """The C ABI validates pointers, alignment and capacities on the host and
+    returns before anything is enqueued (fake addresses, never dereferenced)."""
     w = W.custom("t", 1024, 2, 1, [W.vs(16, 16), W.bs(4)])
     prob, hp = _prob(w), ms.head_params(w.heads)
-    A = _Fake(1 << 20)
-    st = _Stream()
+    pr = ctypes.byref(prob)
+    A = 1 << 20
+    MB = 1 << 20
     # null q
-    _expect(1, ms.ms_estimate_vs, prob, hp, None, A, A, A, A, None, None, st)
+    _raw(1, "ms_estimate_vs", pr, hp, None, _vp(A), _vp(A), _vp(A), None, None, _vp(A), MB, None)
     # misaligned k
-    _expect(1, ms.ms_estimate_vs, prob, hp, A, _Fake((1 << 20) + 2), A, A, A, None, None, st)
+    _raw(1, "ms_estimate_vs", pr, hp, _vp(A), _vp(A + 2), _vp(A), _vp(A), None, None, _vp(A), MB, None)
     # workspace too small
-    _expect(3, ms.ms_estimate_vs, prob, hp, A, A, A, A, _Fake(1 << 20, 1024), None, None, st)
+    _raw(3, "ms_estimate_vs", pr, hp, _vp(A), _vp(A), _vp(A), _vp(A), None, None, _vp(A), 1024, None)
     # null selection array of a present pattern
-    _expect(1, ms.ms_estimate_block, prob, hp, A, A, None, A, None, st)
+    _raw(1, "ms_estimate_block", pr, hp, _vp(A), _vp(A), None, None, _vp(A), MB, None)
     # index arena too small
-    _expect(3, ms.ms_build_index, prob, hp, A, A, A, _Fake(1 << 20, 4096), st)
+    _raw(3, "ms_build_index", pr, hp, _vp(A), _vp(A), _vp(A), _vp(A), 4096, None)
     # misaligned index arena
-    _expect(1, ms.ms_build_index, prob, hp, A, A, A, _Fake((1 << 20) + 16, 1 << 30), st)
+    _raw(1, "ms_build_index", pr, hp, _vp(A), _vp(A), _vp(A), _vp(A + 16), 1 << 30, None)
     # attention workspace too small
-    _expect(3, ms.ms_dense_attn, prob, A, A, A, A, _Fake(1 << 20, 100), None, st)
+    _raw(3, "ms_dense_attn", pr, _vp(A), _vp(A), _vp(A), _vp(A), None, _vp(A), 100, None)
     # top-k hook: empty input, negative k
     lib = ms.load()
     assert lib.ms_topk_f32(ctypes.c_void_p(1 << 20), 0, 1, ctypes.c_void_p(1 << 20), None) == 1
-    pr = ms.problem(1024, 4, 2)
-    assert lib.ms_attention_recall(ctypes.byref(pr), None, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
+    pr2 = ms.problem(1024, 4, 2)
+    assert lib.ms_attention_recall(ctypes.byref(pr2), None, ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
                                    None) == 1
-    assert lib.ms_attention_recall(ctypes.byref(pr), ctypes.c_void_p((1 << 20) + 2), ctypes.c_void_p(1 << 20),
+    assert lib.ms_attention_recall(ctypes.byref(pr2), ctypes.c_void_p((1 << 20) + 2), ctypes.c_void_p(1 << 20),
                                    ctypes.c_void_p(1 << 20), None) == 1
     assert lib.ms_topk_f32(ctypes.c_void_p(1 << 20), 10, -1, ctypes.c_void_p(1 << 20), None) == 1
     assert b"negative" in lib.ms_last_error()
+
+
+def _binding_rejects(fn, *args, match):
+    with pytest.raises(ms.MsError, match=match) as e:
+        fn(*args)
+    assert e.value.status == 1
+
+
+def test_binding_checks_tensors_before_the_library():
+    """The binding refuses a wrong dtype, a strided view, a short or long
+    buffer and a host tensor before passing a pointer on (the C ABI sees bare
+    addresses and cannot check extents).  Host tensors of the right shape and
+    dtype get as far as the device check, so every other check runs here."""
+    import torch
+    n, hq, hkv = 1024, 2, 1
+    w = W.custom("t", n, hq, hkv, [W.vs(16, 16), W.bs(4)])
+    prob, hp = _prob(w), ms.head_params(w.heads)
+    bf = torch.bfloat16
+    q = torch.zeros(hq, n, 128, dtype=bf)
+    k = torch.zeros(hkv, n, 128, dtype=bf)
+    v = torch.zeros(hkv, n, 128, dtype=bf)
+    out = torch.zeros(hq, n, 128, dtype=bf)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+    nv, ns, nbk = ms.ms_selection_sizes(prob, hp)
+    vert, slash = torch.zeros(nv, dtype=torch.int32), torch.zeros(ns, dtype=torch.int32)
+    blocks = torch.zeros(nbk, dtype=torch.int32)
+    call = ms.ms_sparse_attn
+    _binding_rejects(call, prob, hp, q.float(), k, v, out, ws, match="q: dtype")
+    _binding_rejects(call, prob, hp, q.transpose(1, 2), k, v, out, ws, match="q must be contiguous")
+    _binding_rejects(call, prob, hp, q.reshape(-1)[:-128], k, v, out, ws, match="q holds")
+    _binding_rejects(call, prob, hp, q, k.reshape(-1)[:-1], v, out, ws, match="k holds")
+    _binding_rejects(call, prob, hp, q, k, v.half(), out, ws, match="v: dtype")
+    _binding_rejects(call, prob, hp, q, k, v, out.float(), ws, match="out: dtype")
+    _binding_rejects(call, prob, hp, q, k, v, out, ws, torch.zeros(hq * n - 1), match="lse holds")
+    _binding_rejects(call, prob, hp, q, k, v, out, ws, match="q must be a device tensor")
+    f32 = ms.problem(n, hq, hkv, out_dtype=ms.OUT_F32)
+    _binding_rejects(call, f32, hp, q, k, v, out, ws, match="out: dtype")
+    chunk = ms.problem(n, hq, hkv, q_block0=4)
+    _binding_rejects(ms.ms_dense_attn, chunk, q, k, v, out, ws, match="q holds")   # the chunk has n - 256 rows
+    _binding_rejects(ms.ms_estimate_vs, prob, hp, q, k, vert[:-1], slash, ws, match="vert holds")
+    _binding_rejects(ms.ms_estimate_vs, prob, hp, q, k, vert, slash.long(), ws, match="slash: dtype")
+    _binding_rejects(ms.ms_estimate_vs, prob, hp, q, k, vert, slash, ws, torch.zeros(5), match="dbg_v holds")
+    _binding_rejects(ms.ms_estimate_block, prob, hp, q, k, blocks[:-1], ws, match="blocks holds")
+    _binding_rejects(ms.ms_build_index, prob, hp, vert, slash, blocks, ws.view(torch.int32), match="index: dtype")
+    _binding_rejects(ms.ms_topk_f32, torch.zeros(10), 5, torch.zeros(4, dtype=torch.int32), match="idx holds")
+    _binding_rejects(ms.ms_attention_recall, prob, torch.zeros(hq * n), torch.zeros(hq * n),
+                     torch.zeros(1), match="recall holds")
 
 
 def test_chunk_sizes_follow_the_query_blocks():
