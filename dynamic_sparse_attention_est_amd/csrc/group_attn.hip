@@ -439,21 +439,40 @@ struct Loader {
   }
 };
 
+// Full causal attention.  A workgroup of 8 waves serves four slots of 64
+// query rows (two waves each) that read the same KV head: HPW heads of one
+// query block times 4 / HPW consecutive query blocks (GQA 4:1: four heads of
+// one block; two heads per KV head: two heads of two blocks; one head per KV
+// head: four blocks of that head).  The keys of the slots' longest block are
+// walked once; a slot's waves skip the pieces past their own block's last
+// row, so every K/V tile in LDS feeds up to 256 query rows whatever the group
+// size.
 template <int HPW, int S>
 __device__ __forceinline__ void group_dense_body(const AttnArgs& a) {
-  constexpr int kD16 = 16 / (2 * HPW);  // load-to-LDS instructions per wave per piece
-  static_assert(S >= 3 && kD16 >= 1, "ring and wave counts");
+  constexpr int kSlots = 4;
+  constexpr int kBQ = kSlots / HPW;                // consecutive query blocks per workgroup
+  constexpr int kD16 = 16 / (2 * kSlots);          // load-to-LDS instructions per wave per piece
+  static_assert(S >= 3 && kD16 >= 1 && kSlots % HPW == 0, "ring, wave and slot counts");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wv >> 1;
   const int chunks = a.grp / HPW;
-  int pair, b;
-  map_group(blockIdx.x, a.hkv * chunks, a.nb, pair, b);
+  const int ngroups = (a.nb + kBQ - 1) / kBQ;     // groups of kBQ query blocks, the last one may be short
+  int pair, bg;
+  map_group(blockIdx.x, a.hkv * chunks, ngroups, pair, bg);
   const int kvh = pair % a.hkv, chunk = pair / a.hkv;
-  const int h = kvh * a.grp + chunk * HPW + (wv >> 1);
+  const int h = kvh * a.grp + chunk * HPW + slot % HPW;
+  // Group bg holds the call's query blocks bg*kBQ .. bg*kBQ + kBQ - 1 (those
+  // below nb); slot j takes the (j / HPW)-th from the top.
+  const int btop = min(a.nb - 1, bg * kBQ + kBQ - 1);
+  const int bj = btop - slot / HPW;
+  const bool active = bj >= bg * kBQ;
+  const int b = active ? bj : btop;
   const int64_t n = a.n;
-  const int row0 = (a.qb0 + b) * kBM;  // b indexes the call's query blocks
-  const int npieces = row0 / kKP + 2;  // keys [0, row0 + 64)
+  const int row0 = (a.qb0 + b) * kBM;              // this slot's first query row
+  const int end = active ? row0 + kBM : 0;         // this slot's keys: [0, end)
+  const int npieces = ((a.qb0 + btop) * kBM) / kKP + 2;  // keys [0, top block's row0 + 64)
 
   const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
   const __amdgpu_buffer_rsrc_t kr =
@@ -483,7 +502,14 @@ __device__ __forceinline__ void group_dense_body(const AttnArgs& a) {
     constexpr int ST = decltype(st_c)::value;
     const int p = i + S - 1;
     ld.range(stage<(ST + S - 1) % S>(), p < npieces ? kKP * p : (int)n);
-    hr.advance(s_cur, kKP * i, nullptr, kKP, 0xffffffffu, stage<ST>(), true, stage<(ST + 1) % S>());
+    if constexpr (kBQ == 1) {
+      // one query block: every piece up to the end holds keys of every slot
+      hr.advance(s_cur, kKP * i, nullptr, kKP, 0xffffffffu, stage<ST>(), true, stage<(ST + 1) % S>());
+    } else {
+      // pieces at or past the slot's end hold none of its keys
+      const uint32_t bits = kKP * i < end ? 0xffffffffu : 0u;
+      hr.advance(s_cur, kKP * i, nullptr, kKP, bits, stage<ST>(), kKP * (i + 1) < end, stage<(ST + 1) % S>());
+    }
     // Pieces i+1 (V) and i+2 (K, read ahead) must have landed (this wave's
     // share); S-3 later pieces may still be in flight.
     wait_vm_lgkm0<(S - 3) * kD16>();
@@ -494,7 +520,7 @@ __device__ __forceinline__ void group_dense_body(const AttnArgs& a) {
   while (run_steps<0, S>(step)) {
   }
   wait_vm_lgkm0<0>();  // loads of pieces past the end
-  hr.store(a, h);
+  if (active) hr.store(a, h);
 }
 
 // Sparse attention over the union index of a chunk of HPW heads (MInference
@@ -664,12 +690,15 @@ __device__ __forceinline__ void group_sparse_body(const AttnArgs& a, const Group
   if (active) hr.store(a, h);
 }
 
-// Heads per workgroup (HPW) and ring stages: 4 heads when the group size
-// allows (one workgroup per CU, 8 stages = 128 KiB of LDS), else 2 (two per
-// CU, 4 stages) or 1 (three per CU, 3 stages).
+// Dense: eight waves and eight ring stages (128 KiB of LDS, one workgroup per
+// CU) for every group size; HPW heads of one KV head per workgroup, each over
+// 4 / HPW consecutive query blocks.
 __global__ __launch_bounds__(512) void group_dense_h4(AttnArgs a) { group_dense_body<4, 8>(a); }
-__global__ __launch_bounds__(256) void group_dense_h2(AttnArgs a) { group_dense_body<2, 4>(a); }
-__global__ __launch_bounds__(128) void group_dense_h1(AttnArgs a) { group_dense_body<1, 3>(a); }
+__global__ __launch_bounds__(512) void group_dense_h2(AttnArgs a) { group_dense_body<2, 8>(a); }
+__global__ __launch_bounds__(512) void group_dense_h1(AttnArgs a) { group_dense_body<1, 8>(a); }
+
+// Sparse: heads per workgroup (HPW) and ring stages: 4 heads (one workgroup
+// per CU, 8 stages = 128 KiB of LDS) or 2 (two per CU, 4 stages).
 
 __global__ __launch_bounds__(512) void group_sparse_h4(AttnArgs a, const GroupDesc* __restrict__ groups,
                                                       const char* __restrict__ arena) {
@@ -694,13 +723,14 @@ hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, int h
 
 hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s) {
   const int hpw = hpw_of(a.grp);
-  const dim3 grid((unsigned)((int64_t)a.nb * a.hkv * (a.grp / hpw)));
+  const int bq = 4 / hpw;  // consecutive query blocks per workgroup
+  const dim3 grid((unsigned)((int64_t)((a.nb + bq - 1) / bq) * a.hkv * (a.grp / hpw)));
   if (hpw == 4)
     hipLaunchKernelGGL(group_dense_h4, grid, dim3(512), 0, s, a);
   else if (hpw == 2)
-    hipLaunchKernelGGL(group_dense_h2, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(group_dense_h2, grid, dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL(group_dense_h1, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(group_dense_h1, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

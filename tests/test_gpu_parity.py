@@ -327,10 +327,11 @@ def test_empty_rows_give_zero_and_neg_inf_lse():
 
 
 # Group sizes 1, 2, 4 and 8 take the grouped dense kernel with 1, 2, 4 and 4
-# heads per workgroup (3-, 4-, 8- and 8-stage rings; two chunks per KV head for
-# 8); n = 64 is a single query block, 64 * 37 an odd block count.
+# heads per workgroup over 4, 2, 1 and 1 consecutive query blocks (two chunks
+# per KV head for 8); n = 64 is a single query block, 64 * 37 and 64 * 39 block
+# counts that leave the last workgroup's lower slots empty.
 @pytest.mark.parametrize("n,hq,hkv", [(1024, 4, 2), (64, 2, 2), (64 * 37, 3, 3), (1024, 4, 1), (640, 8, 1),
-                                      (576, 16, 2)])
+                                      (576, 16, 2), (64 * 39, 4, 2), (64 * 6, 1, 1)])
 def test_dense_attention(n, hq, hkv):
     w = W.custom("dense", n, hq, hkv, [W.dense()] * hq, recipe="vs_planted", seed=13 + n + hq)
     st = make(w)
