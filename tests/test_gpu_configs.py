@@ -22,7 +22,7 @@ from test_gpu_parity import LSE_ATOL, _near_tie_ok, _score_check
 pytestmark = pytest.mark.gpu
 
 
-def _check_layer(cid, heads_checked, n_blocks, seed, est_heads=()):
+def _check_layer(cid, heads_checked, n_blocks, seed, est_heads=(), edge_blocks=()):
     w = W.config(cid)
     print(f"[config {cid}] {w.name}: n={w.n} heads={w.n_q_heads}/{w.n_kv_heads}", flush=True)
     st = run_staged(make(w), debug=True)
@@ -65,7 +65,7 @@ def _check_layer(cid, heads_checked, n_blocks, seed, est_heads=()):
     lse = st.lse
     for h in heads_checked:
         p = w.heads[h]
-        blocks = sample_blocks(w.nb, n_blocks, seed + 100 + h)
+        blocks = sorted(set(sample_blocks(w.nb, n_blocks, seed + 100 + h)) | set(edge_blocks))
         got_idx = read_index_blocks(st.prob, st.hp, st.index, h, blocks)
         qh = f64(st.q[h])
         kh, vh = f64(st.k[kv_of(w, h)]), f64(st.v[kv_of(w, h)])
@@ -114,8 +114,29 @@ def test_config3_mixed_128k():
                  est_heads=[vs_h[0], bs_h[0]])
 
 
+def _record_chunk_blocks(w):
+    """Query blocks per chunk of the key-segment mode at full size: the
+    records of one block (32 heads x every 32768-key segment x 64 rows of 128
+    fp32 plus 64 log-sum-exps) in a 4 GiB budget."""
+    nseg = (w.n - 1) // 32768 + 1
+    return (4 << 30) // (nseg * w.n_q_heads * (64 * 128 + 64) * 4)
+
+
 def test_config4_vertical_slash_1m():
-    _check_layer(4, heads_checked=[0, 29], n_blocks=3, seed=4, est_heads=[0])
+    """Scores and end-to-end selections of one Q head per KV head; index and
+    attention of four heads (different KV heads) at the record-chunk edges
+    (chunks of query blocks run from the last block down), at key-segment
+    edges (a block whose rows end a 32768-key segment and the next), the
+    first and last blocks, and random ones."""
+    w = W.config(4)
+    cb = _record_chunk_blocks(w)
+    nb = w.nb
+    # chunk c holds query blocks c*cb .. c*cb + cb - 1 (the last chunk may be short)
+    chunk_edges = [cb - 1, cb, 64 * cb - 1, 64 * cb, (nb // cb) * cb - 1, (nb // cb) * cb]
+    seg_edges = [511, 512, 8191, 8192, nb - 513, nb - 512]
+    edges = sorted({0, 1, nb - 2, nb - 1, *[b for b in chunk_edges + seg_edges if 0 <= b < nb]})
+    _check_layer(4, heads_checked=[0, 9, 18, 27], n_blocks=2, seed=4, est_heads=list(range(0, 32, 4)),
+                 edge_blocks=edges)
 
 
 def test_union_of_many_ranges_per_block():

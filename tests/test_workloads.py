@@ -48,3 +48,26 @@ def test_bs_lowrank_blocks_cluster():
     norms = qb.norm(dim=1)
     # round(0.05 * 64) = 3 planted blocks stand out of the pooled noise.
     assert (norms > 3 * norms.median()).sum().item() == 3
+
+
+def test_query_mean_makes_planted_columns_real_verticals():
+    """With the shared query mean (the 1M structured diagnostic's recipe, at a
+    small n) every planted column has a logit far above the others for the
+    last query rows; without it the planted columns sit in the noise."""
+    import oracle
+    for qm, expect in ((0.5, True), (0.0, False)):
+        w = W.Workload("t", 9, 8192, 1, 1, (W.vs(8, 64),), "vs_planted", n_planted=8, seed=3, query_mean=qm)
+        q, k, _ = W.generate(w)
+        qh, kh = q[0].double().numpy(), k[0].double().numpy()
+        v, _ = oracle.vs_scores(qh[-64:], kh)
+        g = W._gen(w, W._PLANT, 0, "cpu")
+        planted = sorted(torch.randperm(w.n, generator=g)[:8].tolist())
+        got = oracle.topk(v, 8).tolist() == planted
+        assert got == expect, (qm, oracle.topk(v, 8).tolist(), planted)
+
+
+def test_structured_diagnostic_is_the_1m_layer_plus_a_query_mean():
+    w4, w5 = W.config(4, n=4096), W.config(5, n=4096)
+    assert (w5.n_q_heads, w5.n_kv_heads, w5.heads, w5.n_planted) == (w4.n_q_heads, w4.n_kv_heads, w4.heads,
+                                                                      w4.n_planted)
+    assert w4.query_mean == 0.0 and w5.query_mean == 0.5

@@ -90,6 +90,7 @@ class Workload:
     n_planted: int = 0      # planted key columns per KV head
     lowrank_frac: float = 0.0
     seed: int = 0
+    query_mean: float = 0.0  # vs_planted: std of a shared mean added to the group's queries
 
     @property
     def group(self) -> int:
@@ -138,6 +139,16 @@ def config(config_id: int, seed: int = 0, n: Optional[int] = None) -> Workload:
         nn = n or 1048576
         return Workload("vs_1m", 4, nn, 32, 8, tuple(vs(1000, 6096) for _ in range(32)), "vs_planted",
                         n_planted=64, seed=seed)
+    if config_id == 5:
+        # Diagnostic beside the five workloads (not one of them): the 1M
+        # Vertical-Slash layer with a shared query mean per KV group, so that
+        # the planted key columns are real verticals and the slashes through
+        # them (64 offsets per column, seen by the last 64 rows) win the slash
+        # budget, as structured attention would; the rest of the budget stays
+        # scattered.
+        nn = n or 1048576
+        return Workload("vs_1m_s", 5, nn, 32, 8, tuple(vs(1000, 6096) for _ in range(32)), "vs_planted",
+                        n_planted=64, seed=seed, query_mean=0.5)
     raise ValueError(f"unknown config {config_id}")
 
 
@@ -160,7 +171,7 @@ def _gen(w: Workload, tensor_id: int, head: int, device) -> torch.Generator:
     return g
 
 
-_Q, _K, _V, _PLANT, _LOWRANK_U, _LOWRANK_W, _LOWRANK_BLK, _GRID_U = range(8)
+_Q, _K, _V, _PLANT, _LOWRANK_U, _LOWRANK_W, _LOWRANK_BLK, _GRID_U, _QMEAN = range(9)
 
 
 def _randn(w: Workload, tensor_id: int, head: int, shape, device) -> torch.Tensor:
@@ -176,7 +187,9 @@ def generate(w: Workload, device="cpu"):
                   (drawn without replacement) get k_j += 3 * mean(q), the mean
                   over the group's Q heads and all positions; then every key
                   gets k_j += 0.5 * mean over the group's Q heads of q_j (the
-                  local bias toward the main diagonal).
+                  local bias toward the main diagonal).  With query_mean = m > 0
+                  every query of a KV group first gets += mu, one draw of
+                  mu ~ N(0, m^2 I) per group (a shared query direction).
       bs_lowrank  q, k, v ~ N(0, 1).  Per head, round(frac * NB) blocks are
                   chosen; U (128x4) ~ N(0, 1/4); each chosen block draws
                   w ~ N(0, I_4) and all 64 of its tokens, in Q and in K, get
@@ -201,6 +214,10 @@ def generate(w: Workload, device="cpu"):
     if w.recipe == "vs_planted":
         for kv in range(hkv):
             qf = [(_randn(w, _Q, h, (n, d), device) * s) for h in range(kv * grp, (kv + 1) * grp)]
+            if w.query_mean > 0:
+                mu = _randn(w, _QMEAN, kv, (d,), device) * w.query_mean
+                for x in qf:
+                    x += mu
             kf = _randn(w, _K, kv, (n, d), device) * s
             qmean_all = torch.stack([x.mean(dim=0) for x in qf]).mean(dim=0)
             if w.n_planted > 0:
