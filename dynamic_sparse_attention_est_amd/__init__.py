@@ -24,6 +24,7 @@ __all__ = [
     "ms_index_layout", "ms_attn_workspace_bytes", "ms_workspace_bytes", "ms_estimate_vs",
     "ms_estimate_block", "ms_build_index", "ms_sparse_attn_indexed", "ms_sparse_attn",
     "ms_dense_attn", "ms_topk_f32", "ms_version", "read_index", "empty_workspace",
+    "ms_sparse_attn_noalloc", "ms_noalloc_scratch_bytes", "ms_attention_recall",
     "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "DENSE", "GRID", "OUT_BF16", "OUT_F32",
 ]
 
@@ -89,6 +90,8 @@ def load():
         "ms_dense_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ms_topk_f32": (ctypes.c_int, [vp, i64, i32, vp, vp]),
         "ms_attention_recall": (ctypes.c_int, [P, vp, vp, vp, vp]),
+        "ms_sparse_attn_noalloc": (ctypes.c_int, [P, H, vp, vp, vp, vp, vp, vp]),
+        "ms_noalloc_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(sz)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -296,6 +299,22 @@ def ms_sparse_attn(prob, heads, q, k, v, out, ws, lse=None, stream=None) -> None
     _on_device(q=q, k=k, v=v, out=out, ws=ws, lse=lse)
     _check(load().ms_sparse_attn(ctypes.byref(prob), heads, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                  _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def ms_sparse_attn_noalloc(prob, heads, q, k, v, out, lse=None, stream=None) -> None:
+    """ms_sparse_attn with its workspace in the library's static per-GPU
+    scratch: allocates nothing (see include/msattn.h)."""
+    _need_qkv(prob, q, k, v)
+    _need_out(prob, out, lse)
+    _on_device(q=q, k=k, v=v, out=out, lse=lse)
+    _check(load().ms_sparse_attn_noalloc(ctypes.byref(prob), heads, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         _stream(stream)))
+
+
+def ms_noalloc_scratch_bytes() -> int:
+    out = ctypes.c_size_t()
+    _check(load().ms_noalloc_scratch_bytes(ctypes.byref(out)))
+    return out.value
 
 
 def ms_dense_attn(prob, q, k, v, out, ws, lse=None, stream=None) -> None:

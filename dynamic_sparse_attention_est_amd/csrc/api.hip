@@ -7,6 +7,7 @@
 #include <cstring>
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -467,6 +468,34 @@ ms_status check_ws(const void* ws, size_t have, size_t need, const char* name) {
   return MS_OK;
 }
 
+// Scratch of ms_sparse_attn_noalloc: a fixed array in the library's device
+// code, one copy per GPU (each GPU's copy lives at its own address, held until
+// the process ends).  Host code never passes `scratch` itself to a kernel (on
+// the host the name is only a stand-in); it takes the device address of the
+// current GPU's copy from hipGetSymbolAddress, once per device, and uses that.
+constexpr size_t kScratchBytes = size_t{MS_NOALLOC_SCRATCH_MIB} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+ms_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MS_ERR_DEVICE, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_fail(e, "address of the static scratch");
+    if (!ptr || !aligned(ptr, kAlign)) return fail(MS_ERR_DEVICE, "static scratch address is null or misaligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MS_OK;
+}
+
 #define MS_TRY(x)                          \
   do {                                     \
     const ms_status st_ = (x);             \
@@ -804,6 +833,27 @@ ms_status ms_sparse_attn(const ms_problem* prob, const ms_head_params* params, c
   MS_TRY(run_estimate_block(P, qq, kk, blocks, nullptr, w + P.o_est, stream));
   MS_TRY(run_build_index(P, vert, slash, blocks, w + P.o_index, stream));
   return run_attention(P, q, k, v, w + P.o_index, out, lse, w + P.o_attn, stream);
+}
+
+ms_status ms_sparse_attn_noalloc(const ms_problem* prob, const ms_head_params* params, const void* q,
+                                 const void* k, const void* v, void* out, float* lse, hipStream_t stream) {
+  g_err.clear();
+  if (!params) return fail(MS_ERR_INVALID_ARG, "params is null");
+  Plan P;
+  MS_TRY(make_plan(prob, params, P));
+  if (P.o_total > kScratchBytes)
+    return fail(MS_ERR_CAPACITY, "the layer needs %zu bytes of workspace; the static scratch holds %zu (%d MiB)",
+                P.o_total, kScratchBytes, (int)(kScratchBytes >> 20));
+  void* ws = nullptr;
+  MS_TRY(scratch_of_current_device(&ws));
+  return ms_sparse_attn(prob, params, q, k, v, out, lse, ws, kScratchBytes, stream);
+}
+
+ms_status ms_noalloc_scratch_bytes(size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(MS_ERR_INVALID_ARG, "bytes is null");
+  *bytes = kScratchBytes;
+  return MS_OK;
 }
 
 ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, const void* v, void* out, float* lse,

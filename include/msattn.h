@@ -27,8 +27,10 @@
  *             B*H_kv KV heads, sequence-major), within the head limit.
  *   Memory.   Every tensor pointer is a device pointer owned by the caller.
  *             The library allocates nothing and keeps no global state besides a
- *             thread-local error string.  Workspaces and the index arena are
- *             caller-allocated, sized by the *_bytes queries.
+ *             thread-local error string and, for ms_sparse_attn_noalloc only,
+ *             its static scratch array on each GPU and that array's address.
+ *             Workspaces and the index arena are caller-allocated, sized by the
+ *             *_bytes queries.
  *   Errors.   Arguments are validated on the host before anything is enqueued;
  *             an invalid call returns a status, writes nothing and enqueues
  *             nothing.  MS_ERR_DEVICE carries the HIP message in ms_last_error().
@@ -204,6 +206,25 @@ ms_status ms_sparse_attn_indexed(const ms_problem* prob, const ms_head_params* p
  * ws: >= ms_workspace_bytes (holds selections, the index and the V copy). */
 ms_status ms_sparse_attn(const ms_problem* prob, const ms_head_params* params, const void* q, const void* k,
                          const void* v, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as ms_sparse_attn, computed with the same kernels and bitwise the same
+ * results, but with its workspace in a static scratch array inside the
+ * library (MS_NOALLOC_SCRATCH_MIB MiB per GPU, reserved when the library's
+ * device code is loaded on that GPU and held until the process ends).  The
+ * call allocates nothing.  The caller still owns q, k, v, out and lse
+ * (layouts as for ms_sparse_attn).  A layer whose ms_workspace_bytes exceeds
+ * the scratch returns MS_ERR_CAPACITY before anything is enqueued.  Every call
+ * on one GPU uses that GPU's one scratch array (the current device's), which
+ * keeps the previous call's contents (nothing in the path needs it zeroed):
+ * calls that may overlap on one GPU (different streams or host threads
+ * without ordering between them) race and must be serialised by the caller. */
+#define MS_NOALLOC_SCRATCH_MIB 128
+ms_status ms_sparse_attn_noalloc(const ms_problem* prob, const ms_head_params* params, const void* q,
+                                 const void* k, const void* v, void* out, float* lse, hipStream_t stream);
+/* Size in bytes of that static scratch. */
+ms_status ms_noalloc_scratch_bytes(size_t* bytes);
 
 /* Full causal attention with the same kernel and no index (the baseline the
  * speedups are measured against).  ws: >= ms_attn_workspace_bytes. */

@@ -193,6 +193,15 @@ def test_calls_reject_bad_arguments_before_launch():
                                    ctypes.c_void_p(1 << 20), None) == 1
     assert lib.ms_topk_f32(ctypes.c_void_p(1 << 20), 10, -1, ctypes.c_void_p(1 << 20), None) == 1
     assert b"negative" in lib.ms_last_error()
+    # the entry point without a workspace: a layer larger than its static
+    # scratch is refused before any device call
+    big = W.custom("big", 131072, 32, 8, [W.vs(1000, 6096)] * 32)
+    pb = _prob(big)
+    assert ms.ms_workspace_bytes(pb, ms.head_params(big.heads)) > ms.ms_noalloc_scratch_bytes()
+    _raw(3, "ms_sparse_attn_noalloc", ctypes.byref(pb), ms.head_params(big.heads), _vp(A), _vp(A), _vp(A), _vp(A),
+         None, None)
+    assert b"static scratch" in lib.ms_last_error()
+    _raw(1, "ms_sparse_attn_noalloc", pr, None, _vp(A), _vp(A), _vp(A), _vp(A), None, None)
 
 
 def _binding_rejects(fn, *args, match):
