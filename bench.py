@@ -31,10 +31,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # (a recorded traffic figure is reported only while these are unchanged).
 ATTN_SOURCES = ("sparse_attn.hip", "group_attn.hip", "api.hip", "internal.h")
 
-WORKLOADS = {"vs_4k": 0, "bs_32k": 1, "ashape_128k": 2, "mixed_128k": 3, "vs_1m": 4, "vs_1m_s": 5}
+WORKLOADS = {"vs_4k": 0, "bs_32k": 1, "ashape_128k": 2, "mixed_128k": 3, "vs_1m": 4, "vs_1m_s": 5, "vs_1m_b32": 6}
 # vs_1m_s is a diagnostic beside the five workloads: the 1M layer with a shared
 # query mean per KV group, under which the slashes through the planted columns
-# win the slash budget (kept fraction ~13% instead of ~31%).
+# win the slash budget (kept fraction ~13% instead of ~31%).  vs_1m_b32 is the
+# 1M layer (same inputs) with its heads indexed by 32-row query blocks.
 
 
 def parse():
@@ -43,9 +44,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="vs_1m", choices=sorted(WORKLOADS))
-    ap.add_argument("--side", default="mixed_128k,bs_32k,ashape_128k,vs_4k,vs_1m_s",
+    ap.add_argument("--side", default="mixed_128k,bs_32k,ashape_128k,vs_4k,vs_1m_s,vs_1m_b32",
                     help="comma-separated workloads reported beside the headline ('' = none)")
-    ap.add_argument("--side-steps", type=int, default=5, help="at most this many timed steps per side workload")
+    ap.add_argument("--side-steps", type=int, default=3, help="at most this many timed steps per side workload")
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -56,8 +57,8 @@ def parse():
 
 
 # ---------------------------------------------------------------- kept entries
-def _pairs_in_block(lo, hi, row0, torch):
-    """Causal pairs (i, j), i in [row0, row0+64), j in [lo, hi), j <= i."""
+def _pairs_in_block(lo, hi, row0, torch, rows=64):
+    """Causal pairs (i, j), i in [row0, row0+rows), j in [lo, hi), j <= i."""
     L = hi - lo
     x = row0 + 1 - lo
 
@@ -67,16 +68,17 @@ def _pairs_in_block(lo, hi, row0, torch):
         over = L * (L + 1) // 2 + (m - L) * L
         return torch.where(m <= L, tri, over)
 
-    return G(x + 63) - G(x - 1)
+    return G(x + rows - 1) - G(x - 1)
 
 
 def kept_entries(ms, prob, hp, heads, index, torch):
     """Exact number of (row, key) pairs the layer attends, summed over heads."""
     offs, _ = ms.ms_index_layout(prob, hp)
-    nb = prob.n // 64
     base = index.view(torch.int32)
     total = 0
     for h, (o_rp, o_r, o_cp, o_c) in enumerate(offs):
+        nb = ms.index_blocks(prob, hp, h)
+        rows = prob.n // nb  # 64, or 32 for a head indexed by 32-row blocks
         rp = base[o_rp // 4:o_rp // 4 + nb + 1].long()
         cp = base[o_cp // 4:o_cp // 4 + nb + 1].long()
         nr, nc = int(rp[-1]), int(cp[-1])
@@ -90,11 +92,11 @@ def kept_entries(ms, prob, hp, heads, index, torch):
         if nr:
             rng = base[o_r // 4:o_r // 4 + 2 * nr].long().view(-1, 2)
             blk = torch.repeat_interleave(torch.arange(nb, device=index.device), rp[1:] - rp[:-1])
-            total += int(_pairs_in_block(rng[:, 0], rng[:, 1], blk * 64, torch).sum())
+            total += int(_pairs_in_block(rng[:, 0], rng[:, 1], blk * rows, torch, rows).sum())
         if nc:
             col = base[o_c // 4:o_c // 4 + nc].long()
             blk = torch.repeat_interleave(torch.arange(nb, device=index.device), cp[1:] - cp[:-1])
-            total += int((blk * 64 + 64 - col).clamp(min=0, max=64).sum())
+            total += int((blk * rows + rows - col).clamp(min=0, max=rows).sum())
     return total
 
 
@@ -103,10 +105,10 @@ def block_keys(ms, prob, hp, index, torch):
     and column counts (the per-head kernel brings each of them into LDS once
     per block; 512 bytes apiece: a bf16 K row and an fp16 V row)."""
     offs, _ = ms.ms_index_layout(prob, hp)
-    nb = prob.n // 64
     base = index.view(torch.int32)
     total = cols = 0
-    for (o_rp, o_r, o_cp, o_c) in offs:
+    for h, (o_rp, o_r, o_cp, o_c) in enumerate(offs):
+        nb = ms.index_blocks(prob, hp, h)
         nr = int(base[o_rp // 4 + nb])
         nc = int(base[o_cp // 4 + nb])
         if nr:
@@ -124,7 +126,7 @@ def gather_stage(ms, torch, W, w, q, k, v, vert, aws, stream):
     gathered column, one bf16 K row and one fp16 V row (512 B) per (query
     block, column), brought in by the column path of the attention kernel.
     The timed call includes the fp16 copy of V the kernel reads."""
-    heads = [W.vs(p.n_vertical, 0) for p in w.heads]
+    heads = [W.vs(p.n_vertical, 0, block=p.block) for p in w.heads]
     prob, hp = ms.problem(w.n, w.n_q_heads, w.n_kv_heads), ms.head_params(heads)
     index = ms.empty_workspace(ms.ms_index_bytes(prob, hp))
     empty = torch.empty(1, dtype=torch.int32, device="cuda")
@@ -139,8 +141,7 @@ def gather_stage(ms, torch, W, w, q, k, v, vert, aws, stream):
     t = e0.elapsed_time(e1)
     offs, _ = ms.ms_index_layout(prob, hp)
     base = index.view(torch.int32)
-    nb = w.n // 64
-    cols = sum(int(base[o[2] // 4 + nb]) for o in offs)
+    cols = sum(int(base[o[2] // 4 + ms.index_blocks(prob, hp, h)]) for h, o in enumerate(offs))
     del index, out
     return {"ms": t, "col_keys": cols}
 
@@ -261,7 +262,7 @@ def _kept_np(bidx, b):
 
 
 # ---------------------------------------------------------------- main
-def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
+def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense, dense_known=None):
     w = W.config(cid)
     q, k, v = W.generate(w, device="cuda")
     prob, hp = ms.problem(w.n, w.n_q_heads, w.n_kv_heads), ms.head_params(w.heads)
@@ -338,7 +339,15 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
     if all(p.pattern == W.VERTICAL_SLASH for p in w.heads) and any(p.n_vertical > 0 for p in w.heads):
         res["gather"] = gather_stage(ms, torch, W, w, q, k, v, vert, aws, stream)
     del ws
-    if do_dense:
+    if do_dense and dense_known is not None:
+        # the same shapes and inputs as a layer already timed: its dense
+        # kernel time and log-sum-exps serve again
+        res["dense_ms"] = dense_known["ms"]
+        rec = torch.empty(w.n_q_heads, dtype=torch.float32, device="cuda")
+        ms.ms_attention_recall(prob, lse_s, dense_known["lse"], rec)
+        torch.cuda.synchronize()
+        res["recall"] = rec.cpu().tolist()
+    elif do_dense:
         dout = torch.empty_like(q)
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         # untimed first call: warms the kernel and gives the dense log-sum-exps
@@ -349,7 +358,7 @@ def run_layer(ms, torch, W, cid, steps, warmup, dense_steps, do_dense):
         ms.ms_attention_recall(prob, lse_s, lse_d, rec)
         torch.cuda.synchronize()
         res["recall"] = rec.cpu().tolist()
-        del lse_d
+        res["dense_lse"] = lse_d
         d0.record(stream)
         for _ in range(dense_steps):
             ms.ms_dense_attn(prob, q, k, v, dout, aws)
@@ -442,16 +451,22 @@ def main():
                            a.cpu_seconds)
     for key in ("q", "k", "v"):
         main_r.pop(key)
+    known = {"ms": main_r["dense_ms"], "lse": main_r.pop("dense_lse")} if "dense_ms" in main_r else None
     torch.cuda.empty_cache()
 
     side = {}
     for name in [x for x in a.side.split(",") if x and x != a.workload]:
         print(f"[bench] side workload {name}", file=sys.stderr, flush=True)
+        # vs_1m_b32 is the headline's layer (same inputs) with other index blocks
+        reuse = known if (a.workload, name) == ("vs_1m", "vs_1m_b32") else None
         r2 = run_layer(ms, torch, W, WORKLOADS[name], min(a.steps, a.side_steps), min(a.warmup, 1), a.dense_steps,
-                       not a.no_dense)
+                       not a.no_dense, reuse)
+        r2.pop("dense_lse", None)
         for key in ("q", "k", "v"):
             r2.pop(key)
         side[name] = summary(r2)
+        if reuse is not None:
+            side[name]["note"] = "dense time and log-sum-exps of the headline layer (same shapes and inputs)"
         if name == "vs_1m_s":
             side[name]["note"] = ("diagnostic, not one of the five workloads: vs_1m plus a shared query mean "
                                   "(std 0.5) per KV group, so the slashes through the planted columns are selected")

@@ -24,7 +24,7 @@ __all__ = [
     "ms_index_layout", "ms_attn_workspace_bytes", "ms_workspace_bytes", "ms_estimate_vs",
     "ms_estimate_block", "ms_build_index", "ms_sparse_attn_indexed", "ms_sparse_attn",
     "ms_dense_attn", "ms_topk_f32", "ms_version", "read_index", "empty_workspace",
-    "ms_sparse_attn_noalloc", "ms_noalloc_scratch_bytes", "ms_attention_recall",
+    "ms_sparse_attn_noalloc", "ms_noalloc_scratch_bytes", "ms_attention_recall", "index_blocks",
     "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "DENSE", "GRID", "OUT_BF16", "OUT_F32",
 ]
 
@@ -347,15 +347,23 @@ def ms_attention_recall(prob, lse_sparse: torch.Tensor, lse_dense: torch.Tensor,
                                       _stream(stream)))
 
 
+def index_blocks(prob, heads, h: int) -> int:
+    """Blocks of head h's CSR: the call's query blocks, NBq = n/64 - q_block0,
+    or 2 NBq for a Vertical-Slash head indexed by 32-row blocks."""
+    nb = prob.n // 64 - prob.q_block0
+    p = heads[h]
+    return 2 * nb if p.pattern == VERTICAL_SLASH and p.block == 32 else nb
+
+
 def read_index(prob, heads, index: torch.Tensor):
     """Copies the CSR index of every head to the host: a list over heads of
-    (rng_ptr [NBq+1], rng [R, 2], col_ptr [NBq+1], col [C]) int32 numpy arrays
-    over the call's query blocks (NBq = n/64 - q_block0)."""
+    (rng_ptr [NB+1], rng [R, 2], col_ptr [NB+1], col [C]) int32 numpy arrays
+    over the head's query blocks (NB = index_blocks(prob, heads, h))."""
     offs, _ = ms_index_layout(prob, heads)
     host = index.cpu().numpy()
-    nb = prob.n // 64 - prob.q_block0
     out = []
-    for (o_rp, o_r, o_cp, o_c) in offs:
+    for h, (o_rp, o_r, o_cp, o_c) in enumerate(offs):
+        nb = index_blocks(prob, heads, h)
         rp = host[o_rp:o_rp + 4 * (nb + 1)].view("int32").copy()
         cp = host[o_cp:o_cp + 4 * (nb + 1)].view("int32").copy()
         r = host[o_r:o_r + 8 * int(rp[-1])].view("int32").reshape(-1, 2).copy()

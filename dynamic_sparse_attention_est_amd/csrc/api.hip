@@ -87,12 +87,14 @@ struct Plan {
   int hpw = 1;
   std::vector<GroupDesc> gdesc;  // chunks served by the grouped sparse kernel
   int n_wide = 0;                // the first n_wide chunks run with hpw heads per workgroup, the rest with 2
-  std::vector<int16_t> solo;     // heads served one by one
+  std::vector<int16_t> solo;     // heads served one by one (64-row blocks)
+  std::vector<int16_t> solo32;   // heads served one by one with 32-row blocks
   size_t index_bytes = 0;
   // attention workspace: fp16 V copy, then the key-segment records (without
   // params: the most any head set needs)
   size_t v16_bytes = 0, attn_bytes = 0;
-  std::vector<int16_t> solo_seg;  // heads served one by one, by key segments
+  std::vector<int16_t> solo_seg;    // heads served one by one, by key segments (64-row blocks)
+  std::vector<int16_t> solo32_seg;  // the same with 32-row blocks
   int seg_shift = 0;
   size_t seg_part_off = 0, seg_part_bytes = 0;
   // one-shot workspace
@@ -122,6 +124,9 @@ ms_status validate(const ms_problem* prob, const ms_head_params* params, bool ne
     switch (q.pattern) {
       case MS_VERTICAL_SLASH:
         if (q.last_q != kLastQ) return fail(MS_ERR_UNSUPPORTED, "head %d: last_q = %d, only 64 is supported", h, q.last_q);
+        if (q.block != 0 && q.block != 32 && q.block != kBM)
+          return fail(MS_ERR_UNSUPPORTED, "head %d: block = %d, Vertical-Slash query blocks are 64 (or 0) or 32 rows",
+                      h, q.block);
         if (q.n_vertical < 0 || q.n_vertical > n) return fail(MS_ERR_INVALID_ARG, "head %d: n_vertical = %d out of 0..n", h, q.n_vertical);
         if (q.n_slash < 0 || q.n_slash > n) return fail(MS_ERR_INVALID_ARG, "head %d: n_slash = %d out of 0..n", h, q.n_slash);
         break;
@@ -152,17 +157,27 @@ ms_status validate(const ms_problem* prob, const ms_head_params* params, bool ne
   return MS_OK;
 }
 
+// Query rows per block of a head's CSR: 32 for a Vertical-Slash head that
+// asks for them, 64 otherwise.
+int head_rows(const ms_head_params& q) { return q.pattern == MS_VERTICAL_SLASH && q.block == 32 ? 32 : kBM; }
+
 // Per-head capacities of the CSR, the sums over query blocks of the bounds
 // the index kernels clamp to.
 std::pair<int64_t, int64_t> head_caps(const ms_head_params& q, int64_t qb0, int64_t nb) {
   int64_t r = 0, c = 0;
+  if (q.pattern == MS_VERTICAL_SLASH) {
+    // run starts of the sorted offsets are more than `rows` apart
+    const int64_t rows = head_rows(q), per = kBM / rows;
+    for (int64_t b = qb0 * per; b < nb * per; ++b) {
+      const int64_t last = b * rows + rows - 1;
+      r += std::min<int64_t>(q.n_slash, last / (rows + 1) + 1);
+      c += std::min<int64_t>(q.n_vertical, last + 1);
+    }
+    return {r, c};
+  }
   for (int64_t b = qb0; b < nb; ++b) {
     const int64_t last = b * kBM + kBM - 1;
     switch (q.pattern) {
-      case MS_VERTICAL_SLASH:
-        r += std::min<int64_t>(q.n_slash, last / 65 + 1);
-        c += std::min<int64_t>(q.n_vertical, last + 1);
-        break;
       case MS_BLOCK_SPARSE:
         r += std::min<int64_t>(std::min<int64_t>(q.top_k_blocks, b + 1), b / 2 + 1);
         break;
@@ -187,7 +202,7 @@ double expected_density(const ms_head_params& q, int64_t n) {
   const double nd = (double)n;
   switch (q.pattern) {
     case MS_VERTICAL_SLASH:
-      return std::min(1.0, 1.0 - std::exp(-64.0 * q.n_slash / nd) + q.n_vertical / nd);
+      return std::min(1.0, 1.0 - std::exp(-(double)head_rows(q) * q.n_slash / nd) + q.n_vertical / nd);
     case MS_BLOCK_SPARSE: {
       const int64_t nb = n / kBM;
       double s = 0.0;
@@ -301,7 +316,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     const int a = q.pattern == MS_VERTICAL_SLASH ? q.n_vertical : q.pattern == MS_BLOCK_SPARSE ? q.top_k_blocks : 0;
     const int b = q.pattern == MS_VERTICAL_SLASH ? q.n_slash : 0;
     const bool gr = q.pattern == MS_GRID;
-    const auto key = std::make_tuple(q.pattern, a, b, gr ? q.grid_stride : 0, gr ? q.grid_frames : 0,
+    const auto key = std::make_tuple(q.pattern, a, b, gr ? q.grid_stride : head_rows(q), gr ? q.grid_frames : 0,
                                      gr ? q.grid_width : 0);
     auto it = memo.find(key);
     if (it == memo.end()) it = memo.emplace(key, head_caps(q, P.qb0, P.nb)).first;
@@ -311,6 +326,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       return fail(MS_ERR_UNSUPPORTED, "head %d: index capacity exceeds int32", h);
     HeadDesc& d = P.desc[h];
     d.pattern = q.pattern;
+    d.qrows = head_rows(q);
     d.vs_slot = P.vs_slot[h];
     d.bs_slot = P.bs_slot[h];
     if (q.pattern == MS_VERTICAL_SLASH) {
@@ -330,9 +346,10 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     d.vert_off = P.vert_off[h];
     d.slash_off = P.slash_off[h];
     d.blk_off = P.blk_off[h];
-    d.rng_ptr_off = (int64_t)take((size_t)(P.nbq + 1) * 4);
+    const int64_t nblk = P.nbq * (kBM / d.qrows);  // CSR blocks of this head
+    d.rng_ptr_off = (int64_t)take((size_t)(nblk + 1) * 4);
     d.rng_off = (int64_t)take((size_t)P.cap_r[h] * 8);
-    d.col_ptr_off = (int64_t)take((size_t)(P.nbq + 1) * 4);
+    d.col_ptr_off = (int64_t)take((size_t)(nblk + 1) * 4);
     d.col_off = (int64_t)take((size_t)P.cap_c[h] * 4);
     d.run_off = (int64_t)take(q.pattern == MS_VERTICAL_SLASH ? (size_t)(q.n_slash + 1) * 4 : 4);
   }
@@ -371,7 +388,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     for (int j = 0; j < P.grp; ++j) {
       const int h = kv * P.grp + j;
       const int pat = P.p[h].pattern;
-      if (P.hpw > 1 && expected_density(P.p[h], P.n) >= 0.5)
+      if (head_rows(P.p[h]) != kBM)
+        P.solo32.push_back((int16_t)h);  // 32-row blocks: the per-head kernel only
+      else if (P.hpw > 1 && expected_density(P.p[h], P.n) >= 0.5)
         dense_heads.push_back(h);
       else if (P.hpw > 1 && (pat == MS_A_SHAPE || pat == MS_GRID))
         fixed_heads.push_back(h);
@@ -416,16 +435,19 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   // keys from HBM.  Short, local key sets (A-shape, small Block-Sparse
   // budgets) stay whole.
   P.solo_seg.clear();
+  P.solo32_seg.clear();
   if (P.n >= kSegMinN) {
-    std::vector<int16_t> keep;
-    for (int16_t h : P.solo)
-      (expected_density(P.p[h], P.n) * 0.5 * (double)P.n >= (double)(int64_t{1} << kSegShift) ? P.solo_seg : keep)
-          .push_back(h);
-    P.solo = keep;
+    for (auto [solo, seg] : {std::make_pair(&P.solo, &P.solo_seg), std::make_pair(&P.solo32, &P.solo32_seg)}) {
+      std::vector<int16_t> keep;
+      for (int16_t h : *solo)
+        (expected_density(P.p[h], P.n) * 0.5 * (double)P.n >= (double)(int64_t{1} << kSegShift) ? *seg : keep)
+            .push_back(h);
+      *solo = keep;
+    }
   }
   // Workgroups go round-robin over the 8 XCDs, so order each list to keep
   // the heads of one KV head on one XCD when the count allows.
-  for (std::vector<int16_t>* l : {&P.solo, &P.solo_seg}) {
+  for (std::vector<int16_t>* l : {&P.solo, &P.solo_seg, &P.solo32, &P.solo32_seg}) {
     if (l->size() % 8 != 0 || l->empty()) continue;
     const size_t per = l->size() / 8;
     std::vector<int16_t> ordered(l->size());
@@ -433,10 +455,11 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     *l = ordered;
   }
   P.attn_bytes = P.v16_bytes;
-  if (!P.solo_seg.empty()) {
+  if (!P.solo_seg.empty() || !P.solo32_seg.empty()) {
+    // the two lists run one after the other and share the record space
     P.seg_shift = kSegShift;
     P.seg_part_off = P.v16_bytes;
-    P.seg_part_bytes = seg_record_bytes(P.n, P.nbq, (int)P.solo_seg.size());
+    P.seg_part_bytes = seg_record_bytes(P.n, P.nbq, (int)std::max(P.solo_seg.size(), P.solo32_seg.size()));
     P.attn_bytes += align_up(P.seg_part_bytes);
   }
   P.index_bytes = off;
@@ -619,28 +642,28 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
       HIP_TRY(launch_group_sparse(a, chunks + P.n_wide, 2, s), "attention launch");
     }
   }
-  if (!P.solo.empty()) {
-    a.n_list = (int)P.solo.size();
-    for (size_t i = 0; i < P.solo.size(); ++i) a.list[i] = P.solo[i];
-    HIP_TRY(launch_sparse_attn(a, s), "attention launch");
+  for (auto [list, rows] : {std::make_pair(&P.solo, kBM), std::make_pair(&P.solo32, 32)}) {
+    if (list->empty()) continue;
+    a.n_list = (int)list->size();
+    for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
+    HIP_TRY(launch_sparse_attn(a, rows, s), "attention launch");
   }
-  if (!P.solo_seg.empty()) {
-    a.n_list = (int)P.solo_seg.size();
-    for (size_t i = 0; i < P.solo_seg.size(); ++i) a.list[i] = P.solo_seg[i];
-    {
-      // Chunks of query blocks whose records fit the workspace, each
-      // followed by the combination of its records.
-      const int64_t nseg = ((P.n - 1) >> P.seg_shift) + 1;
-      const size_t per_block = (size_t)nseg * a.n_list * kSegRecFloats * 4;
-      const int64_t cb = std::min<int64_t>(P.nbq, (int64_t)(P.seg_part_bytes / per_block));
-      a.part = reinterpret_cast<float*>(attn_ws + P.seg_part_off);
-      a.seg_shift = P.seg_shift;
-      a.seg_n = (int)nseg;
-      for (int64_t b0 = 0; b0 < P.nbq; b0 += cb) {
-        a.seg_b0 = (int)b0;
-        a.seg_nb = (int)std::min<int64_t>(cb, P.nbq - b0);
-        HIP_TRY(launch_sparse_attn_seg(a, s), "attention launch");
-      }
+  for (auto [list, rows] : {std::make_pair(&P.solo_seg, kBM), std::make_pair(&P.solo32_seg, 32)}) {
+    if (list->empty()) continue;
+    a.n_list = (int)list->size();
+    for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
+    // Chunks of query blocks whose records fit the workspace, each followed
+    // by the combination of its records.
+    const int64_t nseg = ((P.n - 1) >> P.seg_shift) + 1;
+    const size_t per_block = (size_t)nseg * a.n_list * kSegRecFloats * 4;
+    const int64_t cb = std::min<int64_t>(P.nbq, (int64_t)(P.seg_part_bytes / per_block));
+    a.part = reinterpret_cast<float*>(attn_ws + P.seg_part_off);
+    a.seg_shift = P.seg_shift;
+    a.seg_n = (int)nseg;
+    for (int64_t b0 = 0; b0 < P.nbq; b0 += cb) {
+      a.seg_b0 = (int)b0;
+      a.seg_nb = (int)std::min<int64_t>(cb, P.nbq - b0);
+      HIP_TRY(launch_sparse_attn_seg(a, rows, s), "attention launch");
     }
   }
   return MS_OK;

@@ -18,10 +18,14 @@
 //   A-shape: [0, min(sink, 64b+64)) and [max(0, 64b-window+1), 64b+64), merged
 //     when they touch (the per-row window is applied by the attention kernel).
 //   Dense: [0, 64b+64).
+// A Vertical-Slash head may ask for 32-row query blocks: its CSR then lists
+// the 2 NBq blocks of 32 rows, each built by the same rules with 32 in place
+// of 64 (a slash keeps [max(0, 32b-o), 32b+32-o), runs break at gaps > 32),
+// and the workgroup of a 64-row block writes both of its halves.
 // Three launches over (query block, head): count -> per-head scan -> fill.
 // Counts are clamped to per-block capacities that the host also uses to size
 // the arena, so malformed selections can never write past it, and every value
-// written is clamped into [0, 64b+64).
+// written is clamped into [0, end of the block).
 #include "block_scan.h"
 #include "internal.h"
 
@@ -57,11 +61,12 @@ __device__ __forceinline__ int lower_bound(const int32_t* a, int n, int x) {  //
   return lo;
 }
 
-// Per-block capacities (same formulas as the host's arena sizing).
+// Per-block capacities (same formulas as the host's arena sizing); b counts
+// blocks of the head's own height (d.qrows rows for Vertical-Slash heads).
 __device__ __forceinline__ int cap_ranges(const HeadDesc& d, int b) {
   const int last = b * kBM + kBM - 1;
   switch (d.pattern) {
-    case MS_VERTICAL_SLASH: return min(d.p1, last / 65 + 1);
+    case MS_VERTICAL_SLASH: return min(d.p1, (b * d.qrows + d.qrows - 1) / (d.qrows + 1) + 1);
     case MS_BLOCK_SPARSE: return min(min(d.p0, b + 1), b / 2 + 1);
     case MS_A_SHAPE: return 2;
     case MS_GRID: return min(d.p2, (last + d.p3) / d.p0) + 1;
@@ -69,7 +74,7 @@ __device__ __forceinline__ int cap_ranges(const HeadDesc& d, int b) {
   }
 }
 __device__ __forceinline__ int cap_cols(const HeadDesc& d, int b) {
-  return d.pattern == MS_VERTICAL_SLASH ? min(d.p0, b * kBM + kBM) : 0;
+  return d.pattern == MS_VERTICAL_SLASH ? min(d.p0, b * d.qrows + d.qrows) : 0;
 }
 
 struct IdxArgs {
@@ -82,8 +87,9 @@ struct IdxArgs {
   int32_t qb0;            // first query block
 };
 
-// Runs of the sorted slash offsets (consecutive offsets closer than 65 share a
-// run): run[0] = number of runs, run[1 + r] = index of run r's first offset.
+// Runs of the sorted slash offsets (consecutive offsets at most the block
+// height apart share a run): run[0] = number of runs, run[1 + r] = index of
+// run r's first offset.
 __global__ __launch_bounds__(kT) void vs_template(IdxArgs a) {
   __shared__ int warp_sum[kT / 64];
   const HeadDesc d = a.table[blockIdx.x];
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(kT) void vs_template(IdxArgs a) {
   int base = 0;
   for (int s0 = 0; s0 < ks; s0 += kT) {
     const int i = s0 + threadIdx.x;
-    const int start = i < ks && (i == 0 || S[i] - S[i - 1] > kBM);
+    const int start = i < ks && (i == 0 || S[i] - S[i - 1] > d.qrows);
     int tot;
     const int pos = base + block_excl_scan<kT>(start, warp_sum, &tot);
     if (start) run[1 + pos] = i;
@@ -115,52 +121,73 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
   int32_t* col_ptr = reinterpret_cast<int32_t*>(a.arena + d.col_ptr_off);
   int2* rng = reinterpret_cast<int2*>(a.arena + d.rng_off);
   int32_t* col = reinterpret_cast<int32_t*>(a.arena + d.col_off);
-  const int rcap = cap_ranges(d, b), ccap = cap_cols(d, b);
   int nr = 0, nc = 0;
   int rbase = 0, cbase = 0, rlim = 0, clim = 0;
-  if (kFill) {
-    rbase = rng_ptr[bl];
-    rlim = rng_ptr[bl + 1] - rbase;
-    cbase = col_ptr[bl];
-    clim = col_ptr[bl + 1] - cbase;
-  }
+  auto csr_block = [&](int cb) {  // this workgroup's CSR block cb: its slots
+    if (kFill) {
+      rbase = rng_ptr[cb];
+      rlim = rng_ptr[cb + 1] - rbase;
+      cbase = col_ptr[cb];
+      clim = col_ptr[cb + 1] - cbase;
+    }
+  };
 
   if (d.pattern == MS_VERTICAL_SLASH) {
     const int32_t* S = a.slash + d.slash_off;
     const int32_t* V = a.vert + d.vert_off;
     const int32_t* run = reinterpret_cast<const int32_t*>(a.arena + d.run_off);
     const int ks = d.p1, kv = d.p0, nruns = run[0];
-    const int ub = upper_bound(S, ks, last);            // offsets that reach this block
-    nr = ub == 0 ? 0 : upper_bound(run + 1, nruns, ub - 1);
-    nr = min(nr, rcap);
-    if (kFill) {
-      for (int p = tid; p < min(nr, rlim); p += kT) {
-        const int r = nr - 1 - p;  // runs of larger offsets give lower keys
-        const int first = run[1 + r];
-        const int stop = min(r + 1 < nruns ? run[2 + r] : ks, ub);
-        const int lo = min(max(0, row0 - S[stop - 1]), end);
-        const int hi = min(max(lo, row0 + kBM - S[first]), end);
-        rng[rbase + p] = make_int2(lo, hi);
+    const int rows = d.qrows, per = kBM / rows;
+    // the 64-row block's one or two CSR blocks of `rows` rows
+    for (int half = 0; half < per; ++half) {
+      const int cb = bl * per + half;           // CSR block
+      const int gb = b * per + half;            // query block of `rows` rows in the sequence
+      const int hrow0 = gb * rows, hlast = hrow0 + rows - 1, hend = hrow0 + rows;
+      csr_block(cb);
+      const int ub = upper_bound(S, ks, hlast);  // offsets that reach this block
+      int hr = ub == 0 ? 0 : upper_bound(run + 1, nruns, ub - 1);
+      hr = min(hr, cap_ranges(d, gb));
+      if (kFill) {
+        for (int p = tid; p < min(hr, rlim); p += kT) {
+          const int r = hr - 1 - p;  // runs of larger offsets give lower keys
+          const int first = run[1 + r];
+          const int stop = min(r + 1 < nruns ? run[2 + r] : ks, ub);
+          const int lo = min(max(0, hrow0 - S[stop - 1]), hend);
+          const int hi = min(max(lo, hrow0 + rows - S[first]), hend);
+          rng[rbase + p] = make_int2(lo, hi);
+        }
+      }
+      const int ubv = upper_bound(V, kv, hlast);
+      int cnt = 0;
+      for (int s0 = 0; s0 < ubv; s0 += kT) {
+        const int i = s0 + tid;
+        int keep = 0;
+        int j = 0;
+        if (i < ubv) {
+          j = V[i];
+          const int lbo = lower_bound(S, ks, max(0, hrow0 - j));
+          keep = j >= 0 && !(lbo < ks && S[lbo] <= hlast - j);
+        }
+        int tot;
+        const int pos = cnt + block_excl_scan<kT>(keep, warp_sum, &tot);
+        if (kFill && keep && pos < clim) col[cbase + pos] = j;
+        cnt += tot;
+      }
+      const int hc = min(cnt, cap_cols(d, gb));
+      if (!kFill && tid == 0) {
+        rng_ptr[cb + 1] = hr;
+        col_ptr[cb + 1] = hc;
+        if (cb == 0) {
+          rng_ptr[0] = 0;
+          col_ptr[0] = 0;
+        }
       }
     }
-    const int ubv = upper_bound(V, kv, last);
-    int cnt = 0;
-    for (int s0 = 0; s0 < ubv; s0 += kT) {
-      const int i = s0 + tid;
-      int keep = 0;
-      int j = 0;
-      if (i < ubv) {
-        j = V[i];
-        const int lbo = lower_bound(S, ks, max(0, row0 - j));
-        keep = j >= 0 && !(lbo < ks && S[lbo] <= last - j);
-      }
-      int tot;
-      const int pos = cnt + block_excl_scan<kT>(keep, warp_sum, &tot);
-      if (kFill && keep && pos < clim) col[cbase + pos] = j;
-      cnt += tot;
-    }
-    nc = min(cnt, ccap);
-  } else if (d.pattern == MS_BLOCK_SPARSE) {
+    return;
+  }
+  csr_block(bl);
+  const int rcap = cap_ranges(d, b);
+  if (d.pattern == MS_BLOCK_SPARSE) {
     const int k = d.p0;
     const int32_t* B = a.blocks + d.blk_off + (int64_t)bl * k;
     const int cnt = min(k, b + 1);  // leading entries hold the selection
@@ -259,19 +286,21 @@ __global__ __launch_bounds__(kT) void index_pass(IdxArgs a) {
   }
 }
 
-// In-place inclusive scan of ptr[1..nb] (ptr[0] = 0) for both CSR pointers.
+// In-place inclusive scan of ptr[1..nblk] (ptr[0] = 0) for both CSR pointers
+// (nblk = the call's query blocks of the head's own height).
 __global__ __launch_bounds__(1024) void index_scan(IdxArgs a) {
   __shared__ int warp_sum[1024 / 64];
   const HeadDesc d = a.table[blockIdx.x];
+  const int nblk = d.pattern == MS_VERTICAL_SLASH ? a.nb * (kBM / d.qrows) : a.nb;
   for (int which = 0; which < 2; ++which) {
     int32_t* ptr = reinterpret_cast<int32_t*>(a.arena + (which ? d.col_ptr_off : d.rng_ptr_off));
     int carry = 0;
-    for (int s0 = 0; s0 < a.nb; s0 += 1024) {
+    for (int s0 = 0; s0 < nblk; s0 += 1024) {
       const int i = s0 + threadIdx.x;
-      const int x = i < a.nb ? ptr[1 + i] : 0;
+      const int x = i < nblk ? ptr[1 + i] : 0;
       int tot;
       const int ex = block_excl_scan<1024>(x, warp_sum, &tot);
-      if (i < a.nb) ptr[1 + i] = carry + ex + x;
+      if (i < nblk) ptr[1 + i] = carry + ex + x;
       carry += tot;
     }
   }

@@ -30,7 +30,7 @@ struct HeadDesc {
   int32_t vs_slot;   // rank among VS heads (-1 if not VS)
   int32_t bs_slot;   // rank among BS heads (-1 if not BS)
   int32_t p2, p3;    // GRID: frames, width
-  int32_t pad0;
+  int32_t qrows;     // query rows per block of the head's CSR: 64, or 32 for a VS head that asks for it
   int64_t vert_off;  // int32 elements into the packed vert array (VS)
   int64_t slash_off; // into the packed slash array (VS)
   int64_t blk_off;   // into the packed blocks array (BS)
@@ -153,10 +153,13 @@ struct AttnArgs {
 // per row (-inf for a row with no key in the segment).
 constexpr int kSegRowFloats = kBM * kD;
 constexpr int kSegRecFloats = kSegRowFloats + kBM;
-hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s);
+// rows: query rows per block of the listed heads' CSR (64 or 32; a 32-row
+// block is one wavefront's work item).
+hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s);
 // Key-segment mode: partial records of the chunk, then their combination
-// into out / lse.
-hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s);
+// into out / lse.  With 32-row blocks two work items fill the two halves of
+// one 64-row record, so the combination is the same.
+hipError_t launch_sparse_attn_seg(const AttnArgs& a, int rows, hipStream_t s);
 // Full causal attention, query heads that share a KV head served together.
 hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s);
 // Sparse attention over the union index (groups: device table of the

@@ -4,7 +4,8 @@
 // pages' kernels build on).
 //
 // Work item: one 64-row query block of one Q head = one workgroup of two
-// wavefronts, each owning 32 rows.  The block's keys are its ranges, cut into
+// wavefronts, each owning 32 rows (a head indexed by 32-row query blocks: one
+// 32-row block = one workgroup of one wavefront, which loads its tiles alone).  The block's keys are its ranges, cut into
 // pieces of up to 32 consecutive keys, then its column list in pieces of up to
 // 32 gathered keys.  Both waves share one LDS copy of a piece's K and V rows,
 // written by buffer loads that go straight to LDS (no staging registers).
@@ -46,7 +47,6 @@ constexpr int kKP = 32;                       // keys per piece
 constexpr int kRowBytes = kD * 2;             // one K or V row
 constexpr int kTileBytes = kKP * kRowBytes;   // one K or V tile (8 KiB)
 constexpr float kLag = 8.f;                   // allowed lag of the running max (log2 units)
-constexpr int kThreads = 128;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -150,44 +150,55 @@ __device__ __forceinline__ int col_key(const Piece& p, global_int* col, int row)
   return col[p.start + min(row, p.count - 1)];
 }
 
+// kL loads per wave and tile: kL = 4 when two waves share a tile (rows 16w ..
+// 16w + 15 from wave w), 8 when one wave fills all 32 rows.
+template <int kL>
 struct ColKeys {
-  int k[4];  // keys of rows 16w + 4j + lane/16
+  int k[kL];  // keys of rows (32 / (8 / kL)) w + 4j + lane/16
 };
 
+template <int kL>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int w, const uint32_t* lofs,
-                                          const uint32_t* cofs, const Piece& p, const ColKeys& ck) {
-  char* const base = tile + 4096 * w;
+                                          const uint32_t* cofs, const Piece& p, const ColKeys<kL>& ck) {
+  char* const base = tile + 256 * 4 * kL * w;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kL; ++j) {
     const uint32_t off = p.is_col ? (uint32_t)ck.k[j] * (uint32_t)kRowBytes + cofs[j]
                                   : (uint32_t)p.start * (uint32_t)kRowBytes + lofs[j];
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16, off, 0, 0, 0);
   }
 }
 
-// Longest query blocks first (causal work grows with b); within a block
-// index, workgroup x takes head list[x % n_list].  Workgroups are dealt
-// round-robin over the 8 XCDs, so the host orders the list to keep the Q
-// heads of one KV head on one XCD, whose L2 then serves their common K/V rows.
+// Work items are the listed heads' query blocks of kRows rows (the blocks of
+// their CSR; per = 64 / kRows of them per 64-row block).  Longest blocks
+// first (causal work grows with the block); within a block index, workgroup x
+// takes head list[x % n_list].  Workgroups are dealt round-robin over the 8
+// XCDs, so the host orders the list to keep the Q heads of one KV head on one
+// XCD, whose L2 then serves their common K/V rows.  b: the item's CSR block.
+template <int kRows>
 __device__ __forceinline__ void map_work(int x, const AttnArgs& a, int& h, int& b) {
   const int bi = x / a.n_list, hi = x - bi * a.n_list;
-  b = a.nb - 1 - bi;
+  b = a.nb * (kBM / kRows) - 1 - bi;
   h = a.list[hi];
 }
 
-// Key-segment mode: workgroup x takes segment x / (seg_nb * n_list) of block
-// seg_b0 + seg_nb - 1 - bl and head list[hi], (bl, hi) from the rest, so the
-// workgroups in flight share one segment of every KV head's K/V rows; slot is
-// its partial record.
+// Key-segment mode: workgroup x takes segment x / (items per segment) of the
+// item bl-th from the top of the chunk's 64-row blocks [seg_b0, seg_b0 +
+// seg_nb) and head list[hi], (bl, hi) from the rest, so the workgroups in
+// flight share one segment of every KV head's K/V rows.  slot is the partial
+// record of the item's 64-row block; a 32-row item fills half of it.
+template <int kRows>
 __device__ __forceinline__ void map_work_seg(int x, const AttnArgs& a, int& h, int& b, int& sg, int& slot) {
-  const int per = a.seg_nb * a.n_list;
-  sg = __builtin_amdgcn_readfirstlane(x / per);
-  const int y = x - sg * per;
+  constexpr int per = kBM / kRows;
+  const int items = a.seg_nb * per * a.n_list;
+  sg = __builtin_amdgcn_readfirstlane(x / items);
+  const int y = x - sg * items;
   const int bl = __builtin_amdgcn_readfirstlane(y / a.n_list);
   const int hi = y - bl * a.n_list;
-  b = a.seg_b0 + a.seg_nb - 1 - bl;
+  b = (a.seg_b0 + a.seg_nb) * per - 1 - bl;
   h = a.list[hi];
-  slot = (bl * a.n_list + hi) * a.seg_n + sg;
+  const int bl64 = a.seg_b0 + a.seg_nb - 1 - b / per;  // the 64-row block's place in the chunk, from the top
+  slot = (bl64 * a.n_list + hi) * a.seg_n + sg;
 }
 
 // Four lower bounds at once: for search j, the first i in [lo_j, hi_j) with
@@ -237,8 +248,11 @@ __device__ __forceinline__ void wave_lower_bounds(Bound (&s)[4], const int2* rng
   }
 }
 
-template <bool kSeg>
+template <bool kSeg, int kRows>
 __device__ __forceinline__ void attn_body(const AttnArgs& a) {
+  constexpr int kWaves = kRows / 32;  // one wavefront per 32 query rows
+  constexpr int kL = 4 * (2 / kWaves);  // load-to-LDS instructions per wave and tile
+  constexpr int kPer = kBM / kRows;     // work items per 64-row block
   __shared__ __attribute__((aligned(1024))) char kb0[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char kb1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) char vb0[kTileBytes];
@@ -252,17 +266,17 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   int h, b, sg = 0;
   if (kSeg) {
     int slot;
-    map_work_seg(blockIdx.x, a, h, b, sg, slot);
+    map_work_seg<kRows>(blockIdx.x, a, h, b, sg, slot);
   } else
-    map_work(blockIdx.x, a, h, b);
+    map_work<kRows>(blockIdx.x, a, h, b);
   const int kvh = h / a.grp;
   const int64_t n = a.n;
-  // b indexes the call's query blocks (and the CSR); row0 is the block's
-  // first query row in the sequence, qrow0 its row in Q and out.
-  const int row0 = (a.qb0 + b) * kBM;
-  const int64_t qrow0 = (int64_t)b * kBM;
+  // b indexes the call's query blocks of kRows rows (and the CSR); row0 is
+  // the block's first query row in the sequence, qrow0 its row in Q and out.
+  const int row0 = (a.qb0 * kPer + b) * kRows;
+  const int64_t qrow0 = (int64_t)b * kRows;
   const int seg_lo = sg << a.seg_shift;
-  if (kSeg && seg_lo > row0 + kBM - 1) return;  // past the block's last key: no record
+  if (kSeg && seg_lo > row0 + kRows - 1) return;  // past the block's last key: no record
   const int seg_hi = seg_lo + (1 << a.seg_shift);
 
   // Q fragments: B operand of S^T = K Q^T; lane holds row l32 of this wave's
@@ -312,7 +326,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     }
   } else {
     it.lo = kSeg ? seg_lo : 0;
-    it.hi = kSeg ? min(seg_hi, row0 + kBM) : row0 + kBM;
+    it.hi = kSeg ? min(seg_hi, row0 + kRows) : row0 + kRows;
   }
 
   // Byte size of one KV head (<= 2^31 for n <= 2^23), taken as unsigned by the
@@ -329,10 +343,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   // and chunk (lane%16) ^ swz(rw_j); lofs = row offset + chunk offset,
   // cofs = chunk offset alone (column pieces add key * 256).
   const int rq = lane >> 4;
-  uint32_t lofs[4], cofs[4];
+  uint32_t lofs[kL], cofs[kL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rw = 16 * w + 4 * j + rq;
+  for (int j = 0; j < kL; ++j) {
+    const int rw = 4 * kL * w + 4 * j + rq;
     cofs[j] = 16u * (uint32_t)((lane & 15) ^ swz(rw));
     lofs[j] = (uint32_t)rw * (uint32_t)kRowBytes + cofs[j];
   }
@@ -367,18 +381,18 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   // ck1 of piece i+1 (its V tile is loaded this iteration), ck2 of piece i+2
   // (K tile this iteration, V tile next), ck3 fetched this iteration.
   Piece cur{}, p1{}, p2{}, p3{};
-  ColKeys ck0{}, ck1{}, ck2{}, ck3{};
-  auto fetch_keys = [&](const Piece& p, ColKeys& ck) {
+  ColKeys<kL> ck0{}, ck1{}, ck2{}, ck3{};
+  auto fetch_keys = [&](const Piece& p, ColKeys<kL>& ck) {
     if (p.is_col) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ck.k[j] = col_key(p, col, 16 * w + 4 * j + rq);
+      for (int j = 0; j < kL; ++j) ck.k[j] = col_key(p, col, 4 * kL * w + 4 * j + rq);
     }
   };
-  // Mask keys of a column piece: lanes with lane%16 == 0 hold rows 16w + 4j.
-  auto store_keys = [&](int* dst, const ColKeys& ck) {
+  // Mask keys of a column piece: lanes with lane%16 == 0 hold rows 4 kL w + 4j.
+  auto store_keys = [&](int* dst, const ColKeys<kL>& ck) {
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[16 * w + 4 * j + rq] = ck.k[j];
+      for (int j = 0; j < kL; ++j) dst[4 * kL * w + 4 * j + rq] = ck.k[j];
     }
   };
   it.start();
@@ -437,7 +451,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const int* keys = key_lds[i & 3];
     const int kmin = cur.is_col ? keys[0] : cur.start;
     const int kmax = cur.is_col ? keys[cur.count - 1] : cur.start + cur.count - 1;
-    const bool far = ashape && kmax >= sink && row0 + kBM - 1 - max(kmin, sink) >= window;
+    const bool far = ashape && kmax >= sink && row0 + kRows - 1 - max(kmin, sink) >= window;
     if (cur.count < kKP || kmax > row0 || far) {
       // Slot of element r: 8 (r / 4) + 4 g + r % 4.  In the segment variant
       // the base is made opaque here so the sixteen slots are formed inside
@@ -463,9 +477,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                          fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
-    mx = max_halves(mx) * sl2;
+    // This lane's half of the row decides whether any row's max ran ahead;
+    // only a rescale needs the whole row's max (both halves).
+    mx *= sl2;
     if (__any(mx > m_run + kLag)) {
-      const float mn = fmaxf(m_run, mx);
+      const float mn = fmaxf(m_run, max_halves(mx));
       const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
       m_run = mn;
       l_run *= alpha;
@@ -542,11 +558,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   float* out_f32 = reinterpret_cast<float*>(a.out);
   float* lse = a.lse;
   if (kSeg) {
+    // the record holds the 64 rows of the item's 64-row block
     int hh, bb, ss, slot;
-    map_work_seg(blockIdx.x, a, hh, bb, ss, slot);
+    map_work_seg<kRows>(blockIdx.x, a, hh, bb, ss, slot);
     float* rec = a.part + (int64_t)__builtin_amdgcn_readfirstlane(slot) * kSegRecFloats;
-    out_f32 = rec - ((int64_t)h * a.qm + qrow0) * kD;
-    lse = rec + kSegRowFloats - ((int64_t)h * a.qm + qrow0);
+    const int64_t rrow0 = (int64_t)(b / kPer) * kBM;
+    out_f32 = rec - ((int64_t)h * a.qm + rrow0) * kD;
+    lse = rec + kSegRowFloats - ((int64_t)h * a.qm + rrow0);
   }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
@@ -568,12 +586,21 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     lse[orow] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
-  attn_body<false>(a);
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
+  attn_body<false, 64>(a);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_seg(AttnArgs a) {
-  attn_body<true>(a);
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_seg(AttnArgs a) {
+  attn_body<true, 64>(a);
+}
+
+// 32-row query blocks: one wavefront per work item, filling its tiles alone.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd32(AttnArgs a) {
+  attn_body<false, 32>(a);
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_seg32(AttnArgs a) {
+  attn_body<true, 32>(a);
 }
 
 // Combination of a (head, block)'s segment records (O_s / l_s and lse_s per
@@ -670,18 +697,26 @@ hipError_t launch_v_to_f16(const uint16_t* v, _Float16* v16, int64_t elems, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn(const AttnArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.n_list * a.nb;
-  hipLaunchKernelGGL(sparse_attn_fwd, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s) {
+  if (rows != kBM && rows != 32) return hipErrorInvalidValue;
+  const int64_t blocks = (int64_t)a.n_list * a.nb * (kBM / rows);
+  if (rows == kBM)
+    hipLaunchKernelGGL(sparse_attn_fwd, dim3((unsigned)blocks), dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_fwd32, dim3((unsigned)blocks), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn_seg(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_sparse_attn_seg(const AttnArgs& a, int rows, hipStream_t s) {
+  if (rows != kBM && rows != 32) return hipErrorInvalidValue;
   // Segments that reach the chunk's longest block.
   const int nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
   if (nseg > a.seg_n) return hipErrorInvalidValue;
-  const int64_t blocks = (int64_t)nseg * a.seg_nb * a.n_list;
-  hipLaunchKernelGGL(sparse_attn_seg, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  const int64_t blocks = (int64_t)nseg * a.seg_nb * (kBM / rows) * a.n_list;
+  if (rows == kBM)
+    hipLaunchKernelGGL(sparse_attn_seg, dim3((unsigned)blocks), dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_seg32, dim3((unsigned)blocks), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(seg_combine, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(kCombThreads), 0, s, a);

@@ -94,7 +94,9 @@ typedef struct {
   int32_t last_q;       /* VS: last rows scored against all keys; must be 64 */
   int32_t n_vertical;   /* VS: key columns kept, 0..n */
   int32_t n_slash;      /* VS: diagonals kept, 0..n */
-  int32_t block;        /* BS: pooling block; must be 64 */
+  int32_t block;        /* BS: pooling block; must be 64.  VS: query rows per
+                           block of the index, 64 (or 0) or 32 (finer spans:
+                           a slash keeps 32 keys per 32-row block) */
   int32_t top_k_blocks; /* BS: key blocks kept per query block, 1..n/64 */
   int32_t sink;         /* A-shape: initial keys kept, 0..n */
   int32_t window;       /* A-shape: local causal window in keys, 1..n; GRID: local offsets 0..window-1, 1..n */
@@ -134,7 +136,9 @@ ms_status ms_estimate_workspace_bytes(const ms_problem* prob, const ms_head_para
  *   offsets[4h+0] rng_ptr, [4h+1] rng, [4h+2] col_ptr, [4h+3] col
  * from the arena base, and the capacities caps[2h+0] = R_max, caps[2h+1] = C_max
  * (both arrays caller-owned host memory).  Ranges of a query block are sorted,
- * disjoint and non-touching; columns are ascending and lie in no range. */
+ * disjoint and non-touching; columns are ascending and lie in no range.  A
+ * Vertical-Slash head with block == 32 has a CSR over the 2*NBq query blocks
+ * of 32 rows (rows 32b .. 32b+31 for block b - 2*q_block0). */
 ms_status ms_index_bytes(const ms_problem* prob, const ms_head_params* params, size_t* bytes);
 ms_status ms_index_layout(const ms_problem* prob, const ms_head_params* params,
                           int64_t* offsets, int64_t* caps);
@@ -176,7 +180,8 @@ ms_status ms_estimate_block(const ms_problem* prob, const ms_head_params* params
  * pattern; PIT fragment: tile coverage).  Per Q head and 64-row query block b:
  *   VS: each slash o <= 64b+63 keeps keys [max(0, 64b-o), 64b+64-o); spans that
  *       overlap or touch merge into ranges; verticals j <= 64b+63 outside every
- *       range become columns.
+ *       range become columns.  With block == 32 the same per 32-row block b:
+ *       [max(0, 32b-o), 32b+32-o) for o <= 32b+31, verticals j <= 32b+31.
  *   BS: selected key blocks c give [64c, 64c+64), consecutive ones merged.
  *   A-shape: [0, min(sink, 64b+64)) and [max(0, 64b-window+1), 64b+64), merged.
  *   GRID: as VS with no verticals and the fixed offsets 0 .. window-1 and

@@ -39,6 +39,10 @@ function (readings R1..R13 of the design notes):
   R16 Grid heads keep fixed offsets: 0 .. window-1 and tP-w .. tP+w for the
       T previous frames of P tokens; their index is the Vertical-Slash
       conversion of that slash set.
+  R17 A Vertical-Slash head may ask for 32-row query blocks (finer
+      granularity against the PIT fragment's coverage waste): R7 with 32 in
+      place of 64, so a slash keeps a 32-key span per 32-row block and spans
+      merge when they overlap or touch.
 
 Every array is numpy float64 (scores, attention) or int64/int32 (indices).
 Inputs arrive as bfloat16 values widened exactly to float64 by the caller.
@@ -76,4 +80,5 @@ from .core import (  # noqa: F401
     topk_mass,
     estimate_head,
     head_index,
+    query_block_rows,
 )

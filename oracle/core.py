@@ -120,12 +120,15 @@ def _merge(lo: np.ndarray, hi: np.ndarray) -> np.ndarray:
     return np.asarray(out, dtype=np.int64)
 
 
-def vs_block_index(vert: np.ndarray, slash: np.ndarray, b: int) -> BlockIndex:
-    """Ranges and columns of query block b (rows [b*BM, b*BM + BM))."""
-    row0, last = b * BM, b * BM + BM - 1
+def vs_block_index(vert: np.ndarray, slash: np.ndarray, b: int, bm: int = BM) -> BlockIndex:
+    """Ranges and columns of query block b (rows [b*bm, b*bm + bm)).
+
+    bm is the query-block height: 64 (reading R7) or 32 (reading R17, the
+    finer granularity: each slash keeps a 32-key span per 32-row block)."""
+    row0, last = b * bm, b * bm + bm - 1
     o = np.asarray(slash, dtype=np.int64)
     o = o[o <= last]                              # diagonals that reach some row of the block
-    ranges = _merge(np.maximum(0, row0 - o), row0 + BM - o)
+    ranges = _merge(np.maximum(0, row0 - o), row0 + bm - o)
     j = np.asarray(vert, dtype=np.int64)
     j = j[j <= last]
     if ranges.shape[0]:
@@ -135,8 +138,8 @@ def vs_block_index(vert: np.ndarray, slash: np.ndarray, b: int) -> BlockIndex:
     return ranges, np.sort(j)
 
 
-def vs_index(vert: np.ndarray, slash: np.ndarray, n: int) -> List[BlockIndex]:
-    return [vs_block_index(vert, slash, b) for b in range(n // BM)]
+def vs_index(vert: np.ndarray, slash: np.ndarray, n: int, bm: int = BM) -> List[BlockIndex]:
+    return [vs_block_index(vert, slash, b, bm) for b in range(n // bm)]
 
 
 def bs_block_index(blocks: np.ndarray) -> BlockIndex:
@@ -216,14 +219,15 @@ def csr_to_index(rng_ptr, rng, col_ptr, col) -> List[BlockIndex]:
 # Mask and attention ([P1]: attention only over the estimated indices; [P2]
 # "Summary", third stage).  Readings R1 (A-shape window), R7, R8.
 # --------------------------------------------------------------------------
-def block_mask(bidx: BlockIndex, b: int, n: int, ashape: Optional[Tuple[int, int]] = None) -> np.ndarray:
-    """Boolean [BM, n]: row i = b*BM + r may attend key j."""
+def block_mask(bidx: BlockIndex, b: int, n: int, ashape: Optional[Tuple[int, int]] = None,
+               bm: int = BM) -> np.ndarray:
+    """Boolean [bm, n]: row i = b*bm + r may attend key j."""
     ranges, cols = bidx
     keep = np.zeros(n, dtype=bool)
     for lo, hi in ranges.tolist():
         keep[lo:hi] = True
     keep[np.asarray(cols, dtype=np.int64)] = True
-    i = np.arange(b * BM, b * BM + BM)[:, None]
+    i = np.arange(b * bm, b * bm + bm)[:, None]
     j = np.arange(n)[None, :]
     m = keep[None, :] & (j <= i)
     if ashape is not None:
@@ -233,20 +237,20 @@ def block_mask(bidx: BlockIndex, b: int, n: int, ashape: Optional[Tuple[int, int
 
 
 def attention_block(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, bidx: BlockIndex, b: int,
-                    scale: Optional[float] = None, ashape: Optional[Tuple[int, int]] = None):
-    """Masked softmax attention for the 64 rows of block b; returns (out [BM, d], lse [BM])."""
+                    scale: Optional[float] = None, ashape: Optional[Tuple[int, int]] = None, bm: int = BM):
+    """Masked softmax attention for the bm rows of block b; returns (out [bm, d], lse [bm])."""
     n, d = k.shape
     c = 1.0 / math.sqrt(d) if scale is None else scale
     ranges, cols = bidx
     keys = np.unique(np.concatenate([np.concatenate([np.arange(lo, hi) for lo, hi in ranges.tolist()])
                                      if ranges.shape[0] else np.zeros(0, dtype=np.int64),
                                      np.asarray(cols, dtype=np.int64)]).astype(np.int64))
-    out = np.zeros((BM, d))
-    lse = np.full(BM, -np.inf)
+    out = np.zeros((bm, d))
+    lse = np.full(bm, -np.inf)
     if keys.size == 0:
         return out, lse
-    z = (q_rows @ k[keys].T) * c                  # [BM, |keys|]
-    i = np.arange(b * BM, b * BM + BM)[:, None]
+    z = (q_rows @ k[keys].T) * c                  # [bm, |keys|]
+    i = np.arange(b * bm, b * bm + bm)[:, None]
     j = keys[None, :]
     allowed = j <= i
     if ashape is not None:
@@ -264,18 +268,19 @@ def attention_block(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, bidx: Bloc
 
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, index: Sequence[BlockIndex],
                    scale: Optional[float] = None, ashape: Optional[Tuple[int, int]] = None,
-                   blocks: Optional[Sequence[int]] = None):
-    """Attention of one Q head over its index; ``blocks`` restricts to some query blocks.
+                   blocks: Optional[Sequence[int]] = None, bm: int = BM):
+    """Attention of one Q head over its index of bm-row query blocks;
+    ``blocks`` restricts to some query blocks.
 
     Returns (out [n, d], lse [n]); rows of skipped blocks stay NaN.
     """
     n, d = q.shape
     out = np.full((n, d), np.nan)
     lse = np.full(n, np.nan)
-    for b in (range(n // BM) if blocks is None else blocks):
-        o, l = attention_block(q[b * BM:(b + 1) * BM], k, v, index[b], b, scale, ashape)
-        out[b * BM:(b + 1) * BM] = o
-        lse[b * BM:(b + 1) * BM] = l
+    for b in (range(n // bm) if blocks is None else blocks):
+        o, l = attention_block(q[b * bm:(b + 1) * bm], k, v, index[b], b, scale, ashape, bm)
+        out[b * bm:(b + 1) * bm] = o
+        lse[b * bm:(b + 1) * bm] = l
     return out, lse
 
 
@@ -338,11 +343,19 @@ def estimate_head(params, q: np.ndarray, k: np.ndarray, scale: Optional[float] =
     return ("static",)
 
 
+def query_block_rows(params) -> int:
+    """Rows per query block of a head's index: 32 for a Vertical-Slash head
+    that asks for the finer granularity (reading R17), 64 otherwise."""
+    return 32 if params.pattern == VERTICAL_SLASH and getattr(params, "block", BM) == 32 else BM
+
+
 def head_index(params, sel, n: int, q_block0: int = 0) -> List[BlockIndex]:
-    """Index of query blocks q_block0 .. n/64 - 1 (entry r is block q_block0 + r)."""
+    """Index of query blocks q_block0 .. n/64 - 1 (entry r is block q_block0 + r);
+    a head with 32-row blocks (reading R17) lists blocks 2 q_block0 .. n/32 - 1."""
     blocks = range(q_block0, n // BM)
     if params.pattern == VERTICAL_SLASH:
-        return [vs_block_index(sel[1], sel[2], b) for b in blocks]
+        bm = query_block_rows(params)
+        return [vs_block_index(sel[1], sel[2], b, bm) for b in range(q_block0 * BM // bm, n // bm)]
     if params.pattern == BLOCK_SPARSE:
         return bs_index(sel[1])
     if params.pattern == A_SHAPE:

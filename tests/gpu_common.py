@@ -138,7 +138,7 @@ def read_index_blocks(prob, hp, index: torch.Tensor, head: int, blocks):
     {b: (ranges [r, 2] int64, cols [c] int64)}."""
     offs, _ = ms.ms_index_layout(prob, hp)
     o_rp, o_r, o_cp, o_c = offs[head]
-    nb = prob.n // 64
+    nb = ms.index_blocks(prob, hp, head)
     base = index.view(torch.int32)
     rp = base[o_rp // 4:o_rp // 4 + nb + 1].cpu().numpy()
     cp = base[o_cp // 4:o_cp // 4 + nb + 1].cpu().numpy()

@@ -2,6 +2,8 @@
 symbol include/msattn.h declares, and rejects bad arguments on the host
 before enqueueing anything (no call here reaches a HIP launch)."""
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -98,6 +100,13 @@ def test_head_validation(head, status):
 def _cap_bound(h, nb):
     """Per-head CSR capacities from the pattern's own bounds."""
     r = c = 0
+    if h.pattern == W.VERTICAL_SLASH and h.block == 32:
+        for b in range(2 * nb):
+            last = 32 * b + 31
+            # run starts are >= 33 apart and <= last
+            r += min(h.n_slash, last // 33 + 1)
+            c += min(h.n_vertical, last + 1)
+        return r, c
     for b in range(nb):
         last = 64 * b + 63
         if h.pattern == W.VERTICAL_SLASH:
@@ -263,3 +272,36 @@ def test_chunk_sizes_follow_the_query_blocks():
     assert ms.ms_estimate_workspace_bytes(part, hp) < ms.ms_estimate_workspace_bytes(full, hp)
     offs, caps = ms.ms_index_layout(part, hp)
     assert caps[0][0] == sum(min(4, b + 1, b // 2 + 1) for b in range(15, 20))
+
+
+@pytest.mark.parametrize("block,status", [(0, 0), (64, 0), (32, 0), (16, 2), (128, 2), (-1, 2)])
+def test_vertical_slash_block_height_validation(block, status):
+    hp = ms.head_params([W.HeadParams(W.VERTICAL_SLASH, n_vertical=4, n_slash=4, block=block)])
+    if status == 0:
+        ms.ms_validate(ms.problem(1024, 1, 1), hp)
+    else:
+        _expect(status, ms.ms_validate, ms.problem(1024, 1, 1), hp)
+
+
+def test_32_row_block_capacities_bound_the_oracle_index():
+    """A Vertical-Slash head with 32-row blocks has a CSR over twice the query
+    blocks; its capacities follow the 32-row bounds and hold the oracle's
+    index of random selections, whole and as a chunk."""
+    n = 64 * 24
+    r = np.random.default_rng(5)
+    for kv, ks in [(10, 40), (300, 700), (n, 5), (1, n)]:
+        hp = W.vs(kv, ks, block=32)
+        vert = np.sort(r.choice(n, min(kv, n), replace=False))
+        slash = np.sort(r.choice(n, min(ks, n), replace=False))
+        for qb0 in (0, 7):
+            prob = ms.problem(n, 1, 1, q_block0=qb0)
+            arr = ms.head_params([hp])
+            assert ms.index_blocks(prob, arr, 0) == 2 * (n // 64 - qb0)
+            offs, caps = ms.ms_index_layout(prob, arr)
+            assert caps[0] == _cap_bound(hp, n // 64 - qb0) if qb0 == 0 else True
+            idx = oracle.head_index(hp, ("vs", vert, slash), n, q_block0=qb0)
+            assert len(idx) == 2 * (n // 64 - qb0)
+            assert sum(x[0].shape[0] for x in idx) <= caps[0][0]
+            assert sum(x[1].shape[0] for x in idx) <= caps[0][1]
+            o = offs[0]
+            assert o[0] + 4 * (2 * (n // 64 - qb0) + 1) <= o[1] and o[2] + 4 * (2 * (n // 64 - qb0) + 1) <= o[3]

@@ -276,3 +276,46 @@ def test_longest_sequence():
             assert np.all(np.isneginf(got_l[~fin]))
             np.testing.assert_allclose(got_l[fin], rl[fin], rtol=0, atol=LSE_ATOL)
         print(f"  head {h}: {len(blocks)} blocks ok", flush=True)
+
+
+def test_32_row_blocks_by_key_segments():
+    """Vertical-Slash heads indexed by 32-row query blocks with long key sets
+    run by key segments: two one-wavefront work items fill the two halves of
+    one 64-row partial record, and the combination is the 64-row one.  n =
+    262144, two such heads beside a 64-row one and a short 32-row head that
+    stays whole; 32-row blocks at segment edges (1023/1024, 2047/2048), at the
+    edge of the record-budget chunks, the first, last and random ones."""
+    n = 262144
+    heads = [W.vs(100, 3000, block=32), W.vs(100, 1500), W.vs(50, 3000, block=32), W.vs(20, 40, block=32)]
+    w = W.custom("seg32", n, 4, 2, heads, recipe="vs_planted", seed=43)
+    st = run_staged(make(w), debug=False)
+    sel = selections(st)
+    nb32 = n // 32
+    seg_heads = 2
+    cb = (4 << 30) // ((n // 32768) * seg_heads * (64 * 128 + 64) * 4)   # 64-row blocks per chunk
+    edges = [0, 1, 1023, 1024, 2047, 2048, 2 * cb - 1, 2 * cb, nb32 - 2, nb32 - 1]
+    q = f64(st.q)
+    for h, p in enumerate(heads):
+        bm = oracle.query_block_rows(p)
+        kh, vh = f64(st.k[kv_of(w, h)]), f64(st.v[kv_of(w, h)])
+        nbh = n // bm
+        blocks = sorted({b for b in (edges if bm == 32 else [e // 2 for e in edges]) if b < nbh}
+                        | set(sample_blocks(nbh, 2, 600 + h)))
+        got_idx = read_index_blocks(st.prob, st.hp, st.index, h, blocks)
+        for b in blocks:
+            ref_b = oracle.vs_block_index(sel[h][1], sel[h][2], b, bm)
+            np.testing.assert_array_equal(got_idx[b][0], ref_b[0], err_msg=f"head {h} block {b} ranges")
+            np.testing.assert_array_equal(got_idx[b][1], ref_b[1], err_msg=f"head {h} block {b} cols")
+            rows = slice(bm * b, bm * b + bm)
+            ro, rl = oracle.attention_block(q[h, rows], kh, vh, ref_b, b, bm=bm)
+            check_attention(f64(st.out[h, rows]), ro, f"head {h} block {b}")
+            got_l = st.lse[h, rows].cpu().numpy().astype(np.float64)
+            fin = np.isfinite(rl)
+            assert np.all(np.isneginf(got_l[~fin]))
+            np.testing.assert_allclose(got_l[fin], rl[fin], rtol=0, atol=LSE_ATOL)
+        print(f"  head {h} ({bm}-row blocks): {len(blocks)} blocks ok", flush=True)
+    ws = ms.empty_workspace(ms.ms_workspace_bytes(st.prob, st.hp))
+    out2 = torch.empty_like(st.out)
+    ms.ms_sparse_attn(st.prob, st.hp, st.q, st.k, st.v, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), st.out.view(torch.int16))

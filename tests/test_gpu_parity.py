@@ -281,7 +281,8 @@ def _attention_check(st: Staged, blocks=None, bf16_out=True):
             np.testing.assert_array_equal(g_arr, r_arr)
         bidx = oracle.csr_to_index(*idx[h])
         kv = kv_of(w, h)
-        ro, rl = oracle.attention_head(q[h], k[kv], v[kv], bidx, ashape=ashape_of(w.heads[h]), blocks=blocks)
+        ro, rl = oracle.attention_head(q[h], k[kv], v[kv], bidx, ashape=ashape_of(w.heads[h]), blocks=blocks,
+                                       bm=oracle.query_block_rows(w.heads[h]))
         rows = np.isfinite(ro[:, 0])
         check_attention(out[h][rows], ro[rows], f"head {h} pattern {w.heads[h].pattern}", bf16_out)
         if lse is not None:
@@ -539,3 +540,62 @@ def test_smallest_sequences_every_pattern(n, q_block0):
             fin = np.isfinite(rl)
             assert np.all(np.isneginf(gl[~fin]))
             np.testing.assert_allclose(gl[fin], rl[fin], rtol=0, atol=LSE_ATOL)
+
+
+# Vertical-Slash heads indexed by 32-row query blocks (reading R17): their CSR
+# lists 32-row blocks and one wavefront serves each block.  Beside 64-row
+# heads of every pattern, with GQA; whole sequences and a chunk.
+@pytest.mark.parametrize("n,hq,hkv,q_block0", [(2048, 8, 2, 0), (64 * 37, 4, 4, 0), (2048, 4, 1, 9), (64, 2, 1, 0)])
+def test_vertical_slash_32_row_blocks(n, hq, hkv, q_block0):
+    c = lambda x: min(x, n)  # noqa: E731  (budgets within the sequence)
+    pool = [W.vs(c(40), c(90), block=32), W.bs(min(5, n // 64)), W.vs(c(40), c(90)), W.ashape(16, c(300)),
+            W.vs(c(200), c(30), block=32), W.dense(), W.vs(n, 3, block=32), W.vs(3, n, block=32)]
+    heads = [pool[i % len(pool)] for i in range(hq)]
+    w = W.custom("vs32", n, hq, hkv, heads, recipe="vs_planted", seed=70 + n + q_block0)
+    if q_block0 == 0:
+        _attention_check(run_staged(make(w)))
+        return
+    q, k, v = W.generate(w, device="cuda")
+    qc = q[:, 64 * q_block0:].contiguous()
+    st = make(w, qkv=(qc, k, v))
+    st.prob = ms.problem(n, hq, hkv, q_block0=q_block0)
+    nv, ns, nbk = ms.ms_selection_sizes(st.prob, st.hp)
+    vert = torch.empty(max(nv, 1), dtype=torch.int32, device="cuda")
+    slash = torch.empty(max(ns, 1), dtype=torch.int32, device="cuda")
+    blocks = torch.empty(max(nbk, 1), dtype=torch.int32, device="cuda")
+    ws = ms.empty_workspace(ms.ms_estimate_workspace_bytes(st.prob, st.hp))
+    ms.ms_estimate_vs(st.prob, st.hp, qc, k, vert, slash, ws)
+    ms.ms_estimate_block(st.prob, st.hp, qc, k, blocks, ws)
+    index = ms.empty_workspace(ms.ms_index_bytes(st.prob, st.hp))
+    ms.ms_build_index(st.prob, st.hp, vert, slash, blocks, index)
+    out = torch.empty_like(qc)
+    lse = torch.empty((hq, qc.shape[1]), dtype=torch.float32, device="cuda")
+    ms.ms_sparse_attn_indexed(st.prob, st.hp, qc, k, v, index, out, ms.empty_workspace(ms.ms_attn_workspace_bytes(st.prob)),
+                              lse)
+    torch.cuda.synchronize()
+    qh, kh, vh = f64(q), f64(k), f64(v)
+    csr = ms.read_index(st.prob, st.hp, index)
+    vs_h = [x for x in range(hq) if heads[x].pattern == W.VERTICAL_SLASH]
+    vh_, sh_ = vert.cpu().numpy(), slash.cpu().numpy()
+    ov = os_ = 0
+    for x in range(hq):
+        p = heads[x]
+        if p.pattern != W.VERTICAL_SLASH:
+            continue
+        sel = ("vs", vh_[ov:ov + p.n_vertical].astype(np.int64), sh_[os_:os_ + p.n_slash].astype(np.int64))
+        ov += p.n_vertical
+        os_ += p.n_slash
+        # the oracle's index of the GPU's own selections, for the chunk's blocks
+        ref = oracle.head_index(p, sel, n, q_block0=q_block0)
+        for g_arr, r_arr in zip(csr[x], oracle.index_to_csr(ref)):
+            np.testing.assert_array_equal(g_arr, r_arr)
+        bm = oracle.query_block_rows(p)
+        kv = x // (hq // hkv)
+        for r, bidx in enumerate(ref):
+            gb = q_block0 * 64 // bm + r
+            ro, rl = oracle.attention_block(qh[x, gb * bm:(gb + 1) * bm], kh[kv], vh[kv], bidx, gb, bm=bm)
+            rows = slice(r * bm, (r + 1) * bm)
+            check_attention(f64(out[x, rows]), ro, f"head {x} block {gb}")
+            fin = np.isfinite(rl)
+            np.testing.assert_allclose(lse[x, rows].cpu().numpy()[fin], rl[fin], rtol=0, atol=LSE_ATOL)
+    assert vs_h

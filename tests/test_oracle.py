@@ -622,3 +622,92 @@ def test_estimate_head_static_patterns_select_nothing():
     q = np.zeros((128, 128))
     for p in (W.ashape(4, 8), W.dense(), W.grid(10, 1, 0, 4)):
         assert oracle.estimate_head(p, q, q) == ("static",)
+
+
+
+# ------------------------------------------------------------ 32-row query blocks (reading R17)
+def _vs_mask_rows(vert, slash, n, bm):
+    """(i, j) kept iff j <= i and (j is a vertical, or some slash o reaching
+    block i // bm has bm*b - o <= j < bm*b + bm - o); element by element."""
+    vert, slash = set(int(x) for x in vert), [int(x) for x in slash]
+    m = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        row0 = (i // bm) * bm
+        for j in range(i + 1):
+            keep = j in vert
+            if not keep:
+                for o in slash:
+                    if o <= row0 + bm - 1 and row0 - o <= j < row0 + bm - o:
+                        keep = True
+                        break
+            m[i, j] = keep
+    return m
+
+
+def test_vs_index_32_row_blocks_golden_hand_worked():
+    g = json.load(open(os.path.join(GOLDEN, "vs_index_bm32_n256.json")))
+    idx = oracle.vs_index(np.array(g["vertical"]), np.array(g["slash"]), g["n"], bm=32)
+    assert len(idx) == g["n"] // 32
+    for blk in g["blocks"]:
+        r, c = idx[blk["b"]]
+        assert r.tolist() == blk["ranges"], blk
+        assert c.tolist() == blk["cols"], blk
+    # through the per-head dispatch: block = 32 asks for 32-row blocks
+    p = W.HeadParams(W.VERTICAL_SLASH, n_vertical=4, n_slash=5, block=32)
+    assert oracle.query_block_rows(p) == 32 and oracle.query_block_rows(W.vs(4, 5)) == 64
+    got = oracle.head_index(p, ("vs", np.array(g["vertical"]), np.array(g["slash"])), g["n"])
+    _assert_index(got, g["blocks"])
+    got = oracle.head_index(p, ("vs", np.array(g["vertical"]), np.array(g["slash"])), g["n"], q_block0=2)
+    assert len(got) == 4
+    _assert_index(got, g["blocks"], 4)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_vs_index_32_row_blocks_match_elementwise_definition(seed):
+    r = rng(80 + seed)
+    n = 256
+    vert = np.sort(r.choice(n, size=int(r.integers(1, 12)), replace=False))
+    slash = np.sort(r.choice(n, size=int(r.integers(1, 10)), replace=False))
+    idx = oracle.vs_index(vert, slash, n, bm=32)
+    ref = _vs_mask_rows(vert, slash, n, 32)
+    got = np.concatenate([oracle.block_mask(idx[b], b, n, bm=32) for b in range(n // 32)])
+    np.testing.assert_array_equal(got, ref)
+    # the 64-row definition is the same brute force with 64
+    np.testing.assert_array_equal(_vs_mask_rows(vert, slash, n, 64), _vs_mask_by_definition(vert, slash, n))
+    # canonical form, and every 32-row block keeps a subset of its 64-row block
+    m64 = np.concatenate([oracle.block_mask(b64, b, n) for b, b64 in enumerate(oracle.vs_index(vert, slash, n))])
+    assert not np.any(got & ~m64)
+    for b, (rg, cols) in enumerate(idx):
+        end = 32 * b + 32
+        assert np.all(rg[:, 0] < rg[:, 1]) and np.all(rg[1:, 0] > rg[:-1, 1])
+        assert np.all((rg >= 0) & (rg <= end)) and np.all(np.diff(cols) > 0) and np.all(cols < end)
+
+
+def test_single_slash_keeps_one_32_key_span_per_row():
+    # One slash o: row i of 32-row block b keeps keys [32b - o, 32b + 32 - o) up
+    # to its own diagonal, i.e. min(32, i - (32b - o) + 1) keys when they exist.
+    n, o = 256, 40
+    idx = oracle.vs_index(np.zeros(0, dtype=np.int64), np.array([o]), n, bm=32)
+    m = np.concatenate([oracle.block_mask(idx[b], b, n, bm=32) for b in range(n // 32)])
+    for i in range(n):
+        lo = 32 * (i // 32) - o
+        want = [j for j in range(max(0, lo), min(lo + 32, i + 1))]
+        assert np.nonzero(m[i])[0].tolist() == want, i
+
+
+def test_attention_32_row_blocks_brute_force_and_full_coverage():
+    n = 256
+    q, k, v = _qkv(81, n)
+    r = rng(82)
+    vert = np.sort(r.choice(n, 9, replace=False))
+    slash = np.sort(r.choice(n, 5, replace=False))
+    out, lse = oracle.attention_head(q, k, v, oracle.vs_index(vert, slash, n, bm=32), bm=32)
+    mask = _vs_mask_rows(vert, slash, n, 32)
+    z = torch.from_numpy(q @ k.T / math.sqrt(128)).masked_fill(~torch.from_numpy(mask), float("-inf"))
+    p = torch.softmax(z, dim=1).nan_to_num(0.0).numpy()
+    np.testing.assert_allclose(out, p @ v, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=1).numpy(), rtol=1e-12, atol=1e-12)
+    # every offset kept: 32-row blocks reduce to dense causal attention too
+    ref, _ = oracle.attention_head(q, k, v, oracle.dense_index(n))
+    full, _ = oracle.attention_head(q, k, v, oracle.vs_index(np.arange(0), np.arange(n), n, bm=32), bm=32)
+    np.testing.assert_allclose(full, ref, rtol=1e-12, atol=1e-14)

@@ -56,8 +56,9 @@ class HeadParams:
     grid_width: int = 0
 
 
-def vs(n_vertical: int, n_slash: int, last_q: int = 64) -> HeadParams:
-    return HeadParams(VERTICAL_SLASH, last_q=last_q, n_vertical=n_vertical, n_slash=n_slash)
+def vs(n_vertical: int, n_slash: int, last_q: int = 64, block: int = 64) -> HeadParams:
+    """A Vertical-Slash head; block = 32 indexes it by 32-row query blocks."""
+    return HeadParams(VERTICAL_SLASH, last_q=last_q, n_vertical=n_vertical, n_slash=n_slash, block=block)
 
 
 def bs(top_k: int) -> HeadParams:
@@ -149,6 +150,12 @@ def config(config_id: int, seed: int = 0, n: Optional[int] = None) -> Workload:
         nn = n or 1048576
         return Workload("vs_1m_s", 5, nn, 32, 8, tuple(vs(1000, 6096) for _ in range(32)), "vs_planted",
                         n_planted=64, seed=seed, query_mean=0.5)
+    if config_id == 6:
+        # The 1M layer (same inputs as vs_1m: same config id for the draws)
+        # with its Vertical-Slash heads indexed by 32-row query blocks.
+        nn = n or 1048576
+        return Workload("vs_1m_b32", 4, nn, 32, 8, tuple(vs(1000, 6096, block=32) for _ in range(32)), "vs_planted",
+                        n_planted=64, seed=seed)
     raise ValueError(f"unknown config {config_id}")
 
 
