@@ -89,6 +89,7 @@ struct Plan {
   int n_wide = 0;                // the first n_wide chunks run with hpw heads per workgroup, the rest with 2
   std::vector<int16_t> solo;     // heads served one by one (64-row blocks)
   std::vector<int16_t> solo32;   // heads served one by one with 32-row blocks
+  std::vector<int16_t> ablk;     // A-shape heads of MHA layers, four query blocks per workgroup
   size_t index_bytes = 0;
   // attention workspace: fp16 V copy, then the key-segment records (without
   // params: the most any head set needs)
@@ -302,7 +303,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.e_qpool = take((size_t)P.n_bs * P.nbq * kD * f);
   P.e_kpool = take((size_t)P.bs_kv_heads.size() * P.nb * kD * f);
   P.e_scores = take((size_t)P.n_bs * P.nbq * P.nb * f);
-  P.e_topk = take(topk_scratch_bytes(P.n, std::max(P.n_vs, 1)));
+  P.e_topk = take(topk_scratch_bytes(P.n, std::max(std::min(2 * P.n_vs, TopkJobs::kMaxJobs), 1)));
   P.est_bytes = std::max<size_t>(off, kAlign);
   // Index arena: head table, chunk table, then each head's CSR, then each
   // chunk's union CSR.
@@ -394,6 +395,11 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
         dense_heads.push_back(h);
       else if (P.hpw > 1 && (pat == MS_A_SHAPE || pat == MS_GRID))
         fixed_heads.push_back(h);
+      else if (P.hpw == 1 && pat == MS_A_SHAPE && P.p[h].window >= 256)
+        // one head per KV head: four query blocks share one walk of the
+        // sink and the union of their windows (a window of at least 256 keys
+        // keeps most of that walk useful to every block)
+        P.ablk.push_back((int16_t)h);
       else
         P.solo.push_back((int16_t)h);
     }
@@ -541,23 +547,37 @@ ms_status run_estimate_vs(const Plan& P, const uint16_t* q, const uint16_t* k, i
                              reinterpret_cast<float*>(ws + P.e_stats), reinterpret_cast<float*>(ws + P.e_diag), v_sc,
                              s_sc, s),
           "vertical-slash estimation launch");
-  TopkJobs jv{}, js{};
+  // Both selections of every VS head in one chain of launches: the vertical
+  // jobs (scores v_sc, written to vert) first, then the slash jobs (scores
+  // s_sc, which follows v_sc in the workspace, written to slash).
+  struct Job {
+    int64_t src_off, dst_off;
+    int32_t k;
+    bool slash;
+  };
+  std::vector<Job> all;
   for (int i = 0; i < P.n_vs; ++i) {
     const int h = P.vs_heads[i];
-    if (P.p[h].n_vertical > 0) {
-      jv.src_off[jv.count] = (int64_t)i * P.n;
-      jv.dst_off[jv.count] = P.vert_off[h];
-      jv.k[jv.count++] = P.p[h].n_vertical;
-    }
-    if (P.p[h].n_slash > 0) {
-      js.src_off[js.count] = (int64_t)i * P.n;
-      js.dst_off[js.count] = P.slash_off[h];
-      js.k[js.count++] = P.p[h].n_slash;
-    }
+    if (P.p[h].n_vertical > 0) all.push_back({(int64_t)i * P.n, P.vert_off[h], P.p[h].n_vertical, false});
   }
+  const int64_t s_base = (int64_t)(P.e_s - P.e_v) / (int64_t)sizeof(float);
+  for (int i = 0; i < P.n_vs; ++i) {
+    const int h = P.vs_heads[i];
+    if (P.p[h].n_slash > 0) all.push_back({s_base + (int64_t)i * P.n, P.slash_off[h], P.p[h].n_slash, true});
+  }
+  // batches of at most kMaxJobs, each with its vertical jobs first
   void* tk = ws + P.e_topk;
-  HIP_TRY(launch_topk_chunked(v_sc, P.n, jv, vert, tk, s), "vertical top-k launch");
-  HIP_TRY(launch_topk_chunked(s_sc, P.n, js, slash, tk, s), "slash top-k launch");
+  for (size_t b0 = 0; b0 < all.size(); b0 += TopkJobs::kMaxJobs) {
+    TopkJobs j{};
+    int split = 0;
+    for (size_t x = b0; x < all.size() && j.count < TopkJobs::kMaxJobs; ++x) {
+      j.src_off[j.count] = all[x].src_off;
+      j.dst_off[j.count] = all[x].dst_off;
+      j.k[j.count++] = all[x].k;
+      if (!all[x].slash) split = j.count;
+    }
+    HIP_TRY(launch_topk_chunked(v_sc, P.n, j, vert, slash, split, tk, s), "top-k launch");
+  }
   for (int i = 0; i < P.n_vs; ++i) {
     const int h = P.vs_heads[i];
     if (dbg_v)
@@ -641,6 +661,11 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
       a.n_list = (int)P.gdesc.size() - P.n_wide;
       HIP_TRY(launch_group_sparse(a, chunks + P.n_wide, 2, s), "attention launch");
     }
+  }
+  if (!P.ablk.empty()) {
+    a.n_list = (int)P.ablk.size();
+    for (size_t i = 0; i < P.ablk.size(); ++i) a.list[i] = P.ablk[i];
+    HIP_TRY(launch_group_ashape(a, s), "attention launch");
   }
   for (auto [list, rows] : {std::make_pair(&P.solo, kBM), std::make_pair(&P.solo32, 32)}) {
     if (list->empty()) continue;

@@ -523,6 +523,124 @@ __device__ __forceinline__ void group_dense_body(const AttnArgs& a) {
   if (active) hr.store(a, h);
 }
 
+// A-shape heads of one head per KV head (MHA): a workgroup of 8 waves serves
+// four consecutive query blocks of one head, two waves each, like the dense
+// kernel.  Their keys are the sink [0, sink) and the union of the four
+// blocks' windows, [max(0, lowest row - window + 1), top block's end): at
+// most two ranges, walked in pieces of up to 32 keys; a slot's waves skip the
+// pieces that hold none of their own block's keys ([0, min(sink, end)) and
+// [max(0, row0 - window + 1), end)) and mask the rest per row (causal and the
+// row's own window), so each K/V tile in LDS feeds up to 256 query rows.
+template <int S>
+__device__ __forceinline__ void group_ashape_body(const AttnArgs& a) {
+  constexpr int kSlots = 4;
+  constexpr int kD16 = 16 / (2 * kSlots);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wv >> 1;
+  // Groups are the sequence's query blocks 4g .. 4g+3 (the last one may be
+  // short), so a chunk of a longer prefill walks exactly the keys the whole
+  // sequence does for each of its blocks; slots below the call's first block
+  // stay idle.
+  const int nseq = a.qb0 + a.nb;  // query blocks of the sequence
+  const int gfirst = a.qb0 / kSlots, glast = (nseq - 1) / kSlots;
+  int hi, gi;
+  map_group(blockIdx.x, a.n_list, glast - gfirst + 1, hi, gi);
+  const int g = gfirst + gi;
+  const int h = a.list[hi];
+  const int kvh = h / a.grp;
+  c_head* hd = as_const<c_head>(a.arena) + h;
+  const int sink = hd->p0, window = hd->p1;
+  const int top = min(nseq - 1, kSlots * g + kSlots - 1);  // the group's highest block
+  const int sb = top - slot;                                // this slot's block of the sequence
+  const bool active = sb >= max(kSlots * g, a.qb0);
+  const int b = (active ? sb : top) - a.qb0;                // the call's block (rows of Q and out)
+  const int64_t n = a.n;
+  const int row0 = (a.qb0 + b) * kBM;
+  const int end = row0 + kBM;
+  // this slot's keys: [0, s_end) and [w_lo, end)
+  const int s_end = active ? min(sink, end) : 0;
+  const int w_lo = active ? max(0, row0 - window + 1) : 0;
+  const int w_hi = active ? end : 0;
+  // the workgroup's walk: [0, r1) then [r2lo, r2hi), fixed by the group
+  const int top_end = top * kBM + kBM;
+  const int lo_all = max(0, kSlots * g * kBM - window + 1);
+  const int r1 = sink >= lo_all ? 0 : sink;
+  const int r2lo = sink >= lo_all ? 0 : lo_all;
+  const int r2hi = top_end;
+  const int n1 = (r1 + kKP - 1) / kKP;
+  const int npieces = n1 + (r2hi - r2lo + kKP - 1) / kKP;
+  auto piece = [&](int p, int& start, int& count) {
+    if (p < n1) {
+      start = kKP * p;
+      count = min(kKP, r1 - start);
+    } else if (p < npieces) {
+      start = r2lo + kKP * (p - n1);
+      count = min(kKP, r2hi - start);
+    } else {
+      start = (int)n;  // past the end: reads zeros, holds no key
+      count = 0;
+    }
+  };
+  auto span_bits = [](int lo, int hi, int start, int count) -> uint32_t {
+    const int a0 = max(lo, start) - start, a1 = min(hi, start + count) - start;
+    if (a1 <= a0) return 0u;
+    const uint32_t upto = a1 >= 32 ? 0xffffffffu : ((1u << a1) - 1u);
+    return upto & ~((1u << a0) - 1u);
+  };
+  auto slot_bits = [&](int start, int count) -> uint32_t {
+    return span_bits(0, s_end, start, count) | span_bits(w_lo, w_hi, start, count);
+  };
+
+  const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
+  HeadRows hr;
+  hr.init(a.q + ((int64_t)h * a.qm + (int64_t)b * kBM + 32 * (wv & 1)) * kD, lane, row0, 32 * (wv & 1),
+          a.scale_log2);
+  hr.ashape = true;
+  hr.sink = sink;
+  hr.window = window;
+  Loader<kD16> ld;
+  ld.init(kr, vr, wv, lane);
+
+  int p_start[S], p_count[S];
+  auto prologue = [&](auto st_c) -> bool {
+    constexpr int ST = decltype(st_c)::value;
+    piece(ST, p_start[ST], p_count[ST]);
+    ld.range(stage<ST>(), p_start[ST]);
+    return true;
+  };
+  run_steps<0, S - 1>(prologue);
+  wait_vm_lgkm0<(S - 3) * kD16>();
+  hr.settle_q();
+  barrier_only();
+  f32x16 s_cur = hr.qk(stage<0>());
+
+  int i = 0;
+  auto step = [&](auto st_c) -> bool {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int NS = (ST + S - 1) % S;
+    piece(i + S - 1, p_start[NS], p_count[NS]);
+    ld.range(stage<NS>(), p_start[NS]);
+    const uint32_t bits = slot_bits(p_start[ST], p_count[ST]);
+    constexpr int N1 = (ST + 1) % S;
+    const bool need_n = i + 1 < npieces && slot_bits(p_start[N1], p_count[N1]) != 0u;
+    hr.advance(s_cur, p_start[ST], nullptr, p_count[ST], bits, stage<ST>(), need_n, stage<N1>());
+    wait_vm_lgkm0<(S - 3) * kD16>();
+    barrier_only();
+    ++i;
+    return i < npieces;
+  };
+  while (run_steps<0, S>(step)) {
+  }
+  wait_vm_lgkm0<0>();
+  if (active) hr.store(a, h);
+}
+
 // Sparse attention over the union index of a chunk of HPW heads (MInference
 // 1.0 summary, "Summary", third stage; union_index.hip builds the lists).
 // Phase 1 streams the union ranges through the ring in pieces of up to 32
@@ -697,6 +815,9 @@ __global__ __launch_bounds__(512) void group_dense_h4(AttnArgs a) { group_dense_
 __global__ __launch_bounds__(512) void group_dense_h2(AttnArgs a) { group_dense_body<2, 8>(a); }
 __global__ __launch_bounds__(512) void group_dense_h1(AttnArgs a) { group_dense_body<1, 8>(a); }
 
+// A-shape heads of MHA layers: four query blocks of one head per workgroup.
+__global__ __launch_bounds__(512) void group_ashape_blocks(AttnArgs a) { group_ashape_body<8>(a); }
+
 // Sparse: heads per workgroup (HPW) and ring stages: 4 heads (one workgroup
 // per CU, 8 stages = 128 KiB of LDS) or 2 (two per CU, 4 stages).
 
@@ -718,6 +839,13 @@ hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, int h
     hipLaunchKernelGGL(group_sparse_h2, grid, dim3(256), 0, s, a, groups, a.arena);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_group_ashape(const AttnArgs& a, hipStream_t s) {
+  const int groups = (a.qb0 + a.nb - 1) / 4 - a.qb0 / 4 + 1;
+  const dim3 grid((unsigned)((int64_t)groups * a.n_list));
+  hipLaunchKernelGGL(group_ashape_blocks, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -101,10 +101,12 @@ struct TopkJobs {            // up to kMaxJobs problems in one launch
 };
 hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, hipStream_t s);
 // Same selection with many workgroups per problem (for long vectors); every
-// job's k must lie in 1..n.  scratch: device, >= topk_scratch_bytes(n, jobs).
+// job's k must lie in 1..n.  Jobs 0 .. split-1 write to dst + dst_off, the
+// rest to dst2 + dst_off (two selections share one chain of launches).
+// scratch: device, >= topk_scratch_bytes(n, jobs).
 size_t topk_scratch_bytes(int64_t n, int problems);
-hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, void* scratch,
-                               hipStream_t s);
+hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, int32_t* dst2,
+                               int split, void* scratch, hipStream_t s);
 // Block-Sparse selection: for every BS slot and local query block bl (query
 // block b = qb0 + bl), top-min(k, b+1) of scores[slot][bl][0..b] into blocks
 // row bl (-1 padded to k).  k_of_slot and dst_off_of_slot are host arrays of
@@ -162,6 +164,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s);
 hipError_t launch_sparse_attn_seg(const AttnArgs& a, int rows, hipStream_t s);
 // Full causal attention, query heads that share a KV head served together.
 hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s);
+// A-shape heads listed in a.list (one head per KV head), four consecutive
+// query blocks of a head per workgroup.
+hipError_t launch_group_ashape(const AttnArgs& a, hipStream_t s);
 // Sparse attention over the union index (groups: device table of the
 // a.n_list chunks, hpw = 2 or 4 heads per workgroup, chunks of at most hpw).
 hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, int hpw, hipStream_t s);

@@ -599,3 +599,36 @@ def test_vertical_slash_32_row_blocks(n, hq, hkv, q_block0):
             fin = np.isfinite(rl)
             np.testing.assert_allclose(lse[x, rows].cpu().numpy()[fin], rl[fin], rtol=0, atol=LSE_ATOL)
     assert vs_h
+
+
+# A-shape heads of MHA layers with windows of at least 256 keys: four
+# consecutive query blocks of a head share one workgroup's walk of the sink
+# and the union of their windows.  Sink below, inside and above the lowest
+# window start, no sink, block counts that leave the last group short.
+@pytest.mark.parametrize("n,sink,window", [(64 * 37, 16, 300), (2048, 0, 700), (2048, 600, 256), (64 * 9, 1000, 300),
+                                           (64 * 14, 64, 2048), (64 * 5, 5, 257)])
+def test_ashape_four_block_groups(n, sink, window):
+    heads = [W.ashape(min(sink, n), min(window, n)), W.ashape(0, min(window, n)), W.dense(),
+             W.ashape(min(sink, n), min(window, n))]
+    w = W.custom("ashape_blocks", n, 4, 4, heads, recipe="ashape_sink", seed=80 + n + sink)
+    _attention_check(run_staged(make(w)))
+
+
+def test_ashape_four_block_groups_chunk_equals_whole():
+    """A chunk that starts inside a group of four blocks walks the same keys in
+    the same order for each of its blocks: out and lse equal the whole call's
+    rows bit for bit."""
+    n, q_block0 = 64 * 30, 6
+    heads = [W.ashape(40, 500), W.ashape(0, 1000)]
+    w = W.custom("ashape_chunk", n, 2, 2, heads, recipe="ashape_sink", seed=91)
+    q, k, v = W.generate(w, device="cuda")
+    outs = []
+    for qb0, qq in ((0, q), (q_block0, q[:, 64 * q_block0:].contiguous())):
+        prob, hp = ms.problem(n, 2, 2, q_block0=qb0), ms.head_params(heads)
+        out = torch.empty_like(qq)
+        lse = torch.empty((2, qq.shape[1]), device="cuda")
+        ms.ms_sparse_attn(prob, hp, qq, k, v, out, ms.empty_workspace(ms.ms_workspace_bytes(prob, hp)), lse)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    assert torch.equal(outs[1][0].view(torch.int16), outs[0][0][:, 64 * q_block0:].view(torch.int16))
+    assert torch.equal(outs[1][1], outs[0][1][:, 64 * q_block0:])
