@@ -157,15 +157,23 @@ struct ColKeys {
   int k[kL];  // keys of rows (32 / (8 / kL)) w + 4j + lane/16
 };
 
+// The piece kind is uniform, so the two address forms are separate branches
+// (no per-load select).  The whole byte offset stays in the vector offset,
+// which the buffer range check covers.
 template <int kL>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int w, const uint32_t* lofs,
                                           const uint32_t* cofs, const Piece& p, const ColKeys<kL>& ck) {
   char* const base = tile + 256 * 4 * kL * w;
+  if (p.is_col) {
 #pragma unroll
-  for (int j = 0; j < kL; ++j) {
-    const uint32_t off = p.is_col ? (uint32_t)ck.k[j] * (uint32_t)kRowBytes + cofs[j]
-                                  : (uint32_t)p.start * (uint32_t)kRowBytes + lofs[j];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16, off, 0, 0, 0);
+    for (int j = 0; j < kL; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16,
+                                               (uint32_t)ck.k[j] * (uint32_t)kRowBytes + cofs[j], 0, 0, 0);
+  } else {
+    const uint32_t start = (uint32_t)p.start * (uint32_t)kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kL; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16, start + lofs[j], 0, 0, 0);
   }
 }
 
@@ -452,7 +460,20 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     const int kmin = cur.is_col ? keys[0] : cur.start;
     const int kmax = cur.is_col ? keys[cur.count - 1] : cur.start + cur.count - 1;
     const bool far = ashape && kmax >= sink && row0 + kRows - 1 - max(kmin, sink) >= window;
-    if (cur.count < kKP || kmax > row0 || far) {
+    if ((cur.count < kKP || kmax > row0 || far) && kmax <= row0 && !far) {
+      // Only the piece's tail (slots >= count) is masked: element r of the
+      // lower half-wave is slot 8 (r / 4) + r % 4, of the upper one 4 more, so
+      // each element takes one select on a lane mask built with scalar
+      // instructions (count < 32 here).
+      const uint32_t bits = (1u << cur.count) - 1u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        const uint64_t lanes = (((bits >> c) & 1u) ? 0x00000000ffffffffull : 0ull) |
+                               (((bits >> (c + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
+        s[r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? s[r] : -INFINITY;
+      }
+    } else if (cur.count < kKP || kmax > row0 || far) {
       // Slot of element r: 8 (r / 4) + 4 g + r % 4.  In the segment variant
       // the base is made opaque here so the sixteen slots are formed inside
       // the masked path instead of being held in registers across the loop.
@@ -538,8 +559,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     p2 = p3;
     h1 = h2;
     h2 = h3;
-    ck1 = ck2;
-    ck2 = ck3;
+    // column keys move along only with column pieces (range pieces never read them)
+    if (p1.is_col) ck1 = ck2;
+    if (p2.is_col) ck2 = ck3;
     ++i;
     return true;
   };

@@ -167,19 +167,50 @@ __global__ void topk_init(TopkJobs jobs, TopkState* st) {
   if (j < jobs.count) st[j] = TopkState{0u, 0u, jobs.k[j], 0};
 }
 
+// A chunk of kChunk scores is read as kChunk / (4 kMT) rounds of one 16-byte
+// load per thread, all issued before any is used, so a workgroup has its
+// whole chunk in flight at once; thread t takes scores 4 (kMT r + t) .. +3 of
+// round r.  Score vectors start 16-byte aligned and hold a multiple of 64
+// scores, so a round is either inside the chunk or past its end.
+constexpr int kRounds = kChunk / (4 * kMT);
+
+struct ChunkKeys {
+  uint32_t key[kRounds][4];
+  bool valid[kRounds];
+};
+
+__device__ __forceinline__ void load_chunk(const float* x, int64_t n, int c, int t, ChunkKeys& ck) {
+  const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+  f32x4 v[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int64_t i4 = (int64_t)c * (kChunk / 4) + (int64_t)kMT * r + t;  // 4-score group
+    ck.valid[r] = 4 * i4 < n;
+    v[r] = ck.valid[r] ? x4[i4] : f32x4{};
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ck.key[r][e] = order_key(v[r][e]);
+}
+
 __global__ __launch_bounds__(kMT) void topk_hist(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
                                                  int* hist, int nchunks, int shift) {
   __shared__ int h[256];
   const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
   h[t] = 0;
-  __syncthreads();
   const float* x = src + jobs.src_off[j];
   const uint32_t prefix = st[j].prefix, mask = st[j].mask;
-  const int64_t end = min(n, (int64_t)(c + 1) * kChunk);
-  for (int64_t i = (int64_t)c * kChunk + t; i < end; i += kMT) {
-    const uint32_t key = order_key(x[i]);
-    if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
-  }
+  ChunkKeys ck;
+  load_chunk(x, n, c, t, ck);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = ck.key[r][e];
+      if (ck.valid[r] && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
+    }
   __syncthreads();
   hist[((int64_t)j * nchunks + c) * 256 + t] = h[t];
 }
@@ -211,13 +242,16 @@ __global__ __launch_bounds__(kMT) void topk_count(const float* src, int64_t n, T
   const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
   const float* x = src + jobs.src_off[j];
   const uint32_t T = st[j].prefix;
-  const int64_t end = min(n, (int64_t)(c + 1) * kChunk);
+  ChunkKeys ck;
+  load_chunk(x, n, c, t, ck);
   int gt = 0, eq = 0;
-  for (int64_t i = (int64_t)c * kChunk + t; i < end; i += kMT) {
-    const uint32_t key = order_key(x[i]);
-    gt += key > T;
-    eq += key == T;
-  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gt += ck.valid[r] & (ck.key[r][e] > T);
+      eq += ck.valid[r] & (ck.key[r][e] == T);
+    }
 #pragma unroll
   for (int d = 32; d > 0; d >>= 1) {
     gt += __shfl_xor(gt, d);
@@ -255,27 +289,44 @@ __global__ void topk_bases(const TopkState* st, const int* counts, int* bases, i
   }
 }
 
+// Ordered compaction of a chunk: per round, thread t's four scores are
+// consecutive in index order, so one workgroup scan per round places them.
 __global__ __launch_bounds__(kMT) void topk_write(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
-                                                  const int* bases, int32_t* dst, int nchunks) {
+                                                  const int* bases, int32_t* dst, int32_t* dst2, int split,
+                                                  int nchunks) {
   __shared__ int warp_sum[kMT / 64];
   const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
   const float* x = src + jobs.src_off[j];
-  int32_t* out = dst + jobs.dst_off[j];
+  int32_t* out = (j < split ? dst : dst2) + jobs.dst_off[j];
   const uint32_t T = st[j].prefix;
   const int need = st[j].rem;
   int base = bases[((int64_t)j * nchunks + c) * 2];
   int eq_base = bases[((int64_t)j * nchunks + c) * 2 + 1];
-  const int64_t end = min(n, (int64_t)(c + 1) * kChunk);
-  for (int64_t start = (int64_t)c * kChunk; start < end; start += kMT) {
-    const int64_t i = start + t;
-    const uint32_t key = i < end ? order_key(x[i]) : 0u;
-    const int gt = (i < end) & (key > T);
-    const int eq = (i < end) & (key == T);
+  ChunkKeys ck;
+  load_chunk(x, n, c, t, ck);
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    int gt[4], eq[4], eqc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gt[e] = ck.valid[r] & (ck.key[r][e] > T);
+      eq[e] = ck.valid[r] & (ck.key[r][e] == T);
+      eqc += eq[e];
+    }
     int eq_total, sel_total;
-    const int eq_rank = eq_base + block_excl_scan<kMT>(eq, warp_sum, &eq_total);
-    const int sel = gt | (eq & (eq_rank < need));
-    const int pos = base + block_excl_scan<kMT>(sel, warp_sum, &sel_total);
-    if (sel) out[pos] = (int32_t)i;
+    int eq_rank = eq_base + block_excl_scan<kMT>(eqc, warp_sum, &eq_total);
+    int sel[4], selc = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sel[e] = gt[e] | (eq[e] & (eq_rank < need));
+      eq_rank += eq[e];
+      selc += sel[e];
+    }
+    int pos = base + block_excl_scan<kMT>(selc, warp_sum, &sel_total);
+    const int64_t i0 = 4 * ((int64_t)c * (kChunk / 4) + (int64_t)kMT * r + t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sel[e]) out[pos++] = (int32_t)(i0 + e);
     base += sel_total;
     eq_base += eq_total;
   }
@@ -294,12 +345,24 @@ size_t topk_scratch_bytes(int64_t n, int problems) {
   return 256 + (size_t)problems * sizeof(TopkState) + (size_t)problems * nchunks * (256 + 4) * sizeof(int);
 }
 
-hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, void* scratch,
-                               hipStream_t s) {
+hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, int32_t* dst2,
+                               int split, void* scratch, hipStream_t s) {
   if (jobs.count <= 0) return hipSuccess;
   // Short vectors: one workgroup per vector runs every pass in one launch
   // (the same selection; launch latency dominates at these sizes).
-  if (n <= 2 * kChunk) return launch_topk_rows(src, n, jobs, dst, s);
+  if (n <= 2 * kChunk) {
+    if (split >= jobs.count) return launch_topk_rows(src, n, jobs, dst, s);
+    TopkJobs a = jobs, b = jobs;
+    a.count = split;
+    b.count = jobs.count - split;
+    for (int j = 0; j < b.count; ++j) {
+      b.src_off[j] = jobs.src_off[split + j];
+      b.dst_off[j] = jobs.dst_off[split + j];
+      b.k[j] = jobs.k[split + j];
+    }
+    const hipError_t e = launch_topk_rows(src, n, a, dst, s);
+    return e != hipSuccess ? e : launch_topk_rows(src, n, b, dst2, s);
+  }
   const int nchunks = (int)((n + kChunk - 1) / kChunk);
   char* w = static_cast<char*>(scratch);
   TopkState* st = reinterpret_cast<TopkState*>(w);
@@ -314,7 +377,7 @@ hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs
   }
   hipLaunchKernelGGL(topk_count, grid, dim3(kMT), 0, s, src, n, jobs, st, counts, nchunks);
   hipLaunchKernelGGL(topk_bases, dim3((unsigned)jobs.count), dim3(64), 0, s, st, counts, bases, nchunks);
-  hipLaunchKernelGGL(topk_write, grid, dim3(kMT), 0, s, src, n, jobs, st, bases, dst, nchunks);
+  hipLaunchKernelGGL(topk_write, grid, dim3(kMT), 0, s, src, n, jobs, st, bases, dst, dst2, split, nchunks);
   return hipGetLastError();
 }
 
