@@ -483,9 +483,8 @@ def main():
 
     w = main_r["w"]
     # Roofline of the dominant kernel, the sparse attention of the headline
-    # layer (on long sequences the per-head kernel by key segments, launched
-    # once per chunk of query blocks, plus the combination of its records and
-    # the fp16 V copy, < 2% together): MFMA-bound work of 4*128 flop per kept
+    # layer (on long sequences the per-head kernel, paced, launched once per
+    # 1024 workgroups, plus the fp16 V copy, < 1%): MFMA-bound work of 4*128 flop per kept
     # (row, key) pair, over the attention call's duration measured with HIP
     # events on the library's stream.
     kept_flop = 4.0 * 128 * main_r["kept"]
@@ -494,9 +493,9 @@ def main():
     traffic, trec = recorded_traffic(a.workload, [os.path.join(csrc, f) for f in ATTN_SOURCES])
     roof = {"bound": "mfma", "achieved": main_s["attention_tflops"], "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": main_s["attention_mfma_frac"], "traffic": traffic,
-            "kernel": "sparse attention stage of one call: the attention kernels (per-head kernel by key "
-                      "segments on long sequences, launched per chunk of query blocks, with the combination of "
-                      "its records) and the fp16 V copy they read",
+            "kernel": "sparse attention stage of one call: the attention kernels (on long sequences the "
+                      "per-head kernel in paced mode, one launch per 1024 workgroups) and the fp16 V copy "
+                      "they read",
             "work": "4*128 flop per kept (row, key) pair, kept pairs counted exactly from the index",
             "flop_per_launch": kept_flop, "launch_ms": round(main_r["t_att"], 3)}
     if traffic is not None:

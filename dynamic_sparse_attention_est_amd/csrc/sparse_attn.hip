@@ -31,6 +31,17 @@
 // rows that several of them read; per (query block, key) the work is
 // unchanged.
 //
+// Paced variant (sparse_attn_paced), for the same long sequences with 64-row
+// blocks: each workgroup walks its block's whole index (columns first, which
+// every block of the head shares, then the ranges in key order) and writes
+// out and lse itself, so there are no records to combine.  A launch holds as
+// many workgroups as are resident at once, and the workgroups of one XCD
+// (which share its L2) keep pace: one that is about to start keys of segment
+// s waits until all of them have passed segment s - pace - 1 (one counter per
+// XCD and segment; bounded waits, so a workgroup never waits for good on one
+// that is not resident).  The pacing orders work only; results do not depend
+// on it.
+//
 // LDS tiles are row-major (one 256-byte row per key) with the 16-byte chunks
 // of row r XOR-swizzled: chunk c sits at chunk slot c ^ swz(r).  One
 // load-to-LDS instruction fills four whole rows (1 KiB of contiguous memory
@@ -76,7 +87,7 @@ struct Piece {
 // and are read with readlane: a wait for memory happens once per 64 ranges,
 // not at every range (a wait there would also wait for the K/V tiles in
 // flight).
-template <bool kClip>
+template <bool kClip, bool kPace = false>
 struct PieceIter {
   const int2* rng;
   int r, r_end;
@@ -85,6 +96,15 @@ struct PieceIter {
   int clo, chi;  // kClip: ranges are cut to the key segment [clo, chi)
   int wbase;     // first range of the window
   int wlo, whi;  // this lane's range of the window
+  // kPace: the segment of the last range piece (pieces are not cut at
+  // segment edges; a piece belongs to the segment of its first key), the
+  // first key past it, the segment count of the launch, this XCD's counters
+  // and group size, whether this wave reports arrivals, and whether pacing
+  // is still on (a wait that runs out switches it off for the rest of the
+  // walk, so a workgroup never waits on one that is not resident).
+  int seg, seg_end, nseg, shift, pace, members;
+  uint32_t* cnt;
+  bool reporter, paced;
   __device__ __forceinline__ void load_window(int first) {
     typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
     wbase = first;
@@ -103,7 +123,39 @@ struct PieceIter {
   __device__ __forceinline__ void start() {
     if (r < r_end) load_window(r);
   }
+  // Segments seg .. s_new - 1 are done (their pieces enumerated).
+  __device__ __forceinline__ void arrive(int s_new) {
+    if (reporter && (threadIdx.x & 63) == 0)
+      for (int s = seg; s < s_new; ++s) __hip_atomic_fetch_add(cnt + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Moves to segment s_new: reports the segments passed, then waits until
+  // every workgroup of the group has passed segment s_new - pace - 1.
+  __device__ __forceinline__ void enter(int s_new) {
+    arrive(s_new);
+    seg = s_new;
+    seg_end = (s_new + 1) << shift;
+    const int need = s_new - pace - 1;
+    if (!paced || need < 0) return;
+    for (int t = 0;; ++t) {
+      uint32_t v = 0;
+      if ((threadIdx.x & 63) == 0) v = __hip_atomic_load(cnt + need, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v = __builtin_amdgcn_readfirstlane(v);
+      if (v >= (uint32_t)members) return;
+      if (t >= 4096) {
+        paced = false;
+        return;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
   __device__ __forceinline__ bool next(Piece& p) {
+    if (kPace && c < c_end) {  // columns first: every block of a head reads them
+      p.start = c;
+      p.count = min(kKP, c_end - c);
+      p.is_col = 1;
+      c += p.count;
+      return true;
+    }
     while (lo >= hi && r < r_end) {
       if (r - wbase >= 64) load_window(r);
       lo = __builtin_amdgcn_readlane(wlo, r - wbase);
@@ -115,11 +167,17 @@ struct PieceIter {
       ++r;
     }
     if (lo < hi) {
+      if (kPace && lo >= seg_end) enter(lo >> shift);
       p.start = lo;
       p.count = min(kKP, hi - lo);
       p.is_col = 0;
       lo += p.count;
       return true;
+    }
+    if (kPace) {
+      if (seg < nseg) arrive(nseg);
+      seg = nseg;
+      return false;
     }
     if (c < c_end) {
       p.start = c;
@@ -256,7 +314,16 @@ __device__ __forceinline__ void wave_lower_bounds(Bound (&s)[4], const int2* rng
   }
 }
 
-template <bool kSeg, int kRows>
+// Paced mode: workgroup x takes the item bl-th from the top of the chunk's
+// blocks [seg_b0, seg_b0 + seg_nb) and head list[hi]; its pacing group is its
+// XCD (x % 8, as workgroups are dealt round-robin over the XCDs).
+__device__ __forceinline__ void map_work_paced(int x, const AttnArgs& a, int& h, int& b) {
+  const int bl = x / a.n_list, hi = x - bl * a.n_list;
+  b = a.seg_b0 + a.seg_nb - 1 - bl;
+  h = a.list[hi];
+}
+
+template <bool kSeg, int kRows, bool kPace = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   constexpr int kWaves = kRows / 32;  // one wavefront per 32 query rows
   constexpr int kL = 4 * (2 / kWaves);  // load-to-LDS instructions per wave and tile
@@ -275,6 +342,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   if (kSeg) {
     int slot;
     map_work_seg<kRows>(blockIdx.x, a, h, b, sg, slot);
+  } else if (kPace) {
+    map_work_paced(blockIdx.x, a, h, b);
   } else
     map_work<kRows>(blockIdx.x, a, h, b);
   const int kvh = h / a.grp;
@@ -299,7 +368,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   };
   if (kSeg) load_q();
 
-  PieceIter<kSeg> it{};
+  PieceIter<kSeg, kPace> it{};
+  if (kPace) {
+    const int total = a.n_list * a.seg_nb, grp = blockIdx.x & 7;
+    it.members = total / 8 + (grp < total % 8 ? 1 : 0);
+    it.nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kRows - 1) >> a.seg_shift) + 1;
+    it.cnt = a.pace_cnt + grp * a.seg_n;
+    it.shift = a.seg_shift;
+    it.pace = a.pace;
+    it.seg = 0;
+    it.seg_end = 1 << a.seg_shift;
+    it.reporter = w == 0;
+    it.paced = true;
+  }
   global_int* col = nullptr;
   bool ashape = false;
   int sink = 0, window = 0;
@@ -616,6 +697,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   attn_body<true, 64>(a);
 }
 
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_paced(AttnArgs a) {
+  attn_body<false, 64, true>(a);
+}
+
 // 32-row query blocks: one wavefront per work item, filling its tiles alone.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd32(AttnArgs a) {
   attn_body<false, 32>(a);
@@ -726,6 +811,24 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s) {
     hipLaunchKernelGGL(sparse_attn_fwd, dim3((unsigned)blocks), dim3(128), 0, s, a);
   else
     hipLaunchKernelGGL(sparse_attn_fwd32, dim3((unsigned)blocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_paced(const AttnArgs& a, hipStream_t s) {
+  const int nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
+  if (nseg > a.seg_n || !a.table) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sparse_attn_paced, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_u32(uint32_t* p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, p, count);
   return hipGetLastError();
 }
 
