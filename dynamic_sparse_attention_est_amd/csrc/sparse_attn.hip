@@ -77,9 +77,14 @@ __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 
 
 struct Piece {
   int start;   // first key (range piece) or first column slot (column piece)
-  int count;   // 1..32
+  int count;   // 1..32 (0: past the end of the walk)
   int is_col;
+  int mask;    // masking the piece needs (set by the kernel when the piece is taken)
 };
+
+// Start key of a piece past the end: its tile offsets (start * 256 + ...)
+// are >= 2^31, beyond any KV head's bytes (n <= 2^23).
+constexpr int kPastEnd = 1 << 23;
 
 // Walks a query block's ranges in pieces of <= 32 consecutive keys, then its
 // column list in pieces of <= 32 listed keys.  The position is uniform.  Range
@@ -466,41 +471,71 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   const float sl2 = a.scale_log2;
   const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 
-  // Pieces i (cur), i+1, i+2, i+3.  Column keys (this lane's four rows):
-  // ck1 of piece i+1 (its V tile is loaded this iteration), ck2 of piece i+2
-  // (K tile this iteration, V tile next), ck3 fetched this iteration.
-  Piece cur{}, p1{}, p2{}, p3{};
+  // Pieces in flight: piece i + k sits in slot (i + k) & 3, k = 0..3, with
+  // its column keys (this lane's rows of the piece's tiles).  The loop body
+  // is unrolled four times, so slots, tile buffers and key slots are
+  // compile-time choices and nothing is copied from slot to slot.  A piece
+  // with count 0 lies past the end of the walk: its tile loads fall outside
+  // the KV head (the range check returns zeros without reading memory) and
+  // it is never computed.  mask: 0 none, 1 the piece's tail only (a range
+  // piece of fewer than 32 keys), 2 per element (the diagonal block, an
+  // A-shape window edge, or a column piece).
+  Piece pc0{}, pc1{}, pc2{}, pc3{};
   ColKeys<kL> ck0{}, ck1{}, ck2{}, ck3{};
-  auto fetch_keys = [&](const Piece& p, ColKeys<kL>& ck) {
-    if (p.is_col) {
+  // slot K's piece and column keys (K a compile-time constant)
+  auto pc = [&](auto k) __attribute__((always_inline)) -> Piece& {
+    constexpr int K = decltype(k)::value & 3;
+    if constexpr (K == 0) return pc0;
+    else if constexpr (K == 1) return pc1;
+    else if constexpr (K == 2) return pc2;
+    else return pc3;
+  };
+  auto ck = [&](auto k) __attribute__((always_inline)) -> ColKeys<kL>& {
+    constexpr int K = decltype(k)::value & 3;
+    if constexpr (K == 0) return ck0;
+    else if constexpr (K == 1) return ck1;
+    else if constexpr (K == 2) return ck2;
+    else return ck3;
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  auto fetch = [&](Piece& p, ColKeys<kL>& c) __attribute__((always_inline)) {
+    Piece q;
+    if (!it.next(q)) {
+      q.start = kPastEnd;
+      q.count = 0;
+      q.is_col = 0;
+    }
+    const int kmax = q.start + q.count - 1;
+    const bool far = ashape && kmax >= sink && row0 + kRows - 1 - max(q.start, sink) >= window;
+    // (every field is written on every path, so the compiler keeps the
+    // slots in registers)
+    q.mask = q.count == 0 ? 0 : q.is_col || kmax > row0 || far ? 2 : q.count < kKP ? 1 : 0;
+    p = q;
+    if (q.is_col) {
 #pragma unroll
-      for (int j = 0; j < kL; ++j) ck.k[j] = col_key(p, col, 4 * kL * w + 4 * j + rq);
+      for (int j = 0; j < kL; ++j) c.k[j] = col_key(q, col, 4 * kL * w + 4 * j + rq);
     }
   };
   // Mask keys of a column piece: lanes with lane%16 == 0 hold rows 4 kL w + 4j.
-  auto store_keys = [&](int* dst, const ColKeys<kL>& ck) {
+  auto store_keys = [&](int* dst, const ColKeys<kL>& c) __attribute__((always_inline)) {
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int j = 0; j < kL; ++j) dst[4 * kL * w + 4 * j + rq] = ck.k[j];
+      for (int j = 0; j < kL; ++j) dst[4 * kL * w + 4 * j + rq] = c.k[j];
     }
   };
   it.start();
-  const bool h0 = it.next(cur);
-  bool h1 = h0 && it.next(p1);
-  bool h2 = h1 && it.next(p2);
-  if (h0) fetch_keys(cur, ck0);
-  if (h1) fetch_keys(p1, ck1);
-  if (h2) fetch_keys(p2, ck2);
+  fetch(pc0, ck0);
+  fetch(pc1, ck1);
+  fetch(pc2, ck2);
   __builtin_amdgcn_s_waitcnt(0);
-  if (h0) {
-    load_tile(kr, kb0, w, lofs, cofs, cur, ck0);
-    load_tile(vr, vb0, w, lofs, cofs, cur, ck0);
-    if (cur.is_col) store_keys(key_lds[0], ck0);
-  }
-  if (h1) {
-    load_tile(kr, kb1, w, lofs, cofs, p1, ck1);
-    if (p1.is_col) store_keys(key_lds[1], ck1);
-  }
+  load_tile(kr, kb0, w, lofs, cofs, pc0, ck0);
+  load_tile(vr, vb0, w, lofs, cofs, pc0, ck0);
+  if (pc0.is_col) store_keys(key_lds[0], ck0);
+  load_tile(kr, kb1, w, lofs, cofs, pc1, ck1);
+  if (pc1.is_col) store_keys(key_lds[1], ck1);
   // Settle every outstanding load (Q fragments, first tiles) here, so the
   // wait for them is not placed inside the loop.
   __builtin_amdgcn_s_waitcnt(0);
@@ -515,51 +550,39 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   }
   __syncthreads();  // kb0 is refilled in the first iteration
 
-  int i = 0;
-  // One pipeline iteration; PAR = i & 1 picks the buffers at compile time, so
-  // the compiler sees that the tiles being loaded are not the ones being read.
-  auto step = [&](auto par) -> bool {
+  // One pipeline iteration for piece i with PAR = i & 3.
+  auto step = [&](auto par) __attribute__((always_inline)) -> bool {
     constexpr int PAR = decltype(par)::value;
-    char* const kfill = PAR ? kb1 : kb0;        // K of piece i+2 (piece i's buffer)
-    const char* const kread = PAR ? kb0 : kb1;  // K of piece i+1
-    char* const vfill = PAR ? vb0 : vb1;        // V of piece i+1
-    const char* const vread = PAR ? vb1 : vb0;  // V of piece i
+    using S1 = std::integral_constant<int, (PAR + 1) & 3>;
+    using S2 = std::integral_constant<int, (PAR + 2) & 3>;
+    using S3 = std::integral_constant<int, (PAR + 3) & 3>;
+    const Piece& cur = pc(par);
+    char* const kfill = (PAR & 1) ? kb1 : kb0;        // K of piece i+2 (piece i's buffer)
+    const char* const kread = (PAR & 1) ? kb0 : kb1;  // K of piece i+1
+    char* const vfill = (PAR & 1) ? vb0 : vb1;        // V of piece i+1
+    const char* const vread = (PAR & 1) ? vb1 : vb0;  // V of piece i
 
-    if (h2) {
-      load_tile(kr, kfill, w, lofs, cofs, p2, ck2);
-      if (p2.is_col) store_keys(key_lds[(i + 2) & 3], ck2);
-    }
-    if (h1) load_tile(vr, vfill, w, lofs, cofs, p1, ck1);
-    const bool h3 = h2 && it.next(p3);
-    if (h3) fetch_keys(p3, ck3);
+    load_tile(kr, kfill, w, lofs, cofs, pc(S2{}), ck(S2{}));
+    if (pc(S2{}).is_col) store_keys(key_lds[S2::value], ck(S2{}));
+    load_tile(vr, vfill, w, lofs, cofs, pc(S1{}), ck(S1{}));
+    fetch(pc(S3{}), ck(S3{}));
 
-    // Softmax of piece i.  Masks (causal, piece tail, A-shape window): whether
-    // any is needed is decided per piece, the mask itself per element without
-    // branches.
-    f32x16 s = s_cur;
-    const int* keys = key_lds[i & 3];
-    const int kmin = cur.is_col ? keys[0] : cur.start;
-    const int kmax = cur.is_col ? keys[cur.count - 1] : cur.start + cur.count - 1;
-    const bool far = ashape && kmax >= sink && row0 + kRows - 1 - max(kmin, sink) >= window;
-    if ((cur.count < kKP || kmax > row0 || far) && kmax <= row0 && !far) {
-      // Only the piece's tail (slots >= count) is masked: element r of the
-      // lower half-wave is slot 8 (r / 4) + r % 4, of the upper one 4 more, so
-      // each element takes one select on a lane mask built with scalar
-      // instructions (count < 32 here).
-      const uint32_t bits = (1u << cur.count) - 1u;
+    // Softmax of piece i, masked as its mask kind says (the mask itself per
+    // element without branches).
+    f32x16& s = s_cur;  // masked in place; s_cur takes the next piece's S^T at the end
+    if (cur.mask == 1) {
+      // Only the piece's tail (slots >= count) is masked: element r is slot
+      // 8 (r / 4) + r % 4 + 4 g, so it stays iff 8 (r / 4) + r % 4 < count - 4 g.
+      const int thr = cur.count - 4 * g;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 8 * (r >> 2) + (r & 3);
-        const uint64_t lanes = (((bits >> c) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                               (((bits >> (c + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-        s[r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? s[r] : -INFINITY;
-      }
-    } else if (cur.count < kKP || kmax > row0 || far) {
-      // Slot of element r: 8 (r / 4) + 4 g + r % 4.  In the segment variant
-      // the base is made opaque here so the sixteen slots are formed inside
-      // the masked path instead of being held in registers across the loop.
+      for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) < thr ? s[r] : -INFINITY;
+    } else if (cur.mask == 2) {
+      // Slot of element r: 8 (r / 4) + 4 g + r % 4.  The base is made opaque
+      // here so the sixteen slots are formed inside the masked path instead of
+      // being held in registers across the loop.
+      const int* keys = key_lds[PAR];
       int g4 = 4 * g;
-      if (kSeg) asm volatile("" : "+v"(g4));
+      asm volatile("" : "+v"(g4));
       int key[16];
       if (cur.is_col) {
 #pragma unroll
@@ -633,21 +656,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[4 + dt], pb[1], o[dt], 0, 0, 0);
     l_run += sum;
     __syncthreads();
-    if (!h1) return false;
     s_cur = s_nxt;
-    cur = p1;
-    p1 = p2;
-    p2 = p3;
-    h1 = h2;
-    h2 = h3;
-    // column keys move along only with column pieces (range pieces never read them)
-    if (p1.is_col) ck1 = ck2;
-    if (p2.is_col) ck2 = ck3;
-    ++i;
-    return true;
+    return pc(S1{}).count != 0;
   };
-  if (h0) {
-    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+  if (pc0.count != 0) {
+    while (step(C0{}) && step(C1{}) && step(C2{}) && step(C3{})) {
     }
   }
 
