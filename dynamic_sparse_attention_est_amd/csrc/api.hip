@@ -48,10 +48,11 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 #ifndef MSA_SEG_CAP_MB
 #define MSA_SEG_CAP_MB 4096
 #endif
-// Paced mode of the per-head kernel (64-row blocks of the heads that would
-// run by key segments): launches of kPaceSlots workgroups (the resident
-// count at four per CU), segments of 2^kPaceShift keys, a workgroup at most
-// kPaceLag + 1 segments ahead of the slowest of its XCD.  On a 1M-key
+// Paced mode of the per-head kernel (the heads that would run by key
+// segments): launches of kPaceSlots workgroups (the resident count at four
+// per CU, set by LDS for both the two-wave 64-row and the one-wave 32-row
+// workgroups), segments of 2^kPaceShift keys, a workgroup at most kPaceLag +
+// 1 segments ahead of the slowest of its XCD.  On a 1M-key
 // Vertical-Slash layer the workgroups of an XCD then read their K/V rows
 // from L2 (92% hits against 33% by key segments; HBM reads 31 -> 3.4 TB per
 // call) and attention takes 12% less time.  Swept there: 2^10..2^15-key
@@ -83,11 +84,13 @@ size_t seg_record_bytes(int64_t n, int64_t nb, int heads) {
 }
 
 // Paced mode: query blocks per launch for `heads` heads, and the pacing
-// counters of all launches of a call (per launch, 8 XCDs x segments).
+// counters of all launches of a call over nb 64-row blocks split in blocks
+// of `rows` rows (per launch, 8 XCDs x segments).
 int64_t pace_blocks(int heads) { return std::max<int64_t>(1, kPaceSlots / std::max(heads, 1)); }
-size_t pace_counter_words(int64_t n, int64_t nb, int heads) {
+size_t pace_counter_words(int64_t n, int64_t nb, int heads, int rows) {
   const int64_t nseg = ((n - 1) >> kPaceShift) + 1;
-  const int64_t launches = (nb + pace_blocks(heads) - 1) / pace_blocks(heads);
+  const int64_t nblk = nb * (kBM / rows);
+  const int64_t launches = (nblk + pace_blocks(heads) - 1) / pace_blocks(heads);
   return (size_t)launches * 8 * (size_t)nseg;
 }
 
@@ -128,7 +131,7 @@ struct Plan {
   std::vector<int16_t> solo32_seg;  // the same with 32-row blocks
   int seg_shift = 0;
   size_t seg_part_off = 0, seg_part_bytes = 0;
-  bool paced = false;  // solo_seg runs in paced mode
+  bool paced = false;  // solo_seg and solo32_seg run in paced mode
   size_t pace_off = 0, pace_words = 0;
   // one-shot workspace
   size_t o_vert = 0, o_slash = 0, o_blocks = 0, o_est = 0, o_index = 0, o_attn = 0, o_total = 0;
@@ -269,7 +272,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.out_f32 = prob->out_dtype == MS_OUT_F32;
   P.v16_bytes = align_up((size_t)P.hkv * (size_t)P.n * kD * 2);
   P.attn_bytes = P.v16_bytes + (P.n >= kSegMinN ? align_up(seg_record_bytes(P.n, P.nbq, P.hq)) : 0) +
-                 (P.n >= kSegMinN && kPaced ? align_up(pace_counter_words(P.n, P.nbq, P.hq) * 4) : 0);
+                 (P.n >= kSegMinN && kPaced ? align_up((pace_counter_words(P.n, P.nbq, P.hq, kBM) +
+                                                         pace_counter_words(P.n, P.nbq, P.hq, 32)) * 4)
+                                              : 0);
   if (!have_params) return MS_OK;
   P.p.assign(params, params + P.hq);
   P.vs_slot.assign(P.hq, -1);
@@ -494,8 +499,8 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     *l = ordered;
   }
   P.attn_bytes = P.v16_bytes;
-  P.paced = kPaced && !P.solo_seg.empty();
-  const size_t rec_heads = P.paced ? P.solo32_seg.size() : std::max(P.solo_seg.size(), P.solo32_seg.size());
+  P.paced = kPaced && (!P.solo_seg.empty() || !P.solo32_seg.empty());
+  const size_t rec_heads = P.paced ? 0 : std::max(P.solo_seg.size(), P.solo32_seg.size());
   if (rec_heads > 0) {
     // the two lists run one after the other and share the record space
     P.seg_shift = kSegShift;
@@ -505,7 +510,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   }
   if (P.paced) {
     P.pace_off = P.attn_bytes;
-    P.pace_words = pace_counter_words(P.n, P.nbq, (int)P.solo_seg.size());
+    P.pace_words = 0;
+    if (!P.solo_seg.empty()) P.pace_words += pace_counter_words(P.n, P.nbq, (int)P.solo_seg.size(), kBM);
+    if (!P.solo32_seg.empty()) P.pace_words += pace_counter_words(P.n, P.nbq, (int)P.solo32_seg.size(), 32);
     P.attn_bytes += align_up(P.pace_words * 4);
   }
   P.index_bytes = off;
@@ -714,24 +721,31 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
     HIP_TRY(launch_sparse_attn(a, rows, s), "attention launch");
   }
   if (P.paced) {
-    a.n_list = (int)P.solo_seg.size();
-    for (size_t i = 0; i < P.solo_seg.size(); ++i) a.list[i] = P.solo_seg[i];
     uint32_t* cnt = reinterpret_cast<uint32_t*>(attn_ws + P.pace_off);
     HIP_TRY(launch_zero_u32(cnt, (int64_t)P.pace_words, s), "pacing counter launch");
     const int64_t nseg = ((P.n - 1) >> kPaceShift) + 1;
-    const int64_t cb = pace_blocks(a.n_list);
     a.seg_shift = kPaceShift;
     a.seg_n = (int)nseg;
     a.pace = kPaceLag;
-    for (int64_t b0 = 0, l = 0; b0 < P.nbq; b0 += cb, ++l) {
-      a.seg_b0 = (int)std::max<int64_t>(0, P.nbq - b0 - cb);
-      a.seg_nb = (int)(P.nbq - b0 - a.seg_b0);
-      a.pace_cnt = cnt + l * 8 * nseg;
-      HIP_TRY(launch_sparse_attn_paced(a, s), "attention launch");
+    for (auto [list, rows] : {std::make_pair(&P.solo_seg, kBM), std::make_pair(&P.solo32_seg, 32)}) {
+      if (list->empty()) continue;
+      a.n_list = (int)list->size();
+      for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
+      // launches of the list's blocks of `rows` rows, longest first, each
+      // with its own counters
+      const int64_t nblk = P.nbq * (kBM / rows);
+      const int64_t cb = pace_blocks(a.n_list);
+      for (int64_t b0 = 0; b0 < nblk; b0 += cb) {
+        a.seg_b0 = (int)std::max<int64_t>(0, nblk - b0 - cb);
+        a.seg_nb = (int)(nblk - b0 - a.seg_b0);
+        a.pace_cnt = cnt;
+        cnt += 8 * nseg;
+        HIP_TRY(launch_sparse_attn_paced(a, rows, s), "attention launch");
+      }
     }
   }
   for (auto [list, rows] : {std::make_pair(&P.solo_seg, kBM), std::make_pair(&P.solo32_seg, 32)}) {
-    if (list->empty() || (P.paced && rows == kBM)) continue;
+    if (list->empty() || P.paced) continue;
     a.n_list = (int)list->size();
     for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
     // Chunks of query blocks whose records fit the workspace, each followed

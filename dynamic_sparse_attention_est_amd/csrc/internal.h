@@ -150,11 +150,12 @@ struct AttnArgs {
   float* part;
   int32_t seg_shift, seg_b0, seg_nb, seg_n;
   // Paced mode of the per-head kernel: query blocks [seg_b0, seg_b0 +
-  // seg_nb) of every listed head, each walked whole (columns, then ranges in
-  // key order) by one workgroup that keeps pace with the other workgroups of
-  // its XCD: before it starts keys of segment s (2^seg_shift keys) it waits,
-  // for a bounded time, until all of them have passed segment s - pace - 1.
-  // pace_cnt: seg_n counters per XCD (zero before the launch).
+  // seg_nb) of every listed head (blocks of the heads' CSR: 64 or 32 rows),
+  // each walked whole (columns, then ranges in key order) by one workgroup
+  // that keeps pace with the other workgroups of its XCD: before it starts
+  // keys of segment s (2^seg_shift keys) it waits, for a bounded time, until
+  // all of them have passed segment s - pace - 1.  pace_cnt: seg_n counters
+  // per XCD (zero before the launch).
   uint32_t* pace_cnt;
   int32_t pace;
 };
@@ -170,8 +171,8 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s);
 // into out / lse.  With 32-row blocks two work items fill the two halves of
 // one 64-row record, so the combination is the same.
 hipError_t launch_sparse_attn_seg(const AttnArgs& a, int rows, hipStream_t s);
-// Paced mode (64-row blocks): one launch over the chunk's blocks.
-hipError_t launch_sparse_attn_paced(const AttnArgs& a, hipStream_t s);
+// Paced mode: one launch over the chunk's blocks of `rows` rows (64 or 32).
+hipError_t launch_sparse_attn_paced(const AttnArgs& a, int rows, hipStream_t s);
 // Zeroes `count` 32-bit words (a kernel, so that the call can be captured).
 hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s);
 // Full causal attention, query heads that share a KV head served together.

@@ -377,7 +377,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   if (kPace) {
     const int total = a.n_list * a.seg_nb, grp = blockIdx.x & 7;
     it.members = total / 8 + (grp < total % 8 ? 1 : 0);
-    it.nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kRows - 1) >> a.seg_shift) + 1;
+    it.nseg = (((a.qb0 * kPer + a.seg_b0 + a.seg_nb) * kRows - 1) >> a.seg_shift) + 1;
     it.cnt = a.pace_cnt + grp * a.seg_n;
     it.shift = a.seg_shift;
     it.pace = a.pace;
@@ -714,6 +714,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   attn_body<false, 64, true>(a);
 }
 
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_paced32(AttnArgs a) {
+  attn_body<false, 32, true>(a);
+}
+
 // 32-row query blocks: one wavefront per work item, filling its tiles alone.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd32(AttnArgs a) {
   attn_body<false, 32>(a);
@@ -827,10 +831,15 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn_paced(const AttnArgs& a, hipStream_t s) {
-  const int nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
+hipError_t launch_sparse_attn_paced(const AttnArgs& a, int rows, hipStream_t s) {
+  if (rows != kBM && rows != 32) return hipErrorInvalidValue;
+  const int per = kBM / rows;
+  const int nseg = (((a.qb0 * per + a.seg_b0 + a.seg_nb) * rows - 1) >> a.seg_shift) + 1;
   if (nseg > a.seg_n || !a.table) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sparse_attn_paced, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(128), 0, s, a);
+  if (rows == kBM)
+    hipLaunchKernelGGL(sparse_attn_paced, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_paced32, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
