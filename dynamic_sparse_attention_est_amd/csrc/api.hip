@@ -36,52 +36,23 @@ ms_status device_fail(hipError_t e, const char* what) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Key-segment mode of the per-head attention kernel (sequences of at least
-// kSegMinN keys): segments of 2^kSegShift keys, partial records in at most
-// kSegPartCap bytes of the attention workspace.
-#ifndef MSA_SEG_SHIFT
-#define MSA_SEG_SHIFT 15
-#endif
-#ifndef MSA_SEG_MIN_N
-#define MSA_SEG_MIN_N 131072
-#endif
-#ifndef MSA_SEG_CAP_MB
-#define MSA_SEG_CAP_MB 4096
-#endif
-// Paced mode of the per-head kernel (the heads that would run by key
-// segments): launches of kPaceSlots workgroups (the resident count at four
-// per CU, set by LDS for both the two-wave 64-row and the one-wave 32-row
-// workgroups), segments of 2^kPaceShift keys, a workgroup at most kPaceLag +
-// 1 segments ahead of the slowest of its XCD.  On a 1M-key
-// Vertical-Slash layer the workgroups of an XCD then read their K/V rows
-// from L2 (92% hits against 33% by key segments; HBM reads 31 -> 3.4 TB per
-// call) and attention takes 12% less time.  Swept there: 2^10..2^15-key
-// segments, lag 0..4; 2^13 with lag 1 was fastest.
-#ifndef MSA_PACE
-#define MSA_PACE 1
-#endif
-#ifndef MSA_PACE_SHIFT
-#define MSA_PACE_SHIFT 13
-#endif
-#ifndef MSA_PACE_LAG
-#define MSA_PACE_LAG 1
-#endif
-constexpr bool kPaced = MSA_PACE != 0;
-constexpr int kPaceShift = MSA_PACE_SHIFT;
-constexpr int kPaceLag = MSA_PACE_LAG;
+// Paced mode of the per-head kernel, for heads served one by one whose key
+// sets are long (on average at least kLongKeys keys per query block) on
+// sequences of at least kPaceMinN keys: launches of kPaceSlots workgroups
+// (the resident count at four per CU, set by LDS for both the two-wave
+// 64-row and the one-wave 32-row workgroups), segments of 2^kPaceShift keys,
+// a workgroup at most kPaceLag + 1 segments ahead of the slowest of its XCD.
+// On a 1M-key Vertical-Slash layer the workgroups of an XCD then read their
+// K/V rows from L2 (92% hits against 33% for the scheme it replaced, one
+// workgroup per (block, 32768-key segment) with partial results combined
+// afterwards; HBM reads 31 -> 3.4 TB per call) and attention takes 12% less
+// time.  Swept there: 2^10..2^15-key segments, lag 0..4; 2^13 with lag 1 was
+// fastest.
+constexpr int64_t kPaceMinN = 131072;
+constexpr double kLongKeys = 32768.0;
+constexpr int kPaceShift = 13;
+constexpr int kPaceLag = 1;
 constexpr int kPaceSlots = 1024;
-constexpr int kSegShift = MSA_SEG_SHIFT;
-constexpr int64_t kSegMinN = MSA_SEG_MIN_N;
-constexpr size_t kSegPartCap = (size_t)MSA_SEG_CAP_MB << 20;
-
-// Record space for `heads` heads in key-segment mode: every block's records,
-// or kSegPartCap when that is less (the blocks then run in chunks), but at
-// least one block's.
-size_t seg_record_bytes(int64_t n, int64_t nb, int heads) {
-  const int64_t nseg = ((n - 1) >> kSegShift) + 1;
-  const size_t per_block = (size_t)nseg * heads * kSegRecFloats * 4;
-  return std::max(per_block, std::min(kSegPartCap, per_block * (size_t)nb));
-}
 
 // Paced mode: query blocks per launch for `heads` heads, and the pacing
 // counters of all launches of a call over nb 64-row blocks split in blocks
@@ -124,15 +95,12 @@ struct Plan {
   std::vector<int16_t> solo32;   // heads served one by one with 32-row blocks
   std::vector<int16_t> ablk;     // A-shape heads of MHA layers, four query blocks per workgroup
   size_t index_bytes = 0;
-  // attention workspace: fp16 V copy, then the key-segment records (without
+  // attention workspace: fp16 V copy, then the pacing counters (without
   // params: the most any head set needs)
   size_t v16_bytes = 0, attn_bytes = 0;
-  std::vector<int16_t> solo_seg;    // heads served one by one, by key segments (64-row blocks)
-  std::vector<int16_t> solo32_seg;  // the same with 32-row blocks
-  int seg_shift = 0;
-  size_t seg_part_off = 0, seg_part_bytes = 0;
-  bool paced = false;  // solo_seg and solo32_seg run in paced mode
-  size_t pace_off = 0, pace_words = 0;
+  std::vector<int16_t> solo_paced;    // heads served one by one in paced mode (64-row blocks)
+  std::vector<int16_t> solo32_paced;  // the same with 32-row blocks
+  size_t pace_off = 0, pace_words = 0;  // pacing counters in the attention workspace
   // one-shot workspace
   size_t o_vert = 0, o_slash = 0, o_blocks = 0, o_est = 0, o_index = 0, o_attn = 0, o_total = 0;
 };
@@ -271,10 +239,9 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.scale_log2 = scale * 1.4426950408889634f;
   P.out_f32 = prob->out_dtype == MS_OUT_F32;
   P.v16_bytes = align_up((size_t)P.hkv * (size_t)P.n * kD * 2);
-  P.attn_bytes = P.v16_bytes + (P.n >= kSegMinN ? align_up(seg_record_bytes(P.n, P.nbq, P.hq)) : 0) +
-                 (P.n >= kSegMinN && kPaced ? align_up((pace_counter_words(P.n, P.nbq, P.hq, kBM) +
-                                                         pace_counter_words(P.n, P.nbq, P.hq, 32)) * 4)
-                                              : 0);
+  P.attn_bytes = P.v16_bytes + (P.n >= kPaceMinN ? align_up((pace_counter_words(P.n, P.nbq, P.hq, kBM) +
+                                                              pace_counter_words(P.n, P.nbq, P.hq, 32)) * 4)
+                                                  : 0);
   if (!have_params) return MS_OK;
   P.p.assign(params, params + P.hq);
   P.vs_slot.assign(P.hq, -1);
@@ -473,25 +440,25 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     g.ucol_off = (int64_t)take((size_t)uc * 4);
     g.umask_off = (int64_t)take((size_t)uc);
   }
-  // Solo heads with long key sets (on average at least one segment per query
-  // block) on long sequences run paced (64-row blocks) or by key segments
-  // (32-row blocks): the workgroups in flight then share a stretch of K/V in
-  // L2 instead of streaming every block's keys from HBM.  Short, local key
-  // sets (A-shape, small Block-Sparse budgets) stay whole.
-  P.solo_seg.clear();
-  P.solo32_seg.clear();
-  if (P.n >= kSegMinN) {
-    for (auto [solo, seg] : {std::make_pair(&P.solo, &P.solo_seg), std::make_pair(&P.solo32, &P.solo32_seg)}) {
+  // Solo heads with long key sets (on average at least kLongKeys keys per
+  // query block) on long sequences run paced: the workgroups in flight then
+  // share a stretch of K/V in L2 instead of streaming every block's keys from
+  // HBM.  Short, local key sets (A-shape, small Block-Sparse budgets) stay
+  // whole.
+  P.solo_paced.clear();
+  P.solo32_paced.clear();
+  if (P.n >= kPaceMinN) {
+    for (auto [solo, paced] :
+         {std::make_pair(&P.solo, &P.solo_paced), std::make_pair(&P.solo32, &P.solo32_paced)}) {
       std::vector<int16_t> keep;
       for (int16_t h : *solo)
-        (expected_density(P.p[h], P.n) * 0.5 * (double)P.n >= (double)(int64_t{1} << kSegShift) ? *seg : keep)
-            .push_back(h);
+        (expected_density(P.p[h], P.n) * 0.5 * (double)P.n >= kLongKeys ? *paced : keep).push_back(h);
       *solo = keep;
     }
   }
   // Workgroups go round-robin over the 8 XCDs, so order each list to keep
   // the heads of one KV head on one XCD when the count allows.
-  for (std::vector<int16_t>* l : {&P.solo, &P.solo_seg, &P.solo32, &P.solo32_seg}) {
+  for (std::vector<int16_t>* l : {&P.solo, &P.solo_paced, &P.solo32, &P.solo32_paced}) {
     if (l->size() % 8 != 0 || l->empty()) continue;
     const size_t per = l->size() / 8;
     std::vector<int16_t> ordered(l->size());
@@ -499,22 +466,11 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
     *l = ordered;
   }
   P.attn_bytes = P.v16_bytes;
-  P.paced = kPaced && (!P.solo_seg.empty() || !P.solo32_seg.empty());
-  const size_t rec_heads = P.paced ? 0 : std::max(P.solo_seg.size(), P.solo32_seg.size());
-  if (rec_heads > 0) {
-    // the two lists run one after the other and share the record space
-    P.seg_shift = kSegShift;
-    P.seg_part_off = P.attn_bytes;
-    P.seg_part_bytes = seg_record_bytes(P.n, P.nbq, (int)rec_heads);
-    P.attn_bytes += align_up(P.seg_part_bytes);
-  }
-  if (P.paced) {
-    P.pace_off = P.attn_bytes;
-    P.pace_words = 0;
-    if (!P.solo_seg.empty()) P.pace_words += pace_counter_words(P.n, P.nbq, (int)P.solo_seg.size(), kBM);
-    if (!P.solo32_seg.empty()) P.pace_words += pace_counter_words(P.n, P.nbq, (int)P.solo32_seg.size(), 32);
-    P.attn_bytes += align_up(P.pace_words * 4);
-  }
+  P.pace_off = P.attn_bytes;
+  P.pace_words = 0;
+  if (!P.solo_paced.empty()) P.pace_words += pace_counter_words(P.n, P.nbq, (int)P.solo_paced.size(), kBM);
+  if (!P.solo32_paced.empty()) P.pace_words += pace_counter_words(P.n, P.nbq, (int)P.solo32_paced.size(), 32);
+  P.attn_bytes += align_up(P.pace_words * 4);
   P.index_bytes = off;
   // One-shot workspace.
   off = 0;
@@ -720,14 +676,14 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
     for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
     HIP_TRY(launch_sparse_attn(a, rows, s), "attention launch");
   }
-  if (P.paced) {
+  if (P.pace_words > 0) {
     uint32_t* cnt = reinterpret_cast<uint32_t*>(attn_ws + P.pace_off);
     HIP_TRY(launch_zero_u32(cnt, (int64_t)P.pace_words, s), "pacing counter launch");
     const int64_t nseg = ((P.n - 1) >> kPaceShift) + 1;
     a.seg_shift = kPaceShift;
     a.seg_n = (int)nseg;
     a.pace = kPaceLag;
-    for (auto [list, rows] : {std::make_pair(&P.solo_seg, kBM), std::make_pair(&P.solo32_seg, 32)}) {
+    for (auto [list, rows] : {std::make_pair(&P.solo_paced, kBM), std::make_pair(&P.solo32_paced, 32)}) {
       if (list->empty()) continue;
       a.n_list = (int)list->size();
       for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
@@ -742,24 +698,6 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
         cnt += 8 * nseg;
         HIP_TRY(launch_sparse_attn_paced(a, rows, s), "attention launch");
       }
-    }
-  }
-  for (auto [list, rows] : {std::make_pair(&P.solo_seg, kBM), std::make_pair(&P.solo32_seg, 32)}) {
-    if (list->empty() || P.paced) continue;
-    a.n_list = (int)list->size();
-    for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
-    // Chunks of query blocks whose records fit the workspace, each followed
-    // by the combination of its records.
-    const int64_t nseg = ((P.n - 1) >> P.seg_shift) + 1;
-    const size_t per_block = (size_t)nseg * a.n_list * kSegRecFloats * 4;
-    const int64_t cb = std::min<int64_t>(P.nbq, (int64_t)(P.seg_part_bytes / per_block));
-    a.part = reinterpret_cast<float*>(attn_ws + P.seg_part_off);
-    a.seg_shift = P.seg_shift;
-    a.seg_n = (int)nseg;
-    for (int64_t b0 = 0; b0 < P.nbq; b0 += cb) {
-      a.seg_b0 = (int)b0;
-      a.seg_nb = (int)std::min<int64_t>(cb, P.nbq - b0);
-      HIP_TRY(launch_sparse_attn_seg(a, rows, s), "attention launch");
     }
   }
   return MS_OK;

@@ -143,12 +143,6 @@ struct AttnArgs {
   // (grouped sparse kernel) of this launch.
   int32_t n_list;
   int16_t list[kMaxHeads];
-  // Key-segment mode of the per-head kernel: query blocks [seg_b0, seg_b0 +
-  // seg_nb) of every listed head, each split into key segments of
-  // 2^seg_shift keys; seg_n record slots per (head, block); partial results
-  // (kSegRecFloats floats per record) go to part.
-  float* part;
-  int32_t seg_shift, seg_b0, seg_nb, seg_n;
   // Paced mode of the per-head kernel: query blocks [seg_b0, seg_b0 +
   // seg_nb) of every listed head (blocks of the heads' CSR: 64 or 32 rows),
   // each walked whole (columns, then ranges in key order) by one workgroup
@@ -156,21 +150,13 @@ struct AttnArgs {
   // keys of segment s (2^seg_shift keys) it waits, for a bounded time, until
   // all of them have passed segment s - pace - 1.  pace_cnt: seg_n counters
   // per XCD (zero before the launch).
+  int32_t seg_shift, seg_b0, seg_nb, seg_n;
   uint32_t* pace_cnt;
   int32_t pace;
 };
-// Partial record of one (head, query block, key segment): the segment's
-// normalised output O_s / l_s as 64 fp32 rows of 128, then its log-sum-exp
-// per row (-inf for a row with no key in the segment).
-constexpr int kSegRowFloats = kBM * kD;
-constexpr int kSegRecFloats = kSegRowFloats + kBM;
 // rows: query rows per block of the listed heads' CSR (64 or 32; a 32-row
 // block is one wavefront's work item).
 hipError_t launch_sparse_attn(const AttnArgs& a, int rows, hipStream_t s);
-// Key-segment mode: partial records of the chunk, then their combination
-// into out / lse.  With 32-row blocks two work items fill the two halves of
-// one 64-row record, so the combination is the same.
-hipError_t launch_sparse_attn_seg(const AttnArgs& a, int rows, hipStream_t s);
 // Paced mode: one launch over the chunk's blocks of `rows` rows (64 or 32).
 hipError_t launch_sparse_attn_paced(const AttnArgs& a, int rows, hipStream_t s);
 // Zeroes `count` 32-bit words (a kernel, so that the call can be captured).

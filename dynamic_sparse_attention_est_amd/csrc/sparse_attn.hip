@@ -21,20 +21,9 @@
 // grows by more than that.  Buffer-load range checks (one KV head's rows) turn
 // reads past the sequence into zeros, so piece tails need no clamping.
 //
-// Key-segment variant (sparse_attn_seg + seg_combine), for long sequences:
-// a workgroup takes the keys of one query block that fall in one segment of
-// 2^seg_shift keys (its share of the block's ranges, cut at the segment
-// edges, and of its columns, found by a wave-wide search of the CSR) and
-// writes O / l and the log-sum-exp of that share; the combine kernel merges a
-// block's segment records in segment order.  Workgroups are numbered segment
-// first, so the ones in flight read the same segment of K/V and L2 serves the
-// rows that several of them read; per (query block, key) the work is
-// unchanged.
-//
-// Paced variant (sparse_attn_paced), for the same long sequences with 64-row
-// blocks: each workgroup walks its block's whole index (columns first, which
-// every block of the head shares, then the ranges in key order) and writes
-// out and lse itself, so there are no records to combine.  A launch holds as
+// Paced variant (sparse_attn_paced, sparse_attn_paced32), for long sequences:
+// each workgroup walks its block's whole index (columns first, which every
+// block of the head shares, then the ranges in key order).  A launch holds as
 // many workgroups as are resident at once, and the workgroups of one XCD
 // (which share its L2) keep pace: one that is about to start keys of segment
 // s waits until all of them have passed segment s - pace - 1 (one counter per
@@ -92,13 +81,12 @@ constexpr int kPastEnd = 1 << 23;
 // and are read with readlane: a wait for memory happens once per 64 ranges,
 // not at every range (a wait there would also wait for the K/V tiles in
 // flight).
-template <bool kClip, bool kPace = false>
+template <bool kPace>
 struct PieceIter {
   const int2* rng;
   int r, r_end;
   int lo, hi;
   int c, c_end;
-  int clo, chi;  // kClip: ranges are cut to the key segment [clo, chi)
   int wbase;     // first range of the window
   int wlo, whi;  // this lane's range of the window
   // kPace: the segment of the last range piece (pieces are not cut at
@@ -165,10 +153,6 @@ struct PieceIter {
       if (r - wbase >= 64) load_window(r);
       lo = __builtin_amdgcn_readlane(wlo, r - wbase);
       hi = __builtin_amdgcn_readlane(whi, r - wbase);
-      if (kClip) {
-        lo = max(lo, clo);
-        hi = min(hi, chi);
-      }
       ++r;
     }
     if (lo < hi) {
@@ -253,72 +237,6 @@ __device__ __forceinline__ void map_work(int x, const AttnArgs& a, int& h, int& 
   h = a.list[hi];
 }
 
-// Key-segment mode: workgroup x takes segment x / (items per segment) of the
-// item bl-th from the top of the chunk's 64-row blocks [seg_b0, seg_b0 +
-// seg_nb) and head list[hi], (bl, hi) from the rest, so the workgroups in
-// flight share one segment of every KV head's K/V rows.  slot is the partial
-// record of the item's 64-row block; a 32-row item fills half of it.
-template <int kRows>
-__device__ __forceinline__ void map_work_seg(int x, const AttnArgs& a, int& h, int& b, int& sg, int& slot) {
-  constexpr int per = kBM / kRows;
-  const int items = a.seg_nb * per * a.n_list;
-  sg = __builtin_amdgcn_readfirstlane(x / items);
-  const int y = x - sg * items;
-  const int bl = __builtin_amdgcn_readfirstlane(y / a.n_list);
-  const int hi = y - bl * a.n_list;
-  b = (a.seg_b0 + a.seg_nb) * per - 1 - bl;
-  h = a.list[hi];
-  const int bl64 = a.seg_b0 + a.seg_nb - 1 - b / per;  // the 64-row block's place in the chunk, from the top
-  slot = (bl64 * a.n_list + hi) * a.seg_n + sg;
-}
-
-// Four lower bounds at once: for search j, the first i in [lo_j, hi_j) with
-// key_j(i) >= x_j (hi_j if none), every key nondecreasing in i.  All lanes of
-// the wave probe together, 64 probes per search and round, and the four
-// searches' probes of a round are issued together so they share one memory
-// latency.  Keys: j = 0 range ends, 1 range starts, 2 and 3 columns.
-struct Bound {
-  int lo, hi, x;
-};
-__device__ __forceinline__ void wave_lower_bounds(Bound (&s)[4], const int2* rng, global_int* col, int lane) {
-  bool done[4] = {false, false, false, false};
-  for (;;) {
-    int probe[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int size = s[j].hi - s[j].lo;
-      const int step = size > 64 ? (size + 63) >> 6 : 1;
-      const int i = s[j].lo + lane * step;
-      probe[j] = 0x7fffffff;
-      if (!done[j] && i < s[j].hi) probe[j] = j == 0 ? rng[i].y : j == 1 ? rng[i].x : col[i];
-    }
-    bool all = true;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (done[j]) continue;
-      const int size = s[j].hi - s[j].lo;
-      if (size <= 64) {
-        s[j].lo += __popcll(__ballot(probe[j] < s[j].x));
-        s[j].hi = s[j].lo;
-        done[j] = true;
-        continue;
-      }
-      const int step = (size + 63) >> 6;
-      const uint64_t ge = __ballot(probe[j] >= s[j].x);
-      if (ge & 1) {
-        s[j].hi = s[j].lo;
-        done[j] = true;
-        continue;
-      }
-      const int t = ge ? __builtin_ctzll(ge) : 64;  // key(lo + (t-1) step) < x
-      if (t < 64) s[j].hi = min(s[j].hi, s[j].lo + t * step);
-      s[j].lo = s[j].lo + (t - 1) * step + 1;
-      all = false;
-    }
-    if (all) return;
-  }
-}
-
 // Paced mode: workgroup x takes the item bl-th from the top of the chunk's
 // blocks [seg_b0, seg_b0 + seg_nb) and head list[hi]; its pacing group is its
 // XCD (x % 8, as workgroups are dealt round-robin over the XCDs).
@@ -328,7 +246,7 @@ __device__ __forceinline__ void map_work_paced(int x, const AttnArgs& a, int& h,
   h = a.list[hi];
 }
 
-template <bool kSeg, int kRows, bool kPace = false>
+template <int kRows, bool kPace>
 __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   constexpr int kWaves = kRows / 32;  // one wavefront per 32 query rows
   constexpr int kL = 4 * (2 / kWaves);  // load-to-LDS instructions per wave and tile
@@ -343,13 +261,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  int h, b, sg = 0;
-  if (kSeg) {
-    int slot;
-    map_work_seg<kRows>(blockIdx.x, a, h, b, sg, slot);
-  } else if (kPace) {
+  int h, b;
+  if (kPace)
     map_work_paced(blockIdx.x, a, h, b);
-  } else
+  else
     map_work<kRows>(blockIdx.x, a, h, b);
   const int kvh = h / a.grp;
   const int64_t n = a.n;
@@ -357,13 +272,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   // the block's first query row in the sequence, qrow0 its row in Q and out.
   const int row0 = (a.qb0 * kPer + b) * kRows;
   const int64_t qrow0 = (int64_t)b * kRows;
-  const int seg_lo = sg << a.seg_shift;
-  if (kSeg && seg_lo > row0 + kRows - 1) return;  // past the block's last key: no record
-  const int seg_hi = seg_lo + (1 << a.seg_shift);
 
   // Q fragments: B operand of S^T = K Q^T; lane holds row l32 of this wave's
-  // 32 rows and d = 16t + 8g .. +8.  The segment variant issues them before
-  // its index search, so the two latencies overlap.
+  // 32 rows and d = 16t + 8g .. +8.
   const uint16_t* qh = a.q + ((int64_t)h * a.qm + qrow0 + 32 * w) * kD;
   bf16x8 qf[8];
   auto load_q = [&]() {
@@ -371,9 +282,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     for (int t = 0; t < 8; ++t)
       qf[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + l32 * kD + 16 * t + 8 * g));
   };
-  if (kSeg) load_q();
 
-  PieceIter<kSeg, kPace> it{};
+  PieceIter<kPace> it{};
   if (kPace) {
     const int total = a.n_list * a.seg_nb, grp = blockIdx.x & 7;
     it.members = total / 8 + (grp < total % 8 ? 1 : 0);
@@ -404,23 +314,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       sink = d.p0;
       window = d.p1;
     }
-    if (kSeg) {
-      // This segment's share of the block's index: ranges that end after
-      // seg_lo and start before seg_hi (cut to the segment), and columns in
-      // [seg_lo, seg_hi).
-      Bound sb[4] = {{it.r, it.r_end, seg_lo + 1}, {it.r, it.r_end, seg_hi}, {it.c, it.c_end, seg_lo},
-                     {it.c, it.c_end, seg_hi}};
-      wave_lower_bounds(sb, it.rng, col, lane);
-      it.r = __builtin_amdgcn_readfirstlane(sb[0].lo);
-      it.r_end = __builtin_amdgcn_readfirstlane(sb[1].lo);
-      it.c = __builtin_amdgcn_readfirstlane(sb[2].lo);
-      it.c_end = __builtin_amdgcn_readfirstlane(sb[3].lo);
-      it.clo = seg_lo;
-      it.chi = seg_hi;
-    }
   } else {
-    it.lo = kSeg ? seg_lo : 0;
-    it.hi = kSeg ? min(seg_hi, row0 + kRows) : row0 + kRows;
+    it.lo = 0;
+    it.hi = row0 + kRows;
   }
 
   // Byte size of one KV head (<= 2^31 for n <= 2^23), taken as unsigned by the
@@ -431,7 +327,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   const __amdgpu_buffer_rsrc_t vr =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
 
-  if (!kSeg) load_q();
+  load_q();
 
   // Per-lane constants.  Loads: this lane's row rw_j = 16w + 4j + lane/16
   // and chunk (lane%16) ^ swz(rw_j); lofs = row offset + chunk offset,
@@ -666,22 +562,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 
   const float lt = sum_halves(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  // Epilogue: out = O / l, lse = m ln2 + ln l.  The segment variant writes
-  // the same two results to its partial record (fp32 rows of 128, then the
-  // 64 lse values), with the base pointers shifted so the row offsets match.
+  // Epilogue: out = O / l, lse = m ln2 + ln l.
   const int64_t orow = (int64_t)h * a.qm + qrow0 + 32 * w + l32;  // this lane's row of out and lse
   const int64_t obase = orow * kD;
   float* out_f32 = reinterpret_cast<float*>(a.out);
   float* lse = a.lse;
-  if (kSeg) {
-    // the record holds the 64 rows of the item's 64-row block
-    int hh, bb, ss, slot;
-    map_work_seg<kRows>(blockIdx.x, a, hh, bb, ss, slot);
-    float* rec = a.part + (int64_t)__builtin_amdgcn_readfirstlane(slot) * kSegRecFloats;
-    const int64_t rrow0 = (int64_t)(b / kPer) * kBM;
-    out_f32 = rec - ((int64_t)h * a.qm + rrow0) * kD;
-    lse = rec + kSegRowFloats - ((int64_t)h * a.qm + rrow0);
-  }
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -689,7 +574,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       const int d0 = 32 * dt + 8 * q4 + 4 * g;
       const float x0 = o[dt][4 * q4 + 0] * inv, x1 = o[dt][4 * q4 + 1] * inv;
       const float x2 = o[dt][4 * q4 + 2] * inv, x3 = o[dt][4 * q4 + 3] * inv;
-      if (kSeg || a.out_f32) {
+      if (a.out_f32) {
         *reinterpret_cast<f32x4*>(out_f32 + obase + d0) = f32x4{x0, x1, x2, x3};
       } else {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -698,102 +583,25 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
       }
     }
   }
-  if ((kSeg || lse) && g == 0)
+  if (lse && g == 0)
     lse[orow] = lt > 0.f ? m_run * 0.69314718055994530942f + logf(lt) : -INFINITY;
 }
 
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd(AttnArgs a) {
-  attn_body<false, 64>(a);
-}
-
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_seg(AttnArgs a) {
-  attn_body<true, 64>(a);
+  attn_body<64, false>(a);
 }
 
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_paced(AttnArgs a) {
-  attn_body<false, 64, true>(a);
-}
-
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_paced32(AttnArgs a) {
-  attn_body<false, 32, true>(a);
+  attn_body<64, true>(a);
 }
 
 // 32-row query blocks: one wavefront per work item, filling its tiles alone.
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_fwd32(AttnArgs a) {
-  attn_body<false, 32>(a);
+  attn_body<32, false>(a);
 }
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_seg32(AttnArgs a) {
-  attn_body<true, 32>(a);
-}
-
-// Combination of a (head, block)'s segment records (O_s / l_s and lse_s per
-// row): with M the largest lse_s of a row and c_s = e^(lse_s - M), out =
-// sum_s c_s (O_s / l_s) / sum_s c_s and lse = M + ln(sum_s c_s), summed in
-// segment order.  Threads 0..63 turn each row's lse_s into the weights c_s
-// (LDS, [segment][row], up to 64 segments at a time); every thread then
-// accumulates 16-byte pieces q = 256 j + t of the records (row q / 32), so
-// each load instruction of a wave reads 1 KiB of contiguous memory.
-constexpr int kCombThreads = 256;
-constexpr int kCombSegs = 64;  // segments whose weights LDS holds at once
-__global__ __launch_bounds__(kCombThreads) void seg_combine(AttnArgs a) {
-  __shared__ float cw[kCombSegs][kBM];
-  __shared__ float inv[kBM];
-  const int t = threadIdx.x;
-  const int bl = blockIdx.x / a.n_list, hi = blockIdx.x - bl * a.n_list;
-  const int b = a.seg_b0 + a.seg_nb - 1 - bl;  // the call's query block
-  const int h = a.list[hi];
-  const int row0 = (a.qb0 + b) * kBM;           // its first query row in the sequence
-  const int ns = ((row0 + kBM - 1) >> a.seg_shift) + 1;
-  const float* rec0 = a.part + (int64_t)(bl * a.n_list + hi) * a.seg_n * kSegRecFloats;
-  const int64_t orow0 = (int64_t)h * a.qm + (int64_t)b * kBM;  // first row of out and lse
-  float mx = -INFINITY, den = 0.f;
-  if (t < kBM)
-    for (int sg = 0; sg < ns; ++sg) mx = fmaxf(mx, rec0[(int64_t)sg * kSegRecFloats + kSegRowFloats + t]);
-  constexpr int kPer = kSegRowFloats / 4 / kCombThreads;  // 16-byte pieces per thread
-  f32x4 acc[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) acc[j] = f32x4{};
-  for (int s0 = 0; s0 < ns; s0 += kCombSegs) {
-    const int s1 = min(ns, s0 + kCombSegs);
-    if (t < kBM) {
-      for (int sg = s0; sg < s1; ++sg) {
-        const float ls = rec0[(int64_t)sg * kSegRecFloats + kSegRowFloats + t];
-        const float c = ls == -INFINITY ? 0.f : expf(ls - mx);
-        cw[sg - s0][t] = c;
-        den += c;
-      }
-    }
-    __syncthreads();
-    for (int sg = s0; sg < s1; ++sg) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(rec0 + (int64_t)sg * kSegRecFloats);
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int q = kCombThreads * j + t;
-        acc[j] += cw[sg - s0][q >> 5] * src[q];
-      }
-    }
-    __syncthreads();
-  }
-  if (t < kBM) {
-    inv[t] = den > 0.f ? 1.f / den : 0.f;
-    if (a.lse) a.lse[orow0 + t] = den > 0.f ? mx + logf(den) : -INFINITY;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int q = kCombThreads * j + t;
-    const int rr = q >> 5;
-    const f32x4 x = acc[j] * inv[rr];
-    const int64_t o = (orow0 + rr) * kD + 4 * (q & 31);
-    if (a.out_f32) {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = x;
-    } else {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      const bf16x4 y = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<uint16_t*>(a.out) + o) = y;
-    }
-  }
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_attn_paced32(AttnArgs a) {
+  attn_body<32, true>(a);
 }
 
 __global__ __launch_bounds__(256) void v_to_f16(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -854,20 +662,5 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_attn_seg(const AttnArgs& a, int rows, hipStream_t s) {
-  if (rows != kBM && rows != 32) return hipErrorInvalidValue;
-  // Segments that reach the chunk's longest block.
-  const int nseg = (((a.qb0 + a.seg_b0 + a.seg_nb) * kBM - 1) >> a.seg_shift) + 1;
-  if (nseg > a.seg_n) return hipErrorInvalidValue;
-  const int64_t blocks = (int64_t)nseg * a.seg_nb * (kBM / rows) * a.n_list;
-  if (rows == kBM)
-    hipLaunchKernelGGL(sparse_attn_seg, dim3((unsigned)blocks), dim3(128), 0, s, a);
-  else
-    hipLaunchKernelGGL(sparse_attn_seg32, dim3((unsigned)blocks), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seg_combine, dim3((unsigned)(a.seg_nb * a.n_list)), dim3(kCombThreads), 0, s, a);
-  return hipGetLastError();
-}
 
 }  // namespace msa

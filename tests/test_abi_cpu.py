@@ -159,6 +159,25 @@ def test_workspace_sizes_cover_their_parts():
     assert ms.ms_workspace_bytes(prob, hp) >= est + idx + att
 
 
+def test_attention_workspace_holds_the_pacing_counters():
+    """Below 131072 keys the attention workspace is the fp16 V copy; from
+    there on it also holds the counters of the paced launches (8 XCDs x
+    8192-key segments per launch of 1024 workgroups), sized for every head
+    of the problem paced with 64-row and with 32-row blocks."""
+    for n, hq, hkv in ((65536, 32, 8), (131072, 32, 8), (1 << 20, 32, 8), (262144, 6, 2)):
+        prob = ms.problem(n, hq, hkv)
+        att = ms.ms_attn_workspace_bytes(prob)
+        v16 = hkv * n * 128 * 2
+        if n < 131072:
+            assert att == v16
+            continue
+        nseg = (n - 1) // 8192 + 1
+        per = max(1, 1024 // hq)
+        launches = -(-(n // 64) // per) + -(-(n // 32) // per)
+        words = launches * 8 * nseg
+        assert att == v16 + -(-words * 4 // 256) * 256, (n, att)
+
+
 def _raw(status, name, *args):
     """Calls the C ABI directly (ctypes), bypassing the binding's own checks."""
     lib = ms.load()

@@ -153,10 +153,10 @@ def test_chunk_against_the_oracle():
             np.testing.assert_allclose(gl[fin], rl[fin], rtol=0, atol=LSE_ATOL)
 
 
-def test_chunk_of_a_long_sequence_by_key_segments():
-    """n = 262144: heads served by key segments and the chunk loop of the
-    record budget run with a first query block other than 0; the chunk's
-    output and lse equal the tail of the whole call."""
+def test_chunk_of_a_long_sequence_paced():
+    """n = 262144: paced heads (launches of 1024 workgroups from the last
+    block down) with a first query block other than 0; the chunk's output
+    and lse equal the tail of the whole call."""
     n, q_block0 = 262144, 4096 - 700
     heads = [W.vs(100, 1500), W.bs(500), W.ashape(1024, 40000), W.vs(30, 60)] * 2
     w = W.custom("chunk_seg", n, 8, 2, heads, recipe="vs_planted", seed=63)

@@ -114,27 +114,27 @@ def test_config3_mixed_128k():
                  est_heads=[vs_h[0], bs_h[0]])
 
 
-def _record_chunk_blocks(w):
-    """Query blocks per chunk of the key-segment mode at full size: the
-    records of one block (32 heads x every 32768-key segment x 64 rows of 128
-    fp32 plus 64 log-sum-exps) in a 4 GiB budget."""
-    nseg = (w.n - 1) // 32768 + 1
-    return (4 << 30) // (nseg * w.n_q_heads * (64 * 128 + 64) * 4)
+def _paced_launch_edges(nblk, heads):
+    """Blocks on both sides of the launch boundaries of the paced mode: a
+    launch holds 1024 workgroups, 1024 // heads blocks of every paced head,
+    taken from the last block down (the lowest launch may be short)."""
+    cb = 1024 // heads
+    edges = set()
+    for top in (nblk - cb, nblk - 64 * cb, nblk - (nblk // cb) * cb):
+        edges |= {top - 1, top}
+    return sorted(b for b in edges if 0 <= b < nblk)
 
 
 def test_config4_vertical_slash_1m():
     """Scores and end-to-end selections of one Q head per KV head; index and
-    attention of four heads (different KV heads) at the record-chunk edges
-    (chunks of query blocks run from the last block down), at key-segment
-    edges (a block whose rows end a 32768-key segment and the next), the
-    first and last blocks, and random ones."""
+    attention of four heads (different KV heads) at the edges of the paced
+    launches (32 blocks of all 32 heads each, from the last block down), at
+    pacing-segment edges (a block whose rows end an 8192-key segment and the
+    next), the first and last blocks, and random ones."""
     w = W.config(4)
-    cb = _record_chunk_blocks(w)
     nb = w.nb
-    # chunk c holds query blocks c*cb .. c*cb + cb - 1 (the last chunk may be short)
-    chunk_edges = [cb - 1, cb, 64 * cb - 1, 64 * cb, (nb // cb) * cb - 1, (nb // cb) * cb]
-    seg_edges = [511, 512, 8191, 8192, nb - 513, nb - 512]
-    edges = sorted({0, 1, nb - 2, nb - 1, *[b for b in chunk_edges + seg_edges if 0 <= b < nb]})
+    seg_edges = [127, 128, 511, 512, 8191, 8192, nb - 129, nb - 128]
+    edges = sorted({0, 1, nb - 2, nb - 1, *_paced_launch_edges(nb, 32), *[b for b in seg_edges if 0 <= b < nb]})
     _check_layer(4, heads_checked=[0, 9, 18, 27], n_blocks=2, seed=4, est_heads=list(range(0, 32, 4)),
                  edge_blocks=edges)
 
@@ -165,17 +165,16 @@ def test_union_of_many_ranges_per_block():
 
 
 @pytest.mark.parametrize("out_dtype", [ms.OUT_BF16, ms.OUT_F32])
-def test_key_segments_and_chunks(out_dtype):
+def test_paced_heads(out_dtype):
     """From n = 131072 on, heads served one by one whose key sets are long (on
-    average a segment or more per query block) run by key segments: each
-    workgroup takes one query block's keys in one segment of 32768, the
-    workgroups of a segment are dispatched together, chunks of query blocks
-    run while their partial records fit the record budget, and a second kernel
-    combines the records.  n = 262144 with five such heads (Vertical-Slash,
-    Block-Sparse and A-shape of density 0.3-0.4) beside three short ones that
-    stay whole; blocks at segment edges (511/512, 1023/1024), at the chunk
-    edge of the default 4 GiB budget, the first and last blocks and random
-    ones against the oracle, with lse; and the one-shot call bit for bit."""
+    average 32768 keys or more per query block) run paced: launches of 1024
+    workgroups (here 204 blocks of each of the five paced heads), whose
+    workgroups on one XCD keep pace in 8192-key segments.  n = 262144 with
+    five such heads (Vertical-Slash, Block-Sparse and A-shape of density
+    0.3-0.4) beside three short ones that stay whole; blocks at pacing-segment
+    edges (127/128, 511/512), at launch edges, the first and last blocks and
+    random ones against the oracle, with lse; and the one-shot call bit for
+    bit."""
     n = 262144
     heads = [W.vs(100, 1500), W.bs(500), W.ashape(1024, 40000), W.vs(30, 60),
              W.vs(100, 1500), W.bs(3), W.ashape(128, 900), W.vs(500, 2000)]
@@ -183,8 +182,7 @@ def test_key_segments_and_chunks(out_dtype):
     st = run_staged(make(w, out_dtype=out_dtype), debug=False)
     sel = selections(st)
     nb = n // 64
-    chunk = (4 << 30) // ((n // 32768) * 5 * (64 * 128 + 64) * 4)
-    edges = [0, 1, 511, 512, 1023, 1024, chunk - 1, chunk, nb - 2, nb - 1]
+    edges = sorted({0, 1, 127, 128, 511, 512, nb - 2, nb - 1, *_paced_launch_edges(nb, 5)})
     for h, p in enumerate(w.heads):
         blocks = sorted(set(edges[h % 2::2] + sample_blocks(nb, 2, 500 + h)))
         got_idx = read_index_blocks(st.prob, st.hp, st.index, h, blocks)
@@ -278,22 +276,20 @@ def test_longest_sequence():
         print(f"  head {h}: {len(blocks)} blocks ok", flush=True)
 
 
-def test_32_row_blocks_by_key_segments():
+def test_32_row_blocks_paced():
     """Vertical-Slash heads indexed by 32-row query blocks with long key sets
-    run by key segments: two one-wavefront work items fill the two halves of
-    one 64-row partial record, and the combination is the 64-row one.  n =
-    262144, two such heads beside a 64-row one and a short 32-row head that
-    stays whole; 32-row blocks at segment edges (1023/1024, 2047/2048), at the
-    edge of the record-budget chunks, the first, last and random ones."""
+    run paced with one-wavefront workgroups (launches of 1024: 512 32-row
+    blocks of each of the two paced heads).  n = 262144, two such heads
+    beside a 64-row one and a short 32-row head that stays whole; 32-row
+    blocks at pacing-segment edges (255/256, 1023/1024), at launch edges, the
+    first, last and random ones."""
     n = 262144
     heads = [W.vs(100, 3000, block=32), W.vs(100, 1500), W.vs(50, 3000, block=32), W.vs(20, 40, block=32)]
     w = W.custom("seg32", n, 4, 2, heads, recipe="vs_planted", seed=43)
     st = run_staged(make(w), debug=False)
     sel = selections(st)
     nb32 = n // 32
-    seg_heads = 2
-    cb = (4 << 30) // ((n // 32768) * seg_heads * (64 * 128 + 64) * 4)   # 64-row blocks per chunk
-    edges = [0, 1, 1023, 1024, 2047, 2048, 2 * cb - 1, 2 * cb, nb32 - 2, nb32 - 1]
+    edges = sorted({0, 1, 255, 256, 1023, 1024, nb32 - 2, nb32 - 1, *_paced_launch_edges(nb32, 2)})
     q = f64(st.q)
     for h, p in enumerate(heads):
         bm = oracle.query_block_rows(p)
