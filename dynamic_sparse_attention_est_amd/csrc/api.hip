@@ -94,6 +94,7 @@ struct Plan {
   std::vector<int16_t> solo;     // heads served one by one (64-row blocks)
   std::vector<int16_t> solo32;   // heads served one by one with 32-row blocks
   std::vector<int16_t> ablk;     // A-shape heads of MHA layers, four query blocks per workgroup
+  std::vector<int16_t> cblk;     // heads alone with dense key sets, four query blocks per workgroup
   size_t index_bytes = 0;
   // attention workspace: fp16 V copy, then the pacing counters (without
   // params: the most any head set needs)
@@ -367,6 +368,7 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.hpw = hpw_of(P.grp);
   P.gdesc.clear();
   P.solo.clear();
+  P.cblk.clear();
   auto emit_chunks = [&](int kv, const std::vector<int>& heads) {
     for (size_t c = 0; c < heads.size();) {
       size_t m = std::min<size_t>(P.hpw, heads.size() - c);
@@ -418,6 +420,16 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       emit_chunks(kv, std::vector<int>(fixed_heads.begin() + i, fixed_heads.begin() + e));
       i = e;
     }
+  }
+  // Heads served alone whose key sets cover most causal keys (expected
+  // density >= 3/4; not A-shape, whose windows need a per-row mask) take four
+  // query blocks per workgroup over every key below the group's last row, so
+  // each K/V tile feeds 256 rows instead of 64.
+  {
+    std::vector<int16_t> keep;
+    for (int16_t h : P.solo)
+      (P.p[h].pattern != MS_A_SHAPE && expected_density(P.p[h], P.n) >= 0.75 ? P.cblk : keep).push_back(h);
+    P.solo = keep;
   }
   // With four heads per workgroup, chunks of two go to the two-head kernel
   // instead: the four-head chunks first, then those.
@@ -669,6 +681,11 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
     a.n_list = (int)P.ablk.size();
     for (size_t i = 0; i < P.ablk.size(); ++i) a.list[i] = P.ablk[i];
     HIP_TRY(launch_group_ashape(a, s), "attention launch");
+  }
+  if (!P.cblk.empty()) {
+    a.n_list = (int)P.cblk.size();
+    for (size_t i = 0; i < P.cblk.size(); ++i) a.list[i] = P.cblk[i];
+    HIP_TRY(launch_group_csr(a, s), "attention launch");
   }
   for (auto [list, rows] : {std::make_pair(&P.solo, kBM), std::make_pair(&P.solo32, 32)}) {
     if (list->empty()) continue;

@@ -246,22 +246,17 @@ struct HeadRows {
   // Element r of S^T is key slot 8(r/4) + 4g + r%4.  keys: the piece's key
   // list (column pieces) or null (key = kstart + slot).  bits: the piece's
   // keys that belong to this head.  Away from the diagonal and the A-shape
-  // window only the key set matters; slot 8(r/4) + r%4 (+4 in the upper half
-  // of the wave) is kept iff its bit is set, so each element costs one select
-  // on a lane mask built with scalar instructions.
+  // window only the key set matters: with lb = bits >> 4g, element r is kept
+  // iff bit 8(r/4) + r%4 of lb is set (a bit test and a select per element).
   __device__ __forceinline__ void mask(f32x16& s, int kstart, const int* keys, int cnt, uint32_t bits) const {
     const int kmin = keys ? keys[0] : kstart;
     const int kmax = keys ? keys[cnt - 1] : kstart + cnt - 1;
     const bool far = ashape && kmax >= sink && row0 + kBM - 1 - max(kmin, sink) >= window;
     if (kmax <= row0 && !far) {
       if (bits != 0xffffffffu) {
+        const uint32_t lb = bits >> (4 * g);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = 8 * (r >> 2) + (r & 3);
-          const uint64_t lanes = (((bits >> c) & 1u) ? 0x00000000ffffffffull : 0ull) |
-                                 (((bits >> (c + 4)) & 1u) ? 0xffffffff00000000ull : 0ull);
-          s[r] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? s[r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = (lb >> (8 * (r >> 2) + (r & 3))) & 1u ? s[r] : -INFINITY;
       }
       return;
     }
@@ -641,6 +636,160 @@ __device__ __forceinline__ void group_ashape_body(const AttnArgs& a) {
   if (active) hr.store(a, h);
 }
 
+// A window of 64 consecutive entries of an ascending key list in VGPRs (lane
+// k holds entry base + k), read with readlane like RangeWindow.
+struct KeyWindow {
+  const int* list;
+  int base, end;
+  int key;  // this lane's entry
+  __device__ __forceinline__ void load(int first) {
+    typedef __attribute__((address_space(1))) const int32_t g_i32;
+    base = first;
+    const int k = first + (int)(threadIdx.x & 63);
+    key = k < end ? *reinterpret_cast<g_i32*>(reinterpret_cast<uint64_t>(list + k)) : 0x7fffffff;
+    asm volatile("" : "+v"(key));
+  }
+  __device__ __forceinline__ void init(const int* l, int first, int end_) {
+    list = l;
+    end = end_;
+    load(first);
+  }
+  __device__ __forceinline__ int at(int i) {
+    if (i >= end) return 0x7fffffff;
+    if (i - base >= 64) load(i);
+    return __builtin_amdgcn_readlane(key, i - base);
+  }
+};
+
+// Heads served one by one whose key sets cover most of the causal keys
+// (expected density >= 3/4; MInference 1.0 summary, "Summary", third stage):
+// four consecutive query blocks of one head per workgroup of eight waves,
+// like group_ashape_body, over every key below the group's last row in
+// pieces of 32 aligned keys.  Each block's waves compute a piece only if it
+// holds some of the block's keys, with a per-key mask from the block's own
+// ranges and columns (each walked alongside, from windows of 64 records), so
+// each K/V tile in LDS feeds up to 256 query rows.
+template <int S>
+__device__ __forceinline__ void group_csr_body(const AttnArgs& a) {
+  constexpr int kSlots = 4;
+  constexpr int kD16 = 16 / (2 * kSlots);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wv >> 1;
+  // Groups are the sequence's query blocks 4g .. 4g+3 (the last one may be
+  // short); slots below the call's first block stay idle.
+  const int nseq = a.qb0 + a.nb;
+  const int gfirst = a.qb0 / kSlots, glast = (nseq - 1) / kSlots;
+  int hi, gi;
+  map_group(blockIdx.x, a.n_list, glast - gfirst + 1, hi, gi);
+  const int g = gfirst + gi;
+  const int h = a.list[hi];
+  const int kvh = h / a.grp;
+  c_head* hd = as_const<c_head>(a.arena) + h;
+  const int top = min(nseq - 1, kSlots * g + kSlots - 1);
+  const int sb = top - slot;
+  const bool active = sb >= max(kSlots * g, a.qb0);
+  const int b = (active ? sb : top) - a.qb0;  // the call's block (CSR, rows of Q and out)
+  const int64_t n = a.n;
+  const int row0 = (a.qb0 + b) * kBM;
+  const int top_end = top * kBM + kBM;
+  const int npieces = (top_end + kKP - 1) / kKP;
+  auto piece = [&](int p, int& start, int& count) {
+    if (p < npieces) {
+      start = kKP * p;
+      count = min(kKP, top_end - start);
+    } else {
+      start = (int)n;  // past the end: reads zeros, holds no key
+      count = 0;
+    }
+  };
+  // This slot's ranges and columns, walked in key order alongside the pieces.
+  c_i32* rp = as_const<c_i32>(a.arena + hd->rng_ptr_off);
+  c_i32* cp = as_const<c_i32>(a.arena + hd->col_ptr_off);
+  int ri = active ? rp[b] : 0;
+  const int r_end = active ? rp[b + 1] : 0;
+  int ci = active ? cp[b] : 0;
+  const int c_end = active ? cp[b + 1] : 0;
+  RangeWindow rwin;
+  rwin.init(reinterpret_cast<const int2*>(a.arena + hd->rng_off), ri, r_end);
+  KeyWindow cwin;
+  cwin.init(reinterpret_cast<const int*>(a.arena + hd->col_off), ci, c_end);
+  int rlo = 0x7fffffff, rhi = 0x7fffffff;
+  auto range_advance = [&]() {
+    const int2 x = rwin.at(ri);
+    rlo = x.x;
+    rhi = x.y;
+    if (ri < r_end) ++ri;
+  };
+  range_advance();
+  int ckey = cwin.at(ci);
+  // Keys of piece [start, start + count) that are this slot's (pieces come in
+  // increasing order, every piece once).
+  auto slot_bits = [&](int start, int count) -> uint32_t {
+    if (count == 0) return 0u;
+    const int e = start + count;
+    uint32_t bits = 0u;
+    while (rhi <= start) range_advance();
+    while (rlo < e) {
+      const int lo = max(rlo, start) - start, w = min(rhi, e) - start - lo;
+      bits |= (w >= 32 ? 0xffffffffu : ((1u << w) - 1u)) << lo;
+      if (rhi > e) break;
+      range_advance();
+    }
+    while (ckey < e) {
+      bits |= 1u << (ckey - start);
+      ckey = cwin.at(++ci);
+    }
+    return bits;
+  };
+
+  const int nbytes = (int)((uint32_t)n * (uint32_t)kRowBytes);
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + (int64_t)kvh * n * kD), 0, nbytes, 0x00020000);
+  HeadRows hr;
+  hr.init(a.q + ((int64_t)h * a.qm + (int64_t)b * kBM + 32 * (wv & 1)) * kD, lane, row0, 32 * (wv & 1),
+          a.scale_log2);
+  Loader<kD16> ld;
+  ld.init(kr, vr, wv, lane);
+
+  int p_start[S], p_count[S];
+  auto prologue = [&](auto st_c) -> bool {
+    constexpr int ST = decltype(st_c)::value;
+    piece(ST, p_start[ST], p_count[ST]);
+    ld.range(stage<ST>(), p_start[ST]);
+    return true;
+  };
+  run_steps<0, S - 1>(prologue);
+  uint32_t bits = slot_bits(p_start[0], p_count[0]);  // piece i's keys of this slot
+  wait_vm_lgkm0<(S - 3) * kD16>();
+  hr.settle_q();
+  barrier_only();
+  f32x16 s_cur = hr.qk(stage<0>());
+
+  int i = 0;
+  auto step = [&](auto st_c) -> bool {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int NS = (ST + S - 1) % S;
+    constexpr int N1 = (ST + 1) % S;
+    piece(i + S - 1, p_start[NS], p_count[NS]);
+    ld.range(stage<NS>(), p_start[NS]);
+    const uint32_t bits_n = slot_bits(p_start[N1], p_count[N1]);
+    hr.advance(s_cur, p_start[ST], nullptr, p_count[ST], bits, stage<ST>(), bits_n != 0u, stage<N1>());
+    bits = bits_n;
+    wait_vm_lgkm0<(S - 3) * kD16>();
+    barrier_only();
+    ++i;
+    return i < npieces;
+  };
+  while (run_steps<0, S>(step)) {
+  }
+  wait_vm_lgkm0<0>();
+  if (active) hr.store(a, h);
+}
+
 // Sparse attention over the union index of a chunk of HPW heads (MInference
 // 1.0 summary, "Summary", third stage; union_index.hip builds the lists).
 // Phase 1 streams the union ranges through the ring in pieces of up to 32
@@ -817,6 +966,7 @@ __global__ __launch_bounds__(512) void group_dense_h1(AttnArgs a) { group_dense_
 
 // A-shape heads of MHA layers: four query blocks of one head per workgroup.
 __global__ __launch_bounds__(512) void group_ashape_blocks(AttnArgs a) { group_ashape_body<8>(a); }
+__global__ __launch_bounds__(512) void group_csr_blocks(AttnArgs a) { group_csr_body<8>(a); }
 
 // Sparse: heads per workgroup (HPW) and ring stages: 4 heads (one workgroup
 // per CU, 8 stages = 128 KiB of LDS) or 2 (two per CU, 4 stages).
@@ -846,6 +996,13 @@ hipError_t launch_group_ashape(const AttnArgs& a, hipStream_t s) {
   const int groups = (a.qb0 + a.nb - 1) / 4 - a.qb0 / 4 + 1;
   const dim3 grid((unsigned)((int64_t)groups * a.n_list));
   hipLaunchKernelGGL(group_ashape_blocks, grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_csr(const AttnArgs& a, hipStream_t s) {
+  const int groups = (a.qb0 + a.nb - 1) / 4 - a.qb0 / 4 + 1;
+  const dim3 grid((unsigned)((int64_t)groups * a.n_list));
+  hipLaunchKernelGGL(group_csr_blocks, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -632,3 +632,34 @@ def test_ashape_four_block_groups_chunk_equals_whole():
         outs.append((out, lse))
     assert torch.equal(outs[1][0].view(torch.int16), outs[0][0][:, 64 * q_block0:].view(torch.int16))
     assert torch.equal(outs[1][1], outs[0][1][:, 64 * q_block0:])
+
+
+# Heads served alone whose key sets cover most causal keys (expected density
+# >= 3/4, not A-shape): four consecutive query blocks of a head share one walk
+# over every key below the group's last row, each block keeping its own
+# ranges and columns.  GQA layers whose KV heads hold one such head beside
+# sparse ones, MHA layers where every head is one, block counts that leave the
+# last group short, and chunks that start inside a group.
+@pytest.mark.parametrize("n,hq,hkv,q_block0", [(64 * 39, 8, 2, 0), (64 * 22, 4, 4, 0), (64 * 9, 4, 4, 0),
+                                               (64 * 39, 8, 2, 5), (2048, 4, 4, 30)])
+def test_dense_key_sets_four_block_groups(n, hq, hkv, q_block0):
+    pool = [W.vs(20, n // 4), W.bs(3), W.ashape(16, 100), W.bs(2), W.bs(n // 64), W.vs(5, 2), W.dense(),
+            W.vs(n // 8, n // 5)]
+    heads = pool[:hq] if hkv < hq else [W.vs(20, n // 4), W.bs(n // 64), W.dense(), W.vs(n // 8, n // 5)]
+    w = W.custom("dense_blocks", n, hq, hkv, heads, recipe="vs_planted", seed=70 + n + q_block0)
+    if q_block0 == 0:
+        _attention_check(run_staged(make(w)))
+        return
+    q, k, v = W.generate(w, device="cuda")
+    hp = ms.head_params(heads)
+    outs = []
+    for qb0, qq in ((0, q), (q_block0, q[:, 64 * q_block0:].contiguous())):
+        prob = ms.problem(n, hq, hkv, q_block0=qb0)
+        out = torch.empty_like(qq)
+        lse = torch.empty((hq, qq.shape[1]), device="cuda")
+        ms.ms_sparse_attn(prob, hp, qq, k, v, out, ms.empty_workspace(ms.ms_workspace_bytes(prob, hp)), lse)
+        torch.cuda.synchronize()
+        outs.append((out, lse))
+    # a chunk walks the same keys in the same order for each of its blocks
+    assert torch.equal(outs[1][0].view(torch.int16), outs[0][0][:, 64 * q_block0:].view(torch.int16))
+    assert torch.equal(outs[1][1], outs[0][1][:, 64 * q_block0:])
