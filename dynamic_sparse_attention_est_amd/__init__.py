@@ -23,7 +23,7 @@ __all__ = [
     "ms_validate", "ms_selection_sizes", "ms_estimate_workspace_bytes", "ms_index_bytes",
     "ms_index_layout", "ms_attn_workspace_bytes", "ms_workspace_bytes", "ms_estimate_vs",
     "ms_estimate_block", "ms_build_index", "ms_sparse_attn_indexed", "ms_sparse_attn",
-    "ms_dense_attn", "ms_topk_f32", "ms_version", "read_index", "empty_workspace",
+    "ms_dense_attn", "ms_topk_f32", "ms_set_pace_polls", "ms_version", "read_index", "empty_workspace",
     "ms_sparse_attn_noalloc", "ms_noalloc_scratch_bytes", "ms_attention_recall", "index_blocks",
     "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "DENSE", "GRID", "OUT_BF16", "OUT_F32",
 ]
@@ -89,6 +89,7 @@ def load():
         "ms_sparse_attn": (ctypes.c_int, [P, H, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ms_dense_attn": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
         "ms_topk_f32": (ctypes.c_int, [vp, i64, i32, vp, vp]),
+        "ms_set_pace_polls": (ctypes.c_int, [i32]),
         "ms_attention_recall": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "ms_sparse_attn_noalloc": (ctypes.c_int, [P, H, vp, vp, vp, vp, vp, vp]),
         "ms_noalloc_scratch_bytes": (ctypes.c_int, [ctypes.POINTER(sz)]),
@@ -324,6 +325,11 @@ def ms_dense_attn(prob, q, k, v, out, ws, lse=None, stream=None) -> None:
     _on_device(q=q, k=k, v=v, out=out, ws=ws, lse=lse)
     _check(load().ms_dense_attn(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                                 _nbytes(ws), _stream(stream)))
+
+
+def ms_set_pace_polls(polls: int) -> None:
+    """Test hook: counter reads a paced workgroup's wait may take (0: no waiting)."""
+    _check(load().ms_set_pace_polls(int(polls)))
 
 
 def ms_topk_f32(x: torch.Tensor, k: int, idx: torch.Tensor, stream=None) -> None:

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -53,6 +54,9 @@ constexpr double kLongKeys = 32768.0;
 constexpr int kPaceShift = 13;
 constexpr int kPaceLag = 1;
 constexpr int kPaceSlots = 1024;
+// Counter reads one pacing wait may take (about 1 us each) before the
+// workgroup stops pacing for the rest of its walk; ms_set_pace_polls sets it.
+std::atomic<int32_t> g_pace_polls{4096};
 
 // Paced mode: query blocks per launch for `heads` heads, and the pacing
 // counters of all launches of a call over nb 64-row blocks split in blocks
@@ -700,6 +704,7 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
     a.seg_shift = kPaceShift;
     a.seg_n = (int)nseg;
     a.pace = kPaceLag;
+    a.pace_polls = g_pace_polls.load(std::memory_order_relaxed);
     for (auto [list, rows] : {std::make_pair(&P.solo_paced, kBM), std::make_pair(&P.solo32_paced, 32)}) {
       if (list->empty()) continue;
       a.n_list = (int)list->size();
@@ -962,6 +967,13 @@ ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, co
   a.scale_log2 = P.scale_log2;
   a.out_f32 = P.out_f32;
   HIP_TRY(launch_group_dense(a, stream), "attention launch");
+  return MS_OK;
+}
+
+ms_status ms_set_pace_polls(int32_t polls) {
+  g_err.clear();
+  if (polls < 0) return fail(MS_ERR_INVALID_ARG, "polls = %d is negative", polls);
+  g_pace_polls.store(polls, std::memory_order_relaxed);
   return MS_OK;
 }
 

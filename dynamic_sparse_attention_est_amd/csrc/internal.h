@@ -153,6 +153,7 @@ struct AttnArgs {
   int32_t seg_shift, seg_b0, seg_nb, seg_n;
   uint32_t* pace_cnt;
   int32_t pace;
+  int32_t pace_polls;  // counter reads a wait may take before pacing stops for the walk
 };
 // rows: query rows per block of the listed heads' CSR (64 or 32; a 32-row
 // block is one wavefront's work item).

@@ -94,8 +94,9 @@ struct PieceIter {
   // first key past it, the segment count of the launch, this XCD's counters
   // and group size, whether this wave reports arrivals, and whether pacing
   // is still on (a wait that runs out switches it off for the rest of the
-  // walk, so a workgroup never waits on one that is not resident).
-  int seg, seg_end, nseg, shift, pace, members;
+  // walk, so a workgroup never waits on one that is not resident); polls
+  // bounds the counter reads of one wait.
+  int seg, seg_end, nseg, shift, pace, members, polls;
   uint32_t* cnt;
   bool reporter, paced;
   __device__ __forceinline__ void load_window(int first) {
@@ -134,7 +135,7 @@ struct PieceIter {
       if ((threadIdx.x & 63) == 0) v = __hip_atomic_load(cnt + need, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       v = __builtin_amdgcn_readfirstlane(v);
       if (v >= (uint32_t)members) return;
-      if (t >= 4096) {
+      if (t >= polls) {
         paced = false;
         return;
       }
@@ -295,6 +296,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     it.seg_end = 1 << a.seg_shift;
     it.reporter = w == 0;
     it.paced = true;
+    it.polls = a.pace_polls;
   }
   global_int* col = nullptr;
   bool ashape = false;

@@ -246,6 +246,14 @@ ms_status ms_dense_attn(const ms_problem* prob, const void* q, const void* k, co
 ms_status ms_attention_recall(const ms_problem* prob, const float* lse_sparse, const float* lse_dense,
                               float* recall, hipStream_t stream);
 
+/* Test hook of the paced attention mode: the number of counter reads one wait
+ * of a workgroup for the others of its XCD may take (default 4096, about
+ * 1 us each) before that workgroup stops pacing for the rest of its walk.
+ * 0 turns the waiting off for calls enqueued afterwards (process-wide).
+ * Results never depend on it; only the order in which keys are read does.
+ * Negative values are rejected (MS_ERR_INVALID_ARG). */
+ms_status ms_set_pace_polls(int32_t polls);
+
 /* Test hook of the selection kernel: the k largest of x[0..n) (device fp32),
  * ties to the lower index, written ascending to idx[0..min(k, n)) (device).
  * -0.0 ranks equal to +0.0; x must hold no NaN.  1 <= n <= 2^30, 0 <= k. */

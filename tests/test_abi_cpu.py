@@ -178,6 +178,12 @@ def test_attention_workspace_holds_the_pacing_counters():
         assert att == v16 + -(-words * 4 // 256) * 256, (n, att)
 
 
+def test_pace_polls_hook_rejects_negative_counts():
+    lib = ms.load()
+    assert lib.ms_set_pace_polls(-1) == 1  # MS_ERR_INVALID_ARG
+    assert lib.ms_set_pace_polls(4096) == 0
+
+
 def _raw(status, name, *args):
     """Calls the C ABI directly (ctypes), bypassing the binding's own checks."""
     lib = ms.load()

@@ -315,3 +315,30 @@ def test_32_row_blocks_paced():
     ms.ms_sparse_attn(st.prob, st.hp, st.q, st.k, st.v, out2, ws)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), st.out.view(torch.int16))
+
+
+def test_paced_results_do_not_depend_on_the_waits():
+    """The paced mode orders the K/V reads only: with waiting switched off
+    (every workgroup walks at its own pace) the one-shot call's out and lse
+    equal the paced call's bit for bit.  n = 262144, the paced heads of the
+    paced-heads layer beside short ones."""
+    n = 262144
+    heads = [W.vs(100, 1500), W.bs(500), W.ashape(1024, 40000), W.vs(30, 60),
+             W.vs(100, 1500), W.bs(3), W.ashape(128, 900), W.vs(500, 2000)]
+    w = W.custom("segments", n, 8, 2, heads, recipe="vs_planted", seed=42)
+    q, k, v = W.generate(w, device="cuda")
+    prob, hp = ms.problem(n, 8, 2), ms.head_params(heads)
+    ws = ms.empty_workspace(ms.ms_workspace_bytes(prob, hp))
+    res = []
+    try:
+        for polls in (4096, 0):
+            ms.ms_set_pace_polls(polls)
+            out = torch.empty_like(q)
+            lse = torch.empty((8, n), device="cuda")
+            ms.ms_sparse_attn(prob, hp, q, k, v, out, ws, lse)
+            torch.cuda.synchronize()
+            res.append((out, lse))
+    finally:
+        ms.ms_set_pace_polls(4096)
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1], res[1][1])
