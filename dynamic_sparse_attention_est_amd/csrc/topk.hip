@@ -194,9 +194,14 @@ __device__ __forceinline__ void load_chunk(const float* x, int64_t n, int c, int
     for (int e = 0; e < 4; ++e) ck.key[r][e] = order_key(v[r][e]);
 }
 
+// The last pass (shift 0) also counts the chunk's keys whose upper 24 bits
+// exceed the prefix (above[j][c]) and stores suffix sums (entry d: keys with
+// the prefix and a low byte >= d), so that once the last digit is known a
+// chunk's counts above and at the threshold are two reads, not another pass.
 __global__ __launch_bounds__(kMT) void topk_hist(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
-                                                 int* hist, int nchunks, int shift) {
+                                                 int* hist, int* above, int nchunks, int shift) {
   __shared__ int h[256];
+  __shared__ int red[kMT / 64];
   const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
   h[t] = 0;
   const float* x = src + jobs.src_off[j];
@@ -204,24 +209,61 @@ __global__ __launch_bounds__(kMT) void topk_hist(const float* src, int64_t n, To
   ChunkKeys ck;
   load_chunk(x, n, c, t, ck);
   __syncthreads();
+  int ab = 0;
 #pragma unroll
   for (int r = 0; r < kRounds; ++r)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t key = ck.key[r][e];
       if (ck.valid[r] && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
+      if (shift == 0) ab += ck.valid[r] & ((key >> 8) > (prefix >> 8));
     }
   __syncthreads();
-  hist[((int64_t)j * nchunks + c) * 256 + t] = h[t];
+  int v = h[t];
+  if (shift == 0) {
+    // suffix sums over the 256 bins (thread t ends with bins t .. 255)
+#pragma unroll
+    for (int d = 1; d < 256; d <<= 1) {
+      const int u = t + d < 256 ? h[t + d] : 0;
+      __syncthreads();
+      v += u;
+      h[t] = v;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) ab += __shfl_xor(ab, d);
+    if ((t & 63) == 0) red[t >> 6] = ab;
+    __syncthreads();
+    if (t == 0) {
+      int sum = 0;
+      for (int wv = 0; wv < kMT / 64; ++wv) sum += red[wv];
+      above[(int64_t)j * nchunks + c] = sum;
+    }
+  }
+  hist[((int64_t)j * nchunks + c) * 256 + t] = v;
 }
 
 __global__ __launch_bounds__(256) void topk_digit(TopkState* st, const int* hist, int nchunks, int shift) {
   __shared__ int tot[256];
   const int j = blockIdx.x, t = threadIdx.x;
-  int s = 0;
-  for (int c = 0; c < nchunks; ++c) s += hist[((int64_t)j * nchunks + c) * 256 + t];
-  tot[t] = s;
+  // four independent sums, loads issued sixteen chunks at a time
+  int s4[4] = {0, 0, 0, 0};
+  const int* hj = hist + (int64_t)j * nchunks * 256 + t;
+  int c = 0;
+  for (; c + 16 <= nchunks; c += 16) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s4[u & 3] += hj[(int64_t)(c + u) * 256];
+  }
+  for (; c < nchunks; ++c) s4[0] += hj[(int64_t)c * 256];
+  tot[t] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   __syncthreads();
+  if (shift == 0) {
+    // the last pass stores suffix sums: back to per-bin counts
+    const int next = t < 255 ? tot[t + 1] : 0;
+    __syncthreads();
+    tot[t] -= next;
+    __syncthreads();
+  }
   if (t == 0) {
     const int rem = st[j].rem;
     int above = 0, d = 255;
@@ -235,57 +277,43 @@ __global__ __launch_bounds__(256) void topk_digit(TopkState* st, const int* hist
   }
 }
 
-// Per chunk: how many keys are above the threshold and how many equal it.
-__global__ __launch_bounds__(kMT) void topk_count(const float* src, int64_t n, TopkJobs jobs, const TopkState* st,
-                                                  int* counts, int nchunks) {
-  __shared__ int red[2][kMT / 64];
-  const int c = blockIdx.x, j = blockIdx.y, t = threadIdx.x;
-  const float* x = src + jobs.src_off[j];
-  const uint32_t T = st[j].prefix;
-  ChunkKeys ck;
-  load_chunk(x, n, c, t, ck);
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int r = 0; r < kRounds; ++r)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      gt += ck.valid[r] & (ck.key[r][e] > T);
-      eq += ck.valid[r] & (ck.key[r][e] == T);
-    }
-#pragma unroll
-  for (int d = 32; d > 0; d >>= 1) {
-    gt += __shfl_xor(gt, d);
-    eq += __shfl_xor(eq, d);
-  }
-  if ((t & 63) == 0) {
-    red[0][t >> 6] = gt;
-    red[1][t >> 6] = eq;
-  }
-  __syncthreads();
-  if (t == 0) {
-    int g = 0, e = 0;
-    for (int w = 0; w < kMT / 64; ++w) {
-      g += red[0][w];
-      e += red[1][w];
-    }
-    counts[((int64_t)j * nchunks + c) * 2] = g;
-    counts[((int64_t)j * nchunks + c) * 2 + 1] = e;
-  }
-}
-
 // Per chunk: output offset of its first selected key, and the number of
 // threshold-equal keys in earlier chunks.
-__global__ void topk_bases(const TopkState* st, const int* counts, int* bases, int nchunks) {
-  const int j = blockIdx.x;
-  if (threadIdx.x != 0) return;
+// A chunk's keys above the threshold T and equal to it come from the last
+// pass: above[c] plus the suffix sum past T's low byte, and the difference of
+// the suffix sums at and past it.
+__global__ __launch_bounds__(64) void topk_bases(const TopkState* st, const int* hist, const int* above, int* bases,
+                                                 int nchunks) {
+  const int j = blockIdx.x, lane = threadIdx.x;
   const int need = st[j].rem;
-  int gtp = 0, eqp = 0;
-  for (int c = 0; c < nchunks; ++c) {
+  const int d4 = (int)(st[j].prefix & 255u);
+  int gtp = 0, eqp = 0;  // counts of the chunks before this window
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    // one chunk per lane; exclusive prefix sums over the window by shuffles
+    const int c = c0 + lane;
     const int64_t o = ((int64_t)j * nchunks + c) * 2;
-    bases[o] = gtp + min(need, eqp);
-    bases[o + 1] = eqp;
-    gtp += counts[o];
-    eqp += counts[o + 1];
+    int g = 0, e = 0;
+    if (c < nchunks) {
+      const int* hc = hist + ((int64_t)j * nchunks + c) * 256;
+      const int past = d4 < 255 ? hc[d4 + 1] : 0;
+      g = above[(int64_t)j * nchunks + c] + past;
+      e = hc[d4] - past;
+    }
+    int gs = g, es = e;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int gu = __shfl_up(gs, d), eu = __shfl_up(es, d);
+      if (lane >= d) {
+        gs += gu;
+        es += eu;
+      }
+    }
+    if (c < nchunks) {
+      bases[o] = gtp + gs - g + min(need, eqp + es - e);
+      bases[o + 1] = eqp + es - e;
+    }
+    gtp += __shfl(gs, 63);
+    eqp += __shfl(es, 63);
   }
 }
 
@@ -342,7 +370,7 @@ hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, i
 
 size_t topk_scratch_bytes(int64_t n, int problems) {
   const int64_t nchunks = (n + kChunk - 1) / kChunk;
-  return 256 + (size_t)problems * sizeof(TopkState) + (size_t)problems * nchunks * (256 + 4) * sizeof(int);
+  return 256 + (size_t)problems * sizeof(TopkState) + (size_t)problems * nchunks * (256 + 3) * sizeof(int);
 }
 
 hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, int32_t* dst2,
@@ -367,16 +395,15 @@ hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs
   char* w = static_cast<char*>(scratch);
   TopkState* st = reinterpret_cast<TopkState*>(w);
   int* hist = reinterpret_cast<int*>(w + 256 + (size_t)jobs.count * sizeof(TopkState));
-  int* counts = hist + (size_t)jobs.count * nchunks * 256;
-  int* bases = counts + (size_t)jobs.count * nchunks * 2;
+  int* above = hist + (size_t)jobs.count * nchunks * 256;
+  int* bases = above + (size_t)jobs.count * nchunks;
   const dim3 grid((unsigned)nchunks, (unsigned)jobs.count);
   hipLaunchKernelGGL(topk_init, dim3(1), dim3(TopkJobs::kMaxJobs), 0, s, jobs, st);
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hipLaunchKernelGGL(topk_hist, grid, dim3(kMT), 0, s, src, n, jobs, st, hist, nchunks, shift);
+    hipLaunchKernelGGL(topk_hist, grid, dim3(kMT), 0, s, src, n, jobs, st, hist, above, nchunks, shift);
     hipLaunchKernelGGL(topk_digit, dim3((unsigned)jobs.count), dim3(256), 0, s, st, hist, nchunks, shift);
   }
-  hipLaunchKernelGGL(topk_count, grid, dim3(kMT), 0, s, src, n, jobs, st, counts, nchunks);
-  hipLaunchKernelGGL(topk_bases, dim3((unsigned)jobs.count), dim3(64), 0, s, st, counts, bases, nchunks);
+  hipLaunchKernelGGL(topk_bases, dim3((unsigned)jobs.count), dim3(64), 0, s, st, hist, above, bases, nchunks);
   hipLaunchKernelGGL(topk_write, grid, dim3(kMT), 0, s, src, n, jobs, st, bases, dst, dst2, split, nchunks);
   return hipGetLastError();
 }
