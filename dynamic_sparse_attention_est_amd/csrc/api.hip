@@ -99,6 +99,8 @@ struct Plan {
   std::vector<int16_t> solo32;   // heads served one by one with 32-row blocks
   std::vector<int16_t> ablk;     // A-shape heads of MHA layers, four query blocks per workgroup
   std::vector<int16_t> cblk;     // heads alone with dense key sets, four query blocks per workgroup
+  std::vector<int16_t> hdense4;  // chunks of heads with dense key sets (4 entries each, -1 padded), no union
+  std::vector<int16_t> hdense2;  // the same, chunks of two
   size_t index_bytes = 0;
   // attention workspace: fp16 V copy, then the pacing counters (without
   // params: the most any head set needs)
@@ -373,6 +375,8 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
   P.gdesc.clear();
   P.solo.clear();
   P.cblk.clear();
+  P.hdense4.clear();
+  P.hdense2.clear();
   auto emit_chunks = [&](int kv, const std::vector<int>& heads) {
     for (size_t c = 0; c < heads.size();) {
       size_t m = std::min<size_t>(P.hpw, heads.size() - c);
@@ -382,6 +386,18 @@ ms_status make_plan(const ms_problem* prob, const ms_head_params* params, Plan& 
       if (m == 3) m = 2;
       if (m < 2) {
         P.solo.push_back((int16_t)heads[c++]);
+        continue;
+      }
+      // Chunks whose heads all keep most causal keys walk every key with
+      // per-head masks (group_csr_heads) instead of a union index.
+      bool all_dense = true;
+      for (size_t j = 0; j < m; ++j)
+        all_dense = all_dense && P.p[heads[c + j]].pattern != MS_A_SHAPE &&
+                    expected_density(P.p[heads[c + j]], P.n) >= 0.75;
+      if (all_dense) {
+        std::vector<int16_t>& l = m > 2 ? P.hdense4 : P.hdense2;
+        for (size_t j = 0; j < (m > 2 ? 4u : 2u); ++j) l.push_back(j < m ? (int16_t)heads[c + j] : (int16_t)-1);
+        c += m;
         continue;
       }
       GroupDesc g{};
@@ -690,6 +706,12 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
     a.n_list = (int)P.cblk.size();
     for (size_t i = 0; i < P.cblk.size(); ++i) a.list[i] = P.cblk[i];
     HIP_TRY(launch_group_csr(a, s), "attention launch");
+  }
+  for (auto [list, slots] : {std::make_pair(&P.hdense4, 4), std::make_pair(&P.hdense2, 2)}) {
+    if (list->empty()) continue;
+    a.n_list = (int)list->size() / slots;
+    for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
+    HIP_TRY(launch_group_csr_heads(a, slots, s), "attention launch");
   }
   for (auto [list, rows] : {std::make_pair(&P.solo, kBM), std::make_pair(&P.solo32, 32)}) {
     if (list->empty()) continue;

@@ -661,39 +661,53 @@ struct KeyWindow {
   }
 };
 
-// Heads served one by one whose key sets cover most of the causal keys
-// (expected density >= 3/4; MInference 1.0 summary, "Summary", third stage):
-// four consecutive query blocks of one head per workgroup of eight waves,
-// like group_ashape_body, over every key below the group's last row in
-// pieces of 32 aligned keys.  Each block's waves compute a piece only if it
-// holds some of the block's keys, with a per-key mask from the block's own
-// ranges and columns (each walked alongside, from windows of 64 records), so
-// each K/V tile in LDS feeds up to 256 query rows.
-template <int S>
+// Heads whose key sets cover most of the causal keys (expected density >=
+// 3/4; MInference 1.0 summary, "Summary", third stage), kSlots (head, query
+// block) slots per workgroup of 2 kSlots waves, walking every key below the
+// slots' last row in pieces of 32 aligned keys (no union index).  Each
+// slot's waves compute a piece only if it holds some of the slot's keys,
+// with a per-key mask from the slot's own ranges and columns (each walked
+// alongside, from windows of 64 records), so each K/V tile in LDS feeds up to
+// 64 kSlots query rows.  kHeads: the slots are the heads of a chunk of one
+// KV head (a.list[kSlots u + j], -1 for none) at one query block; otherwise
+// four consecutive query blocks of one head served alone (a.list[u]), like
+// group_ashape_body.
+template <int S, int kSlots, bool kHeads>
 __device__ __forceinline__ void group_csr_body(const AttnArgs& a) {
-  constexpr int kSlots = 4;
   constexpr int kD16 = 16 / (2 * kSlots);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = wv >> 1;
-  // Groups are the sequence's query blocks 4g .. 4g+3 (the last one may be
-  // short); slots below the call's first block stay idle.
-  const int nseq = a.qb0 + a.nb;
-  const int gfirst = a.qb0 / kSlots, glast = (nseq - 1) / kSlots;
-  int hi, gi;
-  map_group(blockIdx.x, a.n_list, glast - gfirst + 1, hi, gi);
-  const int g = gfirst + gi;
-  const int h = a.list[hi];
+  int h, b, top_end;
+  bool active;
+  if constexpr (kHeads) {
+    int u, bb;
+    map_group(blockIdx.x, a.n_list, a.nb, u, bb);
+    const int hs = a.list[kSlots * u + slot];
+    active = hs >= 0;
+    h = active ? hs : a.list[kSlots * u];
+    b = bb;
+    top_end = (a.qb0 + b) * kBM + kBM;
+  } else {
+    // Groups are the sequence's query blocks 4g .. 4g+3 (the last one may be
+    // short); slots below the call's first block stay idle.
+    const int nseq = a.qb0 + a.nb;
+    const int gfirst = a.qb0 / kSlots, glast = (nseq - 1) / kSlots;
+    int hi, gi;
+    map_group(blockIdx.x, a.n_list, glast - gfirst + 1, hi, gi);
+    const int g = gfirst + gi;
+    h = a.list[hi];
+    const int top = min(nseq - 1, kSlots * g + kSlots - 1);
+    const int sb = top - slot;
+    active = sb >= max(kSlots * g, a.qb0);
+    b = (active ? sb : top) - a.qb0;  // the call's block (CSR, rows of Q and out)
+    top_end = top * kBM + kBM;
+  }
   const int kvh = h / a.grp;
   c_head* hd = as_const<c_head>(a.arena) + h;
-  const int top = min(nseq - 1, kSlots * g + kSlots - 1);
-  const int sb = top - slot;
-  const bool active = sb >= max(kSlots * g, a.qb0);
-  const int b = (active ? sb : top) - a.qb0;  // the call's block (CSR, rows of Q and out)
   const int64_t n = a.n;
   const int row0 = (a.qb0 + b) * kBM;
-  const int top_end = top * kBM + kBM;
   const int npieces = (top_end + kKP - 1) / kKP;
   auto piece = [&](int p, int& start, int& count) {
     if (p < npieces) {
@@ -966,7 +980,9 @@ __global__ __launch_bounds__(512) void group_dense_h1(AttnArgs a) { group_dense_
 
 // A-shape heads of MHA layers: four query blocks of one head per workgroup.
 __global__ __launch_bounds__(512) void group_ashape_blocks(AttnArgs a) { group_ashape_body<8>(a); }
-__global__ __launch_bounds__(512) void group_csr_blocks(AttnArgs a) { group_csr_body<8>(a); }
+__global__ __launch_bounds__(512) void group_csr_blocks(AttnArgs a) { group_csr_body<8, 4, false>(a); }
+__global__ __launch_bounds__(512) void group_csr_heads4(AttnArgs a) { group_csr_body<8, 4, true>(a); }
+__global__ __launch_bounds__(256) void group_csr_heads2(AttnArgs a) { group_csr_body<4, 2, true>(a); }
 
 // Sparse: heads per workgroup (HPW) and ring stages: 4 heads (one workgroup
 // per CU, 8 stages = 128 KiB of LDS) or 2 (two per CU, 4 stages).
@@ -1003,6 +1019,17 @@ hipError_t launch_group_csr(const AttnArgs& a, hipStream_t s) {
   const int groups = (a.qb0 + a.nb - 1) / 4 - a.qb0 / 4 + 1;
   const dim3 grid((unsigned)((int64_t)groups * a.n_list));
   hipLaunchKernelGGL(group_csr_blocks, grid, dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_csr_heads(const AttnArgs& a, int slots, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.nb * a.n_list));
+  if (slots == 4)
+    hipLaunchKernelGGL(group_csr_heads4, grid, dim3(512), 0, s, a);
+  else if (slots == 2)
+    hipLaunchKernelGGL(group_csr_heads2, grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -634,18 +634,28 @@ def test_ashape_four_block_groups_chunk_equals_whole():
     assert torch.equal(outs[1][1], outs[0][1][:, 64 * q_block0:])
 
 
-# Heads served alone whose key sets cover most causal keys (expected density
-# >= 3/4, not A-shape): four consecutive query blocks of a head share one walk
-# over every key below the group's last row, each block keeping its own
-# ranges and columns.  GQA layers whose KV heads hold one such head beside
-# sparse ones, MHA layers where every head is one, block counts that leave the
-# last group short, and chunks that start inside a group.
+# Heads whose key sets cover most causal keys (expected density >= 3/4, not
+# A-shape) walk every key below the workgroup's last row, each (head, block)
+# slot keeping its own ranges and columns: heads served alone four
+# consecutive query blocks per workgroup, chunks of two or four heads of one
+# KV head one block per workgroup.  GQA layers whose KV heads hold one such
+# head beside sparse ones or two, three or eight of them, MHA layers where
+# every head is one, block counts that leave the last group short, and
+# chunks that start inside a group.
 @pytest.mark.parametrize("n,hq,hkv,q_block0", [(64 * 39, 8, 2, 0), (64 * 22, 4, 4, 0), (64 * 9, 4, 4, 0),
-                                               (64 * 39, 8, 2, 5), (2048, 4, 4, 30)])
+                                               (64 * 39, 8, 2, 5), (2048, 4, 4, 30), (64 * 23, 8, 1, 0),
+                                               (64 * 23, 8, 1, 3)])
 def test_dense_key_sets_four_block_groups(n, hq, hkv, q_block0):
+    # hkv = 1: eight heads of one KV head, all dense, served as two chunks of
+    # four heads per workgroup over every key (no union index)
     pool = [W.vs(20, n // 4), W.bs(3), W.ashape(16, 100), W.bs(2), W.bs(n // 64), W.vs(5, 2), W.dense(),
             W.vs(n // 8, n // 5)]
-    heads = pool[:hq] if hkv < hq else [W.vs(20, n // 4), W.bs(n // 64), W.dense(), W.vs(n // 8, n // 5)]
+    if hkv == 1:
+        heads = [W.vs(20, n // 4), W.dense(), W.bs(n // 64), W.vs(n // 8, n // 5)] * 2
+    elif hkv < hq:
+        heads = pool[:hq]
+    else:
+        heads = [W.vs(20, n // 4), W.bs(n // 64), W.dense(), W.vs(n // 8, n // 5)]
     w = W.custom("dense_blocks", n, hq, hkv, heads, recipe="vs_planted", seed=70 + n + q_block0)
     if q_block0 == 0:
         _attention_check(run_staged(make(w)))
