@@ -5,11 +5,12 @@
 //
 // Work item: one 64-row query block of one Q head = one workgroup of two
 // wavefronts, each owning 32 rows (a head indexed by 32-row query blocks: one
-// 32-row block = one workgroup of one wavefront, which loads its tiles alone).  The block's keys are its ranges, cut into
-// pieces of up to 32 consecutive keys, then its column list in pieces of up to
-// 32 gathered keys.  Both waves share one LDS copy of a piece's K and V rows,
-// written by buffer loads that go straight to LDS (no staging registers).
-// Software pipeline, per iteration i:
+// 32-row block = one workgroup of one wavefront, which loads its tiles
+// alone).  The block's keys are its ranges, cut into pieces of up to 32
+// consecutive keys, then its column list in pieces of up to 32 gathered keys.
+// Both waves share one LDS copy of a piece's K and V rows, written by buffer
+// loads that go straight to LDS (no staging registers).  Software pipeline,
+// per iteration i (four pieces in flight, in slots fixed at compile time):
 //   - loads issued: K rows of piece i+2, V rows of piece i+1;
 //   - S^T of piece i+1 (32 keys x 32 rows) = K . Q^T   v_mfma_f32_32x32x16_bf16
 //     interleaved with the exponentials of piece i, whose S^T the previous
