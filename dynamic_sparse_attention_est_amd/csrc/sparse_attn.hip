@@ -68,8 +68,17 @@ __device__ __forceinline__ float sum_halves(float x) { return x + __shfl_xor(x, 
 struct Piece {
   int start;   // first key (range piece) or first column slot (column piece)
   int count;   // 1..32 (0: past the end of the walk)
-  int is_col;
+  int is_col;  // keys listed per tile row (a column piece or a two-range piece)
   int mask;    // masking the piece needs (set by the kernel when the piece is taken)
+};
+
+// A range piece whose range ends before 32 keys takes the next range's first
+// keys as well: rows 0 .. split - 1 hold keys start .., rows split .. count -
+// 1 hold keys start2 ..  (split = 0: one range, or a column piece).  Without
+// this, every range's last piece is on average half empty (ranges of a 1M
+// Vertical-Slash layer average about 250 keys, so 6% of the matrix work).
+struct Split {
+  int start2, split;
 };
 
 // Start key of a piece past the end: its tile offsets (start * 256 + ...)
@@ -143,7 +152,11 @@ struct PieceIter {
       __builtin_amdgcn_s_sleep(8);
     }
   }
-  __device__ __forceinline__ bool next(Piece& p) {
+  // join: a range piece that ends its range short of 32 keys may continue
+  // with the next range (paced: only within the same key segment).
+  __device__ __forceinline__ bool next(Piece& p, Split& sp, bool join) {
+    sp.split = 0;
+    sp.start2 = 0;
     if (kPace && c < c_end) {  // columns first: every block of a head reads them
       p.start = c;
       p.count = min(kKP, c_end - c);
@@ -163,6 +176,21 @@ struct PieceIter {
       p.count = min(kKP, hi - lo);
       p.is_col = 0;
       lo += p.count;
+      if (join && p.count < kKP && r < r_end) {
+        if (r - wbase >= 64) load_window(r);
+        const int nlo = __builtin_amdgcn_readlane(wlo, r - wbase);
+        const int nhi = __builtin_amdgcn_readlane(whi, r - wbase);
+        if (!kPace || nlo < seg_end) {
+          const int take = min(kKP - p.count, nhi - nlo);
+          sp.split = p.count;
+          sp.start2 = nlo;
+          p.count += take;
+          p.is_col = 1;
+          lo = nlo + take;
+          hi = nhi;
+          ++r;
+        }
+      }
       return true;
     }
     if (kPace) {
@@ -400,22 +428,35 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   using C1 = std::integral_constant<int, 1>;
   using C2 = std::integral_constant<int, 2>;
   using C3 = std::integral_constant<int, 3>;
+  // Two-range pieces only where no A-shape window test needs the piece's
+  // first key.
+  const bool join = !ashape;
   auto fetch = [&](Piece& p, ColKeys<kL>& c) __attribute__((always_inline)) {
     Piece q;
-    if (!it.next(q)) {
+    Split sp;
+    if (!it.next(q, sp, join)) {
       q.start = kPastEnd;
       q.count = 0;
       q.is_col = 0;
+      sp.split = 0;
     }
-    const int kmax = q.start + q.count - 1;
+    const int kmax = sp.split ? sp.start2 + q.count - sp.split - 1 : q.start + q.count - 1;
     const bool far = ashape && kmax >= sink && row0 + kRows - 1 - max(q.start, sink) >= window;
     // (every field is written on every path, so the compiler keeps the
     // slots in registers)
-    q.mask = q.count == 0 ? 0 : q.is_col || kmax > row0 || far ? 2 : q.count < kKP ? 1 : 0;
+    q.mask = q.count == 0 ? 0 : (q.is_col && !sp.split) || kmax > row0 || far ? 2 : q.count < kKP ? 1 : 0;
     p = q;
     if (q.is_col) {
+      if (sp.split) {
 #pragma unroll
-      for (int j = 0; j < kL; ++j) c.k[j] = col_key(q, col, 4 * kL * w + 4 * j + rq);
+        for (int j = 0; j < kL; ++j) {
+          const int rw = 4 * kL * w + 4 * j + rq;
+          c.k[j] = rw < sp.split ? q.start + rw : sp.start2 + rw - sp.split;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kL; ++j) c.k[j] = col_key(q, col, 4 * kL * w + 4 * j + rq);
+      }
     }
   };
   // Mask keys of a column piece: lanes with lane%16 == 0 hold rows 4 kL w + 4j.
