@@ -705,13 +705,13 @@ ms_status run_attention(const Plan& P, const void* q, const void* k, const void*
   if (!P.cblk.empty()) {
     a.n_list = (int)P.cblk.size();
     for (size_t i = 0; i < P.cblk.size(); ++i) a.list[i] = P.cblk[i];
-    HIP_TRY(launch_group_csr(a, s), "attention launch");
+    HIP_TRY(launch_group_csr(a, 1, s), "attention launch");
   }
   for (auto [list, slots] : {std::make_pair(&P.hdense4, 4), std::make_pair(&P.hdense2, 2)}) {
     if (list->empty()) continue;
     a.n_list = (int)list->size() / slots;
     for (size_t i = 0; i < list->size(); ++i) a.list[i] = (*list)[i];
-    HIP_TRY(launch_group_csr_heads(a, slots, s), "attention launch");
+    HIP_TRY(launch_group_csr(a, slots, s), "attention launch");
   }
   for (auto [list, rows] : {std::make_pair(&P.solo, kBM), std::make_pair(&P.solo32, 32)}) {
     if (list->empty()) continue;

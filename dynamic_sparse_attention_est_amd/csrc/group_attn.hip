@@ -668,42 +668,35 @@ struct KeyWindow {
 // slot's waves compute a piece only if it holds some of the slot's keys,
 // with a per-key mask from the slot's own ranges and columns (each walked
 // alongside, from windows of 64 records), so each K/V tile in LDS feeds up to
-// 64 kSlots query rows.  kHeads: the slots are the heads of a chunk of one
-// KV head (a.list[kSlots u + j], -1 for none) at one query block; otherwise
-// four consecutive query blocks of one head served alone (a.list[u]), like
-// group_ashape_body.
-template <int S, int kSlots, bool kHeads>
+// 64 kSlots query rows.  The slots are HPW heads of one KV head (a.list[HPW u
+// + j], -1 for none; HPW = 1: one head served alone) times kSlots / HPW
+// consecutive query blocks, in groups aligned to the sequence's blocks (the
+// last one may be short), like group_ashape_body.  A slot's pieces are those
+// below its own block's end, in key order, whatever its group: a chunk of a
+// sequence computes what the whole sequence computes.
+template <int S, int kSlots, int HPW>
 __device__ __forceinline__ void group_csr_body(const AttnArgs& a) {
   constexpr int kD16 = 16 / (2 * kSlots);
+  constexpr int kBQ = kSlots / HPW;  // consecutive query blocks per workgroup
+  static_assert(kSlots % HPW == 0, "slot count");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int slot = wv >> 1;
-  int h, b, top_end;
-  bool active;
-  if constexpr (kHeads) {
-    int u, bb;
-    map_group(blockIdx.x, a.n_list, a.nb, u, bb);
-    const int hs = a.list[kSlots * u + slot];
-    active = hs >= 0;
-    h = active ? hs : a.list[kSlots * u];
-    b = bb;
-    top_end = (a.qb0 + b) * kBM + kBM;
-  } else {
-    // Groups are the sequence's query blocks 4g .. 4g+3 (the last one may be
-    // short); slots below the call's first block stay idle.
-    const int nseq = a.qb0 + a.nb;
-    const int gfirst = a.qb0 / kSlots, glast = (nseq - 1) / kSlots;
-    int hi, gi;
-    map_group(blockIdx.x, a.n_list, glast - gfirst + 1, hi, gi);
-    const int g = gfirst + gi;
-    h = a.list[hi];
-    const int top = min(nseq - 1, kSlots * g + kSlots - 1);
-    const int sb = top - slot;
-    active = sb >= max(kSlots * g, a.qb0);
-    b = (active ? sb : top) - a.qb0;  // the call's block (CSR, rows of Q and out)
-    top_end = top * kBM + kBM;
-  }
+  // Slots below the call's first block, or of a missing head, stay idle.
+  const int nseq = a.qb0 + a.nb;
+  const int gfirst = a.qb0 / kBQ, glast = (nseq - 1) / kBQ;
+  int u, gi;
+  map_group(blockIdx.x, a.n_list, glast - gfirst + 1, u, gi);
+  const int g = gfirst + gi;
+  const int top = min(nseq - 1, kBQ * g + kBQ - 1);
+  const int sb = top - slot / HPW;
+  const bool in_call = sb >= max(kBQ * g, a.qb0);
+  const int hs = a.list[HPW * u + slot % HPW];
+  const bool active = hs >= 0 && in_call;
+  const int h = hs >= 0 ? hs : a.list[HPW * u];
+  const int b = (in_call ? sb : top) - a.qb0;  // the call's block (CSR, rows of Q and out)
+  const int top_end = top * kBM + kBM;
   const int kvh = h / a.grp;
   c_head* hd = as_const<c_head>(a.arena) + h;
   const int64_t n = a.n;
@@ -745,6 +738,9 @@ __device__ __forceinline__ void group_csr_body(const AttnArgs& a) {
     const int e = start + count;
     uint32_t bits = 0u;
     while (rhi <= start) range_advance();
+    // the usual case for these heads: one range covers the piece (columns
+    // lie in no range, so none is in it)
+    if (rlo <= start && rhi >= e) return count >= 32 ? 0xffffffffu : (1u << count) - 1u;
     while (rlo < e) {
       const int lo = max(rlo, start) - start, w = min(rhi, e) - start - lo;
       bits |= (w >= 32 ? 0xffffffffu : ((1u << w) - 1u)) << lo;
@@ -980,9 +976,9 @@ __global__ __launch_bounds__(512) void group_dense_h1(AttnArgs a) { group_dense_
 
 // A-shape heads of MHA layers: four query blocks of one head per workgroup.
 __global__ __launch_bounds__(512) void group_ashape_blocks(AttnArgs a) { group_ashape_body<8>(a); }
-__global__ __launch_bounds__(512) void group_csr_blocks(AttnArgs a) { group_csr_body<8, 4, false>(a); }
-__global__ __launch_bounds__(512) void group_csr_heads4(AttnArgs a) { group_csr_body<8, 4, true>(a); }
-__global__ __launch_bounds__(256) void group_csr_heads2(AttnArgs a) { group_csr_body<4, 2, true>(a); }
+__global__ __launch_bounds__(512) void group_csr_blocks(AttnArgs a) { group_csr_body<8, 4, 1>(a); }
+__global__ __launch_bounds__(512) void group_csr_heads2(AttnArgs a) { group_csr_body<8, 4, 2>(a); }
+__global__ __launch_bounds__(512) void group_csr_heads4(AttnArgs a) { group_csr_body<8, 4, 4>(a); }
 
 // Sparse: heads per workgroup (HPW) and ring stages: 4 heads (one workgroup
 // per CU, 8 stages = 128 KiB of LDS) or 2 (two per CU, 4 stages).
@@ -1015,21 +1011,17 @@ hipError_t launch_group_ashape(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_group_csr(const AttnArgs& a, hipStream_t s) {
-  const int groups = (a.qb0 + a.nb - 1) / 4 - a.qb0 / 4 + 1;
+hipError_t launch_group_csr(const AttnArgs& a, int hpw, hipStream_t s) {
+  if (hpw != 1 && hpw != 2 && hpw != 4) return hipErrorInvalidValue;
+  const int bq = 4 / hpw;  // consecutive query blocks per workgroup
+  const int groups = (a.qb0 + a.nb - 1) / bq - a.qb0 / bq + 1;
   const dim3 grid((unsigned)((int64_t)groups * a.n_list));
-  hipLaunchKernelGGL(group_csr_blocks, grid, dim3(512), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_group_csr_heads(const AttnArgs& a, int slots, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.nb * a.n_list));
-  if (slots == 4)
+  if (hpw == 4)
     hipLaunchKernelGGL(group_csr_heads4, grid, dim3(512), 0, s, a);
-  else if (slots == 2)
-    hipLaunchKernelGGL(group_csr_heads2, grid, dim3(256), 0, s, a);
+  else if (hpw == 2)
+    hipLaunchKernelGGL(group_csr_heads2, grid, dim3(512), 0, s, a);
   else
-    return hipErrorInvalidValue;
+    hipLaunchKernelGGL(group_csr_blocks, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -167,14 +167,11 @@ hipError_t launch_group_dense(const AttnArgs& a, hipStream_t s);
 // A-shape heads listed in a.list (one head per KV head), four consecutive
 // query blocks of a head per workgroup.
 hipError_t launch_group_ashape(const AttnArgs& a, hipStream_t s);
-// Heads listed in a.list with dense key sets (any pattern with a CSR), four
-// consecutive query blocks of a head per workgroup over every key below the
-// group's last row.
-hipError_t launch_group_csr(const AttnArgs& a, hipStream_t s);
-// Chunks of `slots` (2 or 4) heads of one KV head with dense key sets, one
-// query block per workgroup, over every key below the block's last row:
-// a.list[slots u + j] is head j of chunk u (-1 for none), a.n_list chunks.
-hipError_t launch_group_csr_heads(const AttnArgs& a, int slots, hipStream_t s);
+// Chunks of hpw (1, 2 or 4) heads of one KV head with dense key sets (any
+// pattern with a CSR), 4 / hpw consecutive query blocks per workgroup, over
+// every key below the group's last row: a.list[hpw u + j] is head j of chunk
+// u (-1 for none), a.n_list chunks.
+hipError_t launch_group_csr(const AttnArgs& a, int hpw, hipStream_t s);
 // Sparse attention over the union index (groups: device table of the
 // a.n_list chunks, hpw = 2 or 4 heads per workgroup, chunks of at most hpw).
 hipError_t launch_group_sparse(const AttnArgs& a, const GroupDesc* groups, int hpw, hipStream_t s);
