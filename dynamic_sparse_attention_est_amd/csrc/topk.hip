@@ -210,12 +210,33 @@ __global__ __launch_bounds__(kMT) void topk_hist(const float* src, int64_t n, To
   load_chunk(x, n, c, t, ck);
   __syncthreads();
   int ab = 0;
+  const int lane = t & 63;
 #pragma unroll
   for (int r = 0; r < kRounds; ++r)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t key = ck.key[r][e];
-      if (ck.valid[r] && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255], 1);
+      const bool act = ck.valid[r] && (key & mask) == prefix;
+      const uint32_t d = (key >> shift) & 255;
+      bool left = act;
+      if (shift == 24) {
+        // The first digit is the sign and the exponent's upper bits, which
+        // neighbouring scores mostly share: the lanes of the two digits met
+        // first add their counts in one LDS atomic per digit instead of one
+        // each on the same address.  (Later digits vary from lane to lane.)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const uint64_t pend = __ballot(left);
+          if (pend == 0) break;
+          const int ld = (int)__builtin_ctzll(pend);
+          const uint32_t dl = __builtin_amdgcn_readlane(d, ld);
+          const bool mine = left && d == dl;
+          const uint64_t same = __ballot(mine);
+          if (lane == ld) atomicAdd(&h[dl], (int)__builtin_popcountll(same));
+          left = left && !mine;
+        }
+      }
+      if (left) atomicAdd(&h[d], 1);
       if (shift == 0) ab += ck.valid[r] & ((key >> 8) > (prefix >> 8));
     }
   __syncthreads();
