@@ -215,10 +215,8 @@ struct PieceIter {
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Loads to LDS: load j (0..3) of wave w fills tile rows 16w + 4j + lane/16;
-// lane writes chunk slot lane%16 and so fetches chunk (lane%16) ^ swz(row).
-// lofs[j] is that chunk's byte offset within a four-row group of keys plus
-// the row's offset, so the address is key_of_row0 * 256 + lofs[j] for a range
-// piece.
+// lane writes chunk slot lane%16 and so fetches chunk (lane%16) ^ swz(row),
+// at byte key_of_row * 256 + 16 ((lane%16) ^ swz(row)).
 
 // Column pieces: the key of a tile row (rows past the piece repeat its last
 // key; the mask drops them).  Global (not flat) loads, which only vmcnt
@@ -234,24 +232,19 @@ struct ColKeys {
   int k[kL];  // keys of rows (32 / (8 / kL)) w + 4j + lane/16
 };
 
-// The piece kind is uniform, so the two address forms are separate branches
-// (no per-load select).  The whole byte offset stays in the vector offset,
-// which the buffer range check covers.
+// Every piece's tile rows come as per-row keys (a range piece's are
+// consecutive), so one address form serves all pieces and the loads need no
+// branch on the piece kind.  The whole byte offset stays in the vector
+// offset, which the buffer range check covers (a piece past the end of the
+// walk reads zeros).
 template <int kL>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int w, const uint32_t* lofs,
-                                          const uint32_t* cofs, const Piece& p, const ColKeys<kL>& ck) {
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int w, const uint32_t* cofs,
+                                          const ColKeys<kL>& ck) {
   char* const base = tile + 256 * 4 * kL * w;
-  if (p.is_col) {
 #pragma unroll
-    for (int j = 0; j < kL; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16,
-                                               (uint32_t)ck.k[j] * (uint32_t)kRowBytes + cofs[j], 0, 0, 0);
-  } else {
-    const uint32_t start = (uint32_t)p.start * (uint32_t)kRowBytes;
-#pragma unroll
-    for (int j = 0; j < kL; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16, start + lofs[j], 0, 0, 0);
-  }
+  for (int j = 0; j < kL; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16,
+                                             (uint32_t)ck.k[j] * (uint32_t)kRowBytes + cofs[j], 0, 0, 0);
 }
 
 // Work items are the listed heads' query blocks of kRows rows (the blocks of
@@ -360,17 +353,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
 
   load_q();
 
-  // Per-lane constants.  Loads: this lane's row rw_j = 16w + 4j + lane/16
-  // and chunk (lane%16) ^ swz(rw_j); lofs = row offset + chunk offset,
-  // cofs = chunk offset alone (column pieces add key * 256).
+  // Per-lane constants.  Loads: this lane's row rw_j = 4 kL w + 4j + lane/16
+  // and chunk (lane%16) ^ swz(rw_j); cofs = that chunk's byte offset (the
+  // row's key * 256 is added per piece).
   const int rq = lane >> 4;
-  uint32_t lofs[kL], cofs[kL];
+  uint32_t cofs[kL];
 #pragma unroll
-  for (int j = 0; j < kL; ++j) {
-    const int rw = 4 * kL * w + 4 * j + rq;
-    cofs[j] = 16u * (uint32_t)((lane & 15) ^ swz(rw));
-    lofs[j] = (uint32_t)rw * (uint32_t)kRowBytes + cofs[j];
-  }
+  for (int j = 0; j < kL; ++j) cofs[j] = 16u * (uint32_t)((lane & 15) ^ swz(4 * kL * w + 4 * j + rq));
   // K fragment t: row l32, chunk 2t + g.
   int kofs[8];
 #pragma unroll
@@ -434,7 +423,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   auto fetch = [&](Piece& p, ColKeys<kL>& c) __attribute__((always_inline)) {
     Piece q;
     Split sp;
-    if (!it.next(q, sp, join)) {
+    // The usual case, without the iterator's other checks: a full piece
+    // inside the current range (paced: starting in the current key segment),
+    // no A-shape window.
+    if (join && it.lo + kKP <= it.hi && (!kPace || it.lo < it.seg_end)) {
+      q.start = it.lo;
+      q.count = kKP;
+      q.is_col = 0;
+      sp.split = 0;
+      it.lo += kKP;
+    } else if (!it.next(q, sp, join)) {
       q.start = kPastEnd;
       q.count = 0;
       q.is_col = 0;
@@ -446,17 +444,19 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     // slots in registers)
     q.mask = q.count == 0 ? 0 : (q.is_col && !sp.split) || kmax > row0 || far ? 2 : q.count < kKP ? 1 : 0;
     p = q;
-    if (q.is_col) {
-      if (sp.split) {
+    // the keys of this lane's tile rows
+    if (!q.is_col) {
 #pragma unroll
-        for (int j = 0; j < kL; ++j) {
-          const int rw = 4 * kL * w + 4 * j + rq;
-          c.k[j] = rw < sp.split ? q.start + rw : sp.start2 + rw - sp.split;
-        }
-      } else {
+      for (int j = 0; j < kL; ++j) c.k[j] = q.start + 4 * kL * w + 4 * j + rq;
+    } else if (sp.split) {
 #pragma unroll
-        for (int j = 0; j < kL; ++j) c.k[j] = col_key(q, col, 4 * kL * w + 4 * j + rq);
+      for (int j = 0; j < kL; ++j) {
+        const int rw = 4 * kL * w + 4 * j + rq;
+        c.k[j] = rw < sp.split ? q.start + rw : sp.start2 + rw - sp.split;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kL; ++j) c.k[j] = col_key(q, col, 4 * kL * w + 4 * j + rq);
     }
   };
   // Mask keys of a column piece: lanes with lane%16 == 0 hold rows 4 kL w + 4j.
@@ -471,10 +471,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
   fetch(pc1, ck1);
   fetch(pc2, ck2);
   __builtin_amdgcn_s_waitcnt(0);
-  load_tile(kr, kb0, w, lofs, cofs, pc0, ck0);
-  load_tile(vr, vb0, w, lofs, cofs, pc0, ck0);
+  load_tile(kr, kb0, w, cofs, ck0);
+  load_tile(vr, vb0, w, cofs, ck0);
   if (pc0.is_col) store_keys(key_lds[0], ck0);
-  load_tile(kr, kb1, w, lofs, cofs, pc1, ck1);
+  load_tile(kr, kb1, w, cofs, ck1);
   if (pc1.is_col) store_keys(key_lds[1], ck1);
   // Settle every outstanding load (Q fragments, first tiles) here, so the
   // wait for them is not placed inside the loop.
@@ -502,9 +502,9 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a) {
     char* const vfill = (PAR & 1) ? vb0 : vb1;        // V of piece i+1
     const char* const vread = (PAR & 1) ? vb1 : vb0;  // V of piece i
 
-    load_tile(kr, kfill, w, lofs, cofs, pc(S2{}), ck(S2{}));
+    load_tile(kr, kfill, w, cofs, ck(S2{}));
     if (pc(S2{}).is_col) store_keys(key_lds[S2::value], ck(S2{}));
-    load_tile(vr, vfill, w, lofs, cofs, pc(S1{}), ck(S1{}));
+    load_tile(vr, vfill, w, cofs, ck(S1{}));
     fetch(pc(S3{}), ck(S3{}));
 
     // Softmax of piece i, masked as its mask kind says (the mask itself per
