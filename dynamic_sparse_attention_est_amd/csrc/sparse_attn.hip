@@ -240,7 +240,14 @@ struct ColKeys {
 template <int kL>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rs, char* tile, int w, const uint32_t* cofs,
                                           const ColKeys<kL>& ck) {
-  char* const base = tile + 256 * 4 * kL * w;
+  // One wave filling whole tiles (kL = 8): the wave's offset is made opaque
+  // here, so the LDS destinations (M0) are formed at each load instead of
+  // being precomputed and held across the loop, where they made the
+  // compiler spill scalar registers (2.5% on a 1M layer of 32-row blocks;
+  // the two-wave kernel runs best with them precomputed).
+  int wofs = 256 * 4 * kL * w;
+  if constexpr (kL == 8) asm volatile("" : "+s"(wofs));
+  char* const base = tile + wofs;
 #pragma unroll
   for (int j = 0; j < kL; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(base + 1024 * j), 16,
