@@ -1,10 +1,13 @@
 """The kernel-aware pattern search: selection logic on the host, and a run on
-the GPU whose choices must be consistent with its own measurements."""
+the GPU whose choices must be consistent with its own measurements and whose
+measured recall matches the oracle's."""
+import numpy as np
 import pytest
 import torch
 
 import dynamic_sparse_attention_est_amd as ms
 from dynamic_sparse_attention_est_amd import search
+import oracle
 import workloads as W
 
 
@@ -48,3 +51,14 @@ def test_search_layer_choices_match_its_measurements():
             mine = next(t for t in trials if t.candidate == p)
             assert mine.recall[h] >= target and mine.ms_per_head <= dense_ms
             assert all(mine.ms_per_head <= t.ms_per_head for t in ok)
+    # A trial's recall is the float64 oracle's attention-mass recall of that
+    # candidate's index (an A-shape candidate, whose index is fixed by its
+    # parameters), within twice the log-sum-exp tolerance per row.
+    a = next(t for t in trials if t.candidate.pattern == ms.A_SHAPE)
+    sink, window = a.candidate.sink, a.candidate.window
+    q64 = q.float().cpu().numpy().astype(np.float64)
+    k64 = k.float().cpu().numpy().astype(np.float64)
+    for h in (0, w.n_q_heads - 1):
+        ref = oracle.attention_recall(q64[h], k64[h // w.group], oracle.ashape_index(sink, window, w.n),
+                                      ashape=(sink, window)).mean()
+        assert abs(a.recall[h] - ref) <= 2.5e-3, f"head {h}: recall {a.recall[h]:.6f} vs {ref:.6f}"
