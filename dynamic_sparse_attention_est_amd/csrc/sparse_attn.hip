@@ -7,10 +7,13 @@
 // wavefronts, each owning 32 rows (a head indexed by 32-row query blocks: one
 // 32-row block = one workgroup of one wavefront, which loads its tiles
 // alone).  The block's keys are its ranges, cut into pieces of up to 32
-// consecutive keys, then its column list in pieces of up to 32 gathered keys.
-// Both waves share one LDS copy of a piece's K and V rows, written by buffer
-// loads that go straight to LDS (no staging registers).  Software pipeline,
-// per iteration i (four pieces in flight, in slots fixed at compile time):
+// consecutive keys (a range's last piece, when short, continuing with the
+// next range's first keys), then its column list in pieces of up to 32
+// gathered keys.  Both waves share one LDS copy of a piece's K and V rows,
+// written by buffer loads that go straight to LDS (no staging registers)
+// from per-row keys, so every piece kind takes one load form.  Software
+// pipeline, per iteration i (four pieces in flight, in slots fixed at compile
+// time):
 //   - loads issued: K rows of piece i+2, V rows of piece i+1;
 //   - S^T of piece i+1 (32 keys x 32 rows) = K . Q^T   v_mfma_f32_32x32x16_bf16
 //     interleaved with the exponentials of piece i, whose S^T the previous
@@ -34,11 +37,12 @@
 //
 // LDS tiles are row-major (one 256-byte row per key) with the 16-byte chunks
 // of row r XOR-swizzled: chunk c sits at chunk slot c ^ swz(r).  One
-// load-to-LDS instruction fills four whole rows (1 KiB of contiguous memory
-// per four keys), and both the K fragment reads and the transposed V reads
-// (ds_read_b64_tr_b16) are free of bank conflicts; the per-lane read offsets
-// are precomputed, so LDS addresses cost no VALU work in the loop.  P and V
-// enter the second product as fp16 (V from an exact fp16 copy).
+// load-to-LDS instruction fills four whole rows (1 KiB of memory per four
+// keys, contiguous for a range piece), and both the K fragment reads and the
+// transposed V reads (ds_read_b64_tr_b16) are free of bank conflicts; the
+// per-lane read offsets are precomputed, so LDS addresses cost no VALU work
+// in the loop.  P and V enter the second product as fp16 (V from an exact
+// fp16 copy).
 #include "internal.h"
 
 namespace msa {
