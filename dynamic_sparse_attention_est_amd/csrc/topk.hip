@@ -45,23 +45,48 @@ __device__ void block_topk(const float* x, int64_t n, int k, int32_t* out, TopkS
     sm.rem = k;
   }
   __syncthreads();
+  static_assert(NT >= 256, "one thread per digit");
+  const int lane = tid & 63;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += NT) sm.hist[i] = 0;
     __syncthreads();
     const uint32_t prefix = sm.prefix, mask = sm.mask;
-    for (int64_t i = tid; i < n; i += NT) {
-      const uint32_t key = order_key(x[i]);
-      if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255], 1);
+    const int rem = sm.rem;
+    for (int64_t i0 = 0; i0 < n; i0 += NT) {
+      const int64_t i = i0 + tid;
+      const uint32_t key = i < n ? order_key(x[i]) : 0u;
+      bool left = i < n && (key & mask) == prefix;
+      const uint32_t d = (key >> shift) & 255;
+      if (shift == 24) {
+        // the first digit (sign and upper exponent bits) is mostly shared by
+        // neighbouring scores: the lanes of the wave's two most common digits
+        // add their counts in one atomic each
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const uint64_t pend = __ballot(left);
+          if (pend == 0) break;
+          const int ld = (int)__builtin_ctzll(pend);
+          const uint32_t dl = __builtin_amdgcn_readlane(d, ld);
+          const bool mine = left && d == dl;
+          const uint64_t same = __ballot(mine);
+          if (lane == ld) atomicAdd(&sm.hist[dl], (int)__builtin_popcountll(same));
+          left = left && !mine;
+        }
+      }
+      if (left) atomicAdd(&sm.hist[d], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int above = 0, d = 255;
-      for (; d > 0; --d) {
-        if (above + sm.hist[d] >= sm.rem) break;
-        above += sm.hist[d];
-      }
-      sm.rem -= above;
-      sm.prefix = prefix | ((uint32_t)d << shift);
+    // Digit of the rem-th largest key: thread t holds bin 255 - t, so its
+    // exclusive prefix sum counts the keys in higher bins; the one thread
+    // whose bin holds the rem-th key records it (bin 0 when no higher bin
+    // does).
+    const int bin = 255 - tid;
+    const int cnt = tid < 256 ? sm.hist[bin] : 0;
+    int tot;
+    const int above = block_excl_scan<NT>(cnt, sm.warp_sum, &tot);
+    if (tid < 256 && above < rem && (above + cnt >= rem || bin == 0)) {
+      sm.rem = rem - above;
+      sm.prefix = prefix | ((uint32_t)bin << shift);
       sm.mask = mask | (255u << shift);
     }
     __syncthreads();
@@ -86,11 +111,12 @@ __device__ void block_topk(const float* x, int64_t n, int k, int32_t* out, TopkS
 
 constexpr int kTopkThreads = 512;
 
+// Jobs 0 .. split-1 write to dst + dst_off, the rest to dst2 + dst_off.
 __global__ __launch_bounds__(kTopkThreads) void topk_rows(const float* src, int64_t n, TopkJobs jobs,
-                                                          int32_t* dst) {
+                                                          int32_t* dst, int32_t* dst2, int split) {
   __shared__ TopkSmem<kTopkThreads> sm;
   const int j = blockIdx.x;
-  block_topk<kTopkThreads>(src + jobs.src_off[j], n, jobs.k[j], dst + jobs.dst_off[j], sm);
+  block_topk<kTopkThreads>(src + jobs.src_off[j], n, jobs.k[j], (j < split ? dst : dst2) + jobs.dst_off[j], sm);
 }
 
 constexpr int kSelThreads = 256;
@@ -385,7 +411,8 @@ __global__ __launch_bounds__(kMT) void topk_write(const float* src, int64_t n, T
 
 hipError_t launch_topk_rows(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, hipStream_t s) {
   if (jobs.count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows, dim3((unsigned)jobs.count), dim3(kTopkThreads), 0, s, src, n, jobs, dst);
+  hipLaunchKernelGGL(topk_rows, dim3((unsigned)jobs.count), dim3(kTopkThreads), 0, s, src, n, jobs, dst, dst,
+                     jobs.count);
   return hipGetLastError();
 }
 
@@ -397,20 +424,13 @@ size_t topk_scratch_bytes(int64_t n, int problems) {
 hipError_t launch_topk_chunked(const float* src, int64_t n, const TopkJobs& jobs, int32_t* dst, int32_t* dst2,
                                int split, void* scratch, hipStream_t s) {
   if (jobs.count <= 0) return hipSuccess;
-  // Short vectors: one workgroup per vector runs every pass in one launch
-  // (the same selection; launch latency dominates at these sizes).
+  // Short vectors: one workgroup per vector runs every pass, every vector of
+  // both selections in one launch (the same selection; launch latency
+  // dominates at these sizes).
   if (n <= 2 * kChunk) {
-    if (split >= jobs.count) return launch_topk_rows(src, n, jobs, dst, s);
-    TopkJobs a = jobs, b = jobs;
-    a.count = split;
-    b.count = jobs.count - split;
-    for (int j = 0; j < b.count; ++j) {
-      b.src_off[j] = jobs.src_off[split + j];
-      b.dst_off[j] = jobs.dst_off[split + j];
-      b.k[j] = jobs.k[split + j];
-    }
-    const hipError_t e = launch_topk_rows(src, n, a, dst, s);
-    return e != hipSuccess ? e : launch_topk_rows(src, n, b, dst2, s);
+    hipLaunchKernelGGL(topk_rows, dim3((unsigned)jobs.count), dim3(kTopkThreads), 0, s, src, n, jobs, dst, dst2,
+                       split);
+    return hipGetLastError();
   }
   const int nchunks = (int)((n + kChunk - 1) / kChunk);
   char* w = static_cast<char*>(scratch);
