@@ -311,15 +311,17 @@ __global__ __launch_bounds__(256) void topk_digit(TopkState* st, const int* hist
     tot[t] -= next;
     __syncthreads();
   }
-  if (t == 0) {
-    const int rem = st[j].rem;
-    int above = 0, d = 255;
-    for (; d > 0; --d) {
-      if (above + tot[d] >= rem) break;
-      above += tot[d];
-    }
+  // Digit of the rem-th largest key: thread t takes bin 255 - t, so its
+  // exclusive prefix sum counts the keys in higher bins; the one thread whose
+  // bin holds the rem-th key records it (bin 0 when no higher bin does).
+  __shared__ int wsum[4];
+  const int rem = st[j].rem;
+  const int bin = 255 - t, cnt = tot[bin];
+  int total;
+  const int above = block_excl_scan<256>(cnt, wsum, &total);
+  if (above < rem && (above + cnt >= rem || bin == 0)) {
     st[j].rem = rem - above;
-    st[j].prefix |= (uint32_t)d << shift;
+    st[j].prefix |= (uint32_t)bin << shift;
     st[j].mask |= 255u << shift;
   }
 }
