@@ -231,7 +231,48 @@ __device__ __forceinline__ void est_body(const VsArgs& a) {
     const bool last_tile_now = tau == last_tile;
     auto score_tile = [&](auto last_c) {
       constexpr bool last = decltype(last_c)::value;
-      if constexpr (!kScores) {
+      if constexpr (!kScores && !last) {
+        // Four products per tile, (key half kt, row half rt) = (g / 2, g % 2);
+        // the statistics of product g-1 (max, then the exponentials and their
+        // sum in element order) are interleaved with the MFMAs of product g.
+        bf16x8 kf[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) kf[t] = kfrag(st, 0, t);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[0][t], acc, 0, 0, 0);
+        auto stats_of = [&](const f32x16& p, int prt, auto with_mfma) {
+          float mx = p[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, p[r]);
+          const float mn = fmaxf(m_run[prt], mx * a.sl2);  // finite: no key is masked in this tile
+          const float alpha = m_run[prt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[prt] - mn);
+          float sum = 0.f;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            with_mfma(t);
+            sum += __builtin_amdgcn_exp2f(fmaf(p[2 * t], a.sl2, -mn));
+            sum += __builtin_amdgcn_exp2f(fmaf(p[2 * t + 1], a.sl2, -mn));
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          z_run[prt] = fmaf(z_run[prt], alpha, sum);
+          m_run[prt] = mn;
+        };
+#pragma unroll
+        for (int gp = 1; gp < 4; ++gp) {
+          const int rt = gp & 1;
+          if (gp == 2) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) kf[t] = kfrag(st, 1, t);
+          }
+          f32x16 nxt = f32x16{};
+          stats_of(acc, (gp - 1) & 1, [&](int t) {
+            nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[rt][t], nxt, 0, 0, 0);
+          });
+          acc = nxt;
+        }
+        stats_of(acc, 1, [&](int) {});
+      } else if constexpr (!kScores) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           bf16x8 kf[8];
