@@ -56,8 +56,11 @@ def _host(st: Staged):
 
 
 # ---------------------------------------------------------------- top-k hook
+# (one workgroup per vector up to 32768 scores, several above; k = 1 and
+# k = n - 1 on both sides of that boundary)
 @pytest.mark.parametrize("n,k,seed", [(1, 1, 0), (7, 3, 1), (513, 0, 2), (513, 600, 3), (4096, 256, 4),
-                                      (100003, 1000, 5), (262144, 6096, 6)])
+                                      (100003, 1000, 5), (262144, 6096, 6), (4096, 4095, 7), (32768, 1, 8),
+                                      (32832, 2, 9), (40000, 39999, 10)])
 def test_topk_hook_bit_exact(n, k, seed):
     g = torch.Generator().manual_seed(seed)
     x = torch.randint(-50, 50, (n,), generator=g).float() * 0.125     # many exact ties
@@ -68,6 +71,15 @@ def test_topk_hook_bit_exact(n, k, seed):
     got = idx.cpu().numpy()[:min(k, n)]
     ref = oracle.topk(x.numpy().astype(np.float64), k)
     np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("n,k", [(5000, 17), (70000, 333)])
+def test_topk_hook_all_scores_equal(n, k):
+    # every key ties: the k lowest indices
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    ms.ms_topk_f32(torch.full((n,), 0.375, device="cuda"), k, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.arange(k))
 
 
 def test_topk_hook_continuous_scores():
